@@ -1,0 +1,181 @@
+"""Benchmark of the sharded-dataflow hot path on one MI355X.
+
+A step is one pass of Arg -> A -> sparse exchange (histogram, scan, stable
+scatter, progress futures) -> B -> Result over the large exchange workload:
+256 shards x 65536 tuples, 64 fp32 payload ~ N(0, 1), each source sending to
+4 destinations drawn with Zipf(1.1) weights (A and B are identities). Inputs
+are resident in HBM before the timed region. One JSON line goes to stdout.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+`value` = exchanged tuples per second (whole step, K steps between two
+synchronisations). `roofline` prices the dominant kernel (the scatter) at its
+algorithmic bytes (520 B per tuple: 256 B payload read + 256 B written, 4 B
+destination read, 4 B source index written) over its mean HIP-event duration
+in the timed region, against the 8 TB/s HBM peak. `cpu_baseline` times the
+CPU oracle (single-threaded NumPy) on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "exchanged tuples/s & % HBM peak; chained sharded A->B steps/s vs N"
+BYTES_PER_TUPLE = 520
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model or platform.processor(), "os_cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
+
+
+def traffic_for(kernel_src: str, kernel: str, launches_g: int):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current source of the kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(kernel)
+    if not rec:
+        return None
+    with open(kernel_src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs every shard on a single MI355X "
+              "(no inter-GPU path is built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import pw_inputs
+    import sparse_shard_exchange_amd as pw
+
+    n, t, p = 256, 65536, 64
+    log("generating inputs")
+    inp = pw_inputs.exchange_zipf(n, t, p)
+    g = n * t
+    x = torch.from_numpy(inp.x).cuda()
+    dest = torch.from_numpy(inp.dest).cuda()
+    counts = np.bincount(inp.dest, minlength=n)
+    ex = pw.Exchange(n, t, p, flags=pw.PW_FLAG_TIMING)
+    torch.cuda.synchronize()
+
+    log("warmup")
+    for _ in range(args.warmup):
+        f = ex.step(x, dest)
+    pw.future_wait(f, 60_000_000_000)
+    ex.plan.reset_times()
+    torch.cuda.synchronize()
+
+    log("timed steps")
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        f = ex.step(x, dest)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pw.future_wait(f, 60_000_000_000)
+    ms_events = e0.elapsed_time(e1) / args.steps
+    ms_wall = (t1 - t0) * 1e3 / args.steps
+    ms = max(ms_events, ms_wall)
+    kt = ex.plan.kernel_times()
+    per_kernel = {k: v[1] / max(v[0], 1) for k, v in kt.items()}
+    scat_ms = per_kernel["scatter"]
+    achieved = BYTES_PER_TUPLE * g / (scat_ms * 1e-3) / 1e9
+    traffic = traffic_for(os.path.join(ROOT, "sparse_shard_exchange_amd", "csrc", "exchange.hip"), "scatter", g)
+
+    result = {
+        "metric": METRIC,
+        "value": g / (ms * 1e-3),
+        "unit": "tuples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "zipf exchange: N=256 shards x T=65536 tuples, 64 fp32 payload ~N(0,1), "
+                        "k=4 destinations per source drawn Zipf(1.1), A=B=identity",
+            "tuples": g,
+            "algorithmic_bytes_per_tuple": BYTES_PER_TUPLE,
+            "hottest_destination_share": float(counts.max() / g),
+            "empty_destinations": int((counts == 0).sum()),
+        },
+        "step_gbs_algorithmic": BYTES_PER_TUPLE * g / (ms * 1e-3) / 1e9,
+        "step_frac_hbm_peak": BYTES_PER_TUPLE * g / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernel_ms": per_kernel,
+        "roofline": {
+            "kernel": "scatter",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        from oracle import exchange as ox
+        xs, ds = inp.x, inp.dest
+        t0 = time.perf_counter()
+        ox.exchange_step(xs, ds, n, n)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": g / dt, "unit": "tuples/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload ({g} tuples, {n} sources) through oracle.exchange.exchange_step, "
+                      f"{dt:.1f} s, single-threaded NumPy",
+            **cpu_info(),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

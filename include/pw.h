@@ -1,0 +1,283 @@
+/*
+ * pw.h -- C ABI of the sharded-dataflow hot path on one MI355X (gfx950).
+ *
+ * The method is the one described on the PATHWAYS page ("PATHWAYS:
+ * Asynchronous Distributed Dataflow for ML"):
+ *   - section 4.3 "Coordination implementation": a chain of two N-sharded
+ *     computations is the four-node graph Arg -> Compute(A) -> Compute(B) ->
+ *     Result; each node emits tuples tagged with destination shards; messages
+ *     travel among dynamically chosen subsets of shards along a sharded edge
+ *     and progress tracking decides when a shard has received all of them;
+ *   - sections 4.4 and 4.5: computations consume buffer futures and a
+ *     successor starts as soon as its input futures are ready; regular
+ *     (statically shaped) subgraphs are prepared ahead of time and handed
+ *     over in one message (parallel asynchronous dispatch);
+ *   - section 4.2 and 4.6: a sharded buffer is one logical object, referred
+ *     to by handle, bookkept once for all of its shards; allocation failure
+ *     means backpressure rather than a crash.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer named "device" is device memory the CALLER owns and keeps
+ *     alive until the future returned by the call has fired; the library
+ *     never allocates, frees or retains device memory of its own. Host
+ *     structs passed in are read during the call only.
+ *   - A stream argument is a hipStream_t passed as void* (NULL = the null
+ *     stream). Calls are stream ordered and return before the device work
+ *     finishes.
+ *   - Every function returns a status code (PW_OK or a negative PW_ERR_*).
+ *     On failure nothing was enqueued, and pw_last_error() (thread local)
+ *     describes the cause. Errors found by kernels (a destination out of
+ *     range, an expired wait) are latched in the plan's device status word
+ *     and reported by the next pw_future_wait on that plan.
+ *   - Nothing aborts or throws across this ABI.
+ *   - No HIP call is made before the first call that needs the device
+ *     (sizing and validation in pw_plan with ws == NULL are host-only).
+ */
+#ifndef PW_H_
+#define PW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PW_ABI_VERSION 1u
+
+/* ---- status codes -------------------------------------------------------- */
+#define PW_OK                0
+#define PW_ERR_INVALID      -1  /* bad argument, descriptor or shape mismatch          */
+#define PW_ERR_NOMEM        -2  /* workspace too small: the caller must grow it and retry
+                                   (the backpressure of section 4.6)                  */
+#define PW_ERR_DEVICE       -3  /* a HIP call failed; pw_last_error() holds its text    */
+#define PW_ERR_TIMEOUT      -4  /* a host wait, or a bounded device wait, expired       */
+#define PW_ERR_BAD_DEST     -5  /* a tuple named a destination outside [0, N); the
+                                   kernels dropped it                                 */
+#define PW_ERR_STATE        -6  /* wrong call order (stale future, destroyed plan, ...) */
+#define PW_ERR_UNSUPPORTED  -7  /* valid request this build does not implement          */
+
+/* ---- element types ------------------------------------------------------- */
+typedef enum { PW_F32 = 0, PW_BF16 = 1 } pw_dtype;
+
+/* ---- graph kinds (one plan = one statically shaped program) -------------- */
+typedef enum {
+  PW_GRAPH_EXCHANGE = 0, /* Arg -> A -> sparse exchange -> B -> Result (section 4.3)          */
+  PW_GRAPH_CHAIN    = 1, /* K chained steps Arg -> A -> B -> Result, identity routing (5.1)   */
+  PW_GRAPH_MOE      = 2, /* A = router + top-k gate, exchange to experts, B = expert FFN,
+                            gated combine back to token order (section 6.3)                 */
+  PW_GRAPH_PIPELINE = 3  /* S stages x M microbatches, GPipe fill/drain (5.3, Table 2)        */
+} pw_graph_kind;
+
+/* ---- elementwise node bodies --------------------------------------------- */
+typedef enum {
+  PW_OP_IDENTITY = 0, /* y = x, bit copy (any dtype)                                   */
+  PW_OP_AFFINE   = 1, /* y = a*x + b in fp32, rounded once (fused multiply-add); fp32 */
+  PW_OP_ROWSUM   = 2  /* B only: one fp32 per tuple, the sum of its P elements; fp32  */
+} pw_op_kind;
+
+typedef struct {
+  uint32_t kind; /* pw_op_kind */
+  float a;
+  float b;
+} pw_op;
+
+/* ---- chain execution modes (section 5.1: OpByOp / Chained / Fused) ------- */
+typedef enum {
+  PW_CHAIN_CHAINED = 0, /* one launch runs every step; each node waits on its input futures
+                           in the HBM future table and fires its own                        */
+  PW_CHAIN_OPBYOP  = 1, /* one host launch per node per step                                 */
+  PW_CHAIN_FUSED   = 2  /* one launch, one node per shard looping over the steps, no futures */
+} pw_chain_mode;
+
+/* ---- plan flags ----------------------------------------------------------- */
+#define PW_FLAG_TRACE   0x1u /* record a device timestamp for every future fire          */
+#define PW_FLAG_TIMING  0x2u /* record HIP events around every kernel (pw_plan_kernel_times) */
+
+/* ---- plan descriptor ------------------------------------------------------ */
+typedef struct {
+  uint32_t abi_version;      /* must be PW_ABI_VERSION                                        */
+  uint32_t kind;             /* pw_graph_kind                                                  */
+  uint32_t num_shards;       /* EXCHANGE/CHAIN: N shards; MOE: experts E; PIPELINE: stages S   */
+  uint32_t num_src_shards;   /* EXCHANGE/MOE: source shards (0 = num_shards)                   */
+  uint64_t tuples_per_shard; /* EXCHANGE: tuples per source shard T; MOE: tokens per source
+                                shard; CHAIN: fp32 elements per shard; PIPELINE: rows per
+                                microbatch                                                     */
+  uint32_t payload_elems;    /* EXCHANGE: elements per tuple P; MOE/PIPELINE: model width d    */
+  uint32_t dtype;            /* EXCHANGE payload dtype (pw_dtype); MOE/PIPELINE: PW_BF16       */
+  pw_op a_op;                /* EXCHANGE/CHAIN: A's body                                       */
+  pw_op b_op;                /* EXCHANGE/CHAIN: B's body                                       */
+  uint32_t top_k;            /* MOE: tuples per token (2)                                      */
+  uint32_t hidden;           /* MOE: expert FFN hidden width                                   */
+  uint32_t microbatches;     /* PIPELINE: M                                                    */
+  uint32_t chain_mode;       /* CHAIN: pw_chain_mode                                           */
+  uint32_t flags;            /* PW_FLAG_*                                                      */
+  uint32_t reserved0;
+  uint64_t spin_limit_ns;    /* bound of every device-side wait (0 = 2 s); an expired wait
+                                latches PW_ERR_TIMEOUT and the waiting work is skipped        */
+  const void* w_router;      /* MOE: device bf16 [d][E] (borrowed)                             */
+  const void* w1;            /* MOE: device bf16 [E][d][hidden]; PIPELINE: bf16 [S][d][d]      */
+  const void* w2;            /* MOE: device bf16 [E][hidden][d]                                */
+} pw_plan_desc;
+
+/* ---- sharded buffer: one logical buffer over N shards (section 4.2) ------- */
+typedef struct {
+  void* base;               /* device: tuple 0 of shard 0; tuples are rows of elems_per_tuple */
+  uint64_t num_tuples;      /* rows over all shards                                          */
+  uint32_t num_shards;
+  uint32_t elems_per_tuple;
+  uint32_t dtype;           /* pw_dtype                                                      */
+  uint32_t reserved0;
+  int64_t* shard_offsets;   /* device [num_shards + 1] row offsets of the shards. Inputs:
+                               NULL = uniform shards. Exchange outputs: written by the call
+                               (the CSR of the destination segments), may be NULL            */
+} pw_sharded_buf;
+
+/* ---- futures (sections 4.4-4.5) -------------------------------------------
+ * A future names one (node, shard) of one plan and one epoch. Epochs count
+ * calls (EXCHANGE, MOE, PIPELINE) or steps (CHAIN) and start at 1. It is a
+ * value type: nothing to free. */
+typedef enum {
+  PW_NODE_ARG = 0, PW_NODE_A = 1, PW_NODE_EXCHANGE = 2, PW_NODE_B = 3, PW_NODE_RESULT = 4,
+  PW_NODE_STAGE = 5 /* PIPELINE: shard = stage * M + microbatch */
+} pw_node;
+
+typedef struct {
+  uint64_t plan_id;
+  uint32_t node;   /* pw_node                                  */
+  int32_t shard;   /* -1 = the whole node (Result)              */
+  uint64_t epoch;
+} pw_future_t;
+
+typedef struct pw_plan_s* pw_plan_t;
+
+/* ---- exchange call arguments ---------------------------------------------- */
+typedef struct {
+  pw_sharded_buf src;   /* EXCHANGE: [G][P] rows, shard-major (tuple g = s*T + i).
+                           MOE: the tokens [tokens][d] bf16                                 */
+  const int32_t* dest;  /* EXCHANGE: device [G] destination per tuple. MOE: NULL (A routes) */
+  pw_sharded_buf dst;   /* [G][P] A(src) rows in exchange order: destination-major, source
+                           order inside a destination. MOE: [k*tokens][d] dispatched rows;
+                           dst.shard_offsets (nullable) receives the N+1 segment offsets     */
+  int32_t* src_index;   /* device [G]: source tuple index held by each output slot (nullable
+                           for EXCHANGE; MOE: tuple g = k*token + slot)                      */
+  int32_t* counts;      /* device [num_src][N]: tuples per (source, destination); nullable   */
+  void* b_out;          /* EXCHANGE: B's output in exchange order -- ROWSUM: fp32 [G];
+                           AFFINE: fp32 [G][P]; IDENTITY: unused. MOE: expert outputs
+                           [k*tokens][d] bf16 (required)                                     */
+  void* result;         /* MOE: combined output [tokens][d] bf16 (required)                  */
+  float* logits;        /* MOE: router logits fp32 [tokens][E]; nullable                     */
+  int32_t* experts;     /* MOE: [tokens][k] chosen experts, best first; nullable             */
+  float* gates;         /* MOE: [tokens][k] gate values; nullable                            */
+} pw_exchange_io;
+
+/* ---- per-kernel timing (PW_FLAG_TIMING) ----------------------------------- */
+typedef struct {
+  char name[32];
+  uint64_t launches;
+  double total_ms;  /* sum of HIP-event durations over the launches */
+} pw_kernel_time;
+
+/* ======================================================================== */
+
+/* ABI version of the loaded library (PW_ABI_VERSION it was built with). */
+uint32_t pw_abi_version(void);
+
+/* Static text for a status code. Never NULL. */
+const char* pw_strerror(int status);
+
+/* Thread-local text of this thread's last failure ("" if none). */
+const char* pw_last_error(void);
+
+/*
+ * pw_plan -- build a statically shaped program once (PATHWAYS page, section
+ * 4.5: host work for every node is done before any node runs, from the known
+ * shapes; section 3 and Appendix B: compiled functions have static shapes).
+ *
+ * Two calls. With ws == NULL it validates `d` on the host only and stores the
+ * workspace size in *ws_required (out may be NULL). With ws != NULL (device
+ * memory of ws_bytes >= *ws_required, 256-byte aligned, caller-owned, kept
+ * alive until pw_plan_destroy) it lays out the tables in ws, clears them,
+ * and returns an opaque handle in *out. ws_bytes too small -> PW_ERR_NOMEM.
+ * The plan holds host metadata only; weights in `d` are borrowed pointers.
+ */
+int pw_plan(const pw_plan_desc* d, void* ws, size_t ws_bytes, size_t* ws_required, pw_plan_t* out);
+
+/* Release the plan's host metadata (not ws). PW_ERR_STATE if its last call
+ * may still be running (wait on its future first). */
+int pw_plan_destroy(pw_plan_t plan);
+
+/*
+ * pw_exchange -- one step Arg -> Compute(A) -> sparse exchange -> Compute(B)
+ * -> Result (PATHWAYS page, section 4.3; for MOE also section 6.3).
+ *
+ * EXCHANGE: every tuple of src goes, transformed by A, to the segment of its
+ * destination in dst; segments are in destination order and keep source
+ * order inside (a stable sort by destination); src_index/counts/segment
+ * offsets describe the move. The future of destination d (node EXCHANGE)
+ * fires once all of its tuples are written; B runs on segment d only after
+ * that future fired and fires node B; Result fires after every B.
+ * MOE: A is the router GEMM with top-k gating (tuple g = k*token + slot goes
+ * to expert experts[token][slot]); B is the expert FFN on each expert's
+ * segment, gated on that expert's future; the combine gathers each token's
+ * k expert rows back and sums them weighted by the gates into `result`.
+ *
+ * Stream ordered; *done receives the Result future. Argument errors return
+ * PW_ERR_INVALID before anything is enqueued.
+ */
+int pw_exchange(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done);
+
+/*
+ * pw_chain_run -- run a chained program in one call (PATHWAYS page, section
+ * 3 "program tracer", section 4.5 parallel asynchronous dispatch, section 5.1
+ * chained execution).
+ *
+ * CHAIN: `steps` repetitions of Arg -> A -> B -> Result over `state` (N shards
+ * of tuples_per_shard fp32, one tuple per shard, identity routing). The
+ * Result of step k is the Arg of step k + 1; on return of the device work
+ * `state` holds the last Result. `aux` (nullable, device, same shape as state)
+ * receives A's last output. Mode per plan (chain_mode).
+ * PIPELINE: steps must be 1. `state` holds the M microbatches [M][rows][d]
+ * bf16; `aux` (device, required) receives every stage output [S][M][rows][d]
+ * bf16. Item (s, m) runs after (s-1, m) fired its future and after (s, m-1).
+ *
+ * *done receives the future of the last Result.
+ */
+int pw_chain_run(pw_plan_t plan, uint64_t steps, pw_sharded_buf* state, void* aux, void* stream,
+                 pw_future_t* done);
+
+/*
+ * pw_future_wait -- block the calling host thread until `f` fired or
+ * timeout_ns passed (< 0: no limit). Returns PW_OK, PW_ERR_TIMEOUT, a status
+ * latched by the plan's kernels (PW_ERR_BAD_DEST, PW_ERR_TIMEOUT), or
+ * PW_ERR_STATE if the future belongs to no live plan or its epoch was never
+ * launched.
+ */
+int pw_future_wait(pw_future_t f, int64_t timeout_ns);
+
+/* Non-blocking form: *fired = 1 if f has fired, else 0. */
+int pw_future_query(pw_future_t f, int* fired);
+
+/*
+ * pw_plan_read_futures -- copy the plan's device future table to host memory
+ * after waiting for its last call: epochs[node * width + shard] (the last
+ * epoch each future fired for), fires[...] (how many times it fired since
+ * the plan was built) and, with PW_FLAG_TRACE, stamps[...] (device clock at
+ * the last fire, 100 MHz ticks). Any pointer may be NULL. *width receives
+ * the number of shard slots per node, *nodes the number of node rows.
+ */
+int pw_plan_read_futures(pw_plan_t plan, uint32_t* epochs, uint32_t* fires, uint64_t* stamps,
+                         size_t capacity, uint32_t* nodes, uint32_t* width);
+
+/* Per-kernel launch counts and HIP-event times accumulated under
+ * PW_FLAG_TIMING (waits for pending events). *n receives the entry count. */
+int pw_plan_kernel_times(pw_plan_t plan, pw_kernel_time* out, int max, int* n);
+
+/* Clear the accumulated kernel times. */
+int pw_plan_reset_times(pw_plan_t plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PW_H_ */

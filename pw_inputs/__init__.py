@@ -49,6 +49,32 @@ def rng_for(workload: int, *key: int) -> np.random.Generator:
     return np.random.default_rng(ss)
 
 
+_CHUNK_ROWS = 1 << 20
+
+
+def _fill_chunked(shape, workload: int, key: tuple, draw) -> np.ndarray:
+    """Fill a [rows, cols] float32 array chunk by chunk (1 Mi rows each), every
+    chunk from its own generator spawned with the chunk index in its key, in
+    parallel threads. The values depend only on (workload, key, shape)."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows, cols = shape
+    out = np.empty((rows, cols), dtype=np.float32)
+    starts = list(range(0, rows, _CHUNK_ROWS))
+
+    def work(i_start):
+        i, start = i_start
+        stop = min(rows, start + _CHUNK_ROWS)
+        draw(rng_for(workload, *key, i), out[start:stop])
+
+    if len(starts) <= 1:
+        for i_s in enumerate(starts):
+            work(i_s)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, len(starts))) as ex:
+            list(ex.map(work, enumerate(starts)))
+    return out
+
+
 def sha256(a) -> str:
     """SHA-256 of an array's raw bytes (numpy array or CPU torch tensor)."""
     if hasattr(a, "numpy") and not isinstance(a, np.ndarray):
@@ -99,7 +125,8 @@ def exchange_zipf(num_shards: int = 256, tuples_per_shard: int = 65536, payload:
     pick = rng_for(2, 2, *key).integers(0, kk, size=(num_shards, tuples_per_shard), dtype=np.int64)
     dest = np.take_along_axis(choices, pick, axis=1).reshape(g).astype(np.int32)
     if with_payload:
-        x = rng_for(2, 0, *key).standard_normal(size=(g, payload), dtype=np.float32)
+        x = _fill_chunked((g, payload), 2, (0, *key),
+                          lambda r, o: r.standard_normal(size=o.shape, dtype=np.float32, out=o))
     else:
         x = np.zeros((0, payload), dtype=np.float32)
     return ExchangeInputs(x, dest, num_shards, tuples_per_shard, choices=choices,

@@ -1,0 +1,73 @@
+// Device helpers shared by the pw kernels: wave64 peer matching, the status
+// latch, and firing / awaiting buffer futures in the HBM future table.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace pw {
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt(uint32_t lane) { return (1ull << lane) - 1ull; }
+
+// Lanes of this wave holding the same destination as this lane, found with
+// one ballot per destination bit (wave64 has no native match instruction).
+// Lanes with valid == false match nothing and get 0.
+// Must be called by all 64 lanes with the same nbits.
+__device__ __forceinline__ uint64_t match_peers(int d, bool valid, uint32_t nbits) {
+  uint64_t m = __ballot(valid);
+  for (uint32_t b = 0; b < nbits; ++b) {
+    const bool bit = (d >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return valid ? m : 0ull;
+}
+
+__device__ __forceinline__ void latch(uint32_t* status, uint32_t code) {
+  uint32_t expected = ST_OK;
+  __hip_atomic_compare_exchange_strong(status, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Fire future (node, shard) for `epoch`. `release` orders every earlier write
+// of this thread (and, after a workgroup barrier, of its workgroup) before the
+// epoch becomes visible to other workgroups; without it, visibility comes
+// from the end of the kernel (consumers in a later launch).
+__device__ __forceinline__ void fire(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch,
+                                     bool release) {
+  const uint32_t i = node * f.width + shard;
+  if (f.stamps) f.stamps[i] = wall_clock64();
+  __hip_atomic_fetch_add(&f.fires[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (release)
+    __hip_atomic_store(&f.epoch[i], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    __hip_atomic_store(&f.epoch[i], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool epoch_reached(uint32_t v, uint32_t epoch) {
+  return (int32_t)(v - epoch) >= 0;
+}
+
+// Wait (acquire) until future (node, shard) fired for `epoch` or later. The
+// wait is bounded by f.spin_ticks of the 100 MHz wall clock; on expiry it
+// latches ST_TIMEOUT and returns false so the caller skips its work and the
+// wave still exits.
+__device__ __forceinline__ bool await(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
+  const uint32_t* p = &f.epoch[node * f.width + shard];
+  if (epoch_reached(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    if (epoch_reached(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
+    if (wall_clock64() - t0 > f.spin_ticks) {
+      latch(f.status, ST_TIMEOUT);
+      return false;
+    }
+  }
+}
+
+}  // namespace pw

@@ -1,0 +1,641 @@
+// Host runtime of the pw C ABI: plan building (workspace layout, static
+// launch shapes), argument validation, stream-ordered launches, futures and
+// kernel timing. It allocates no device memory: the caller hands in the
+// workspace and every buffer.
+//
+// PATHWAYS page ("PATHWAYS: Asynchronous Distributed Dataflow for ML"),
+// section 4.5: because compiled functions have static shapes, all host work
+// for a program (buffer layout, launch shapes, future slots) is done once, up
+// front; afterwards a call only enqueues device work. Section 4.2: the plan
+// keeps one record per logical sharded buffer, never one per shard.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <map>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/pw.h"
+#include "internal.h"
+#include "runtime.h"
+
+namespace pw {
+
+// ------------------------------------------------------------------ errors
+static thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PW_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- registry
+static std::mutex g_reg_mu;
+static std::unordered_map<uint64_t, Plan*> g_plans;
+static uint64_t g_next_id = 1;
+
+Plan* lookup(uint64_t id) {
+  std::lock_guard<std::mutex> lk(g_reg_mu);
+  auto it = g_plans.find(id);
+  return it == g_plans.end() ? nullptr : it->second;
+}
+
+// A handle is live if the registry holds it; the pointer itself is never
+// dereferenced before that check, so stale or forged handles are safe.
+bool is_live(const Plan* p) {
+  if (!p) return false;
+  std::lock_guard<std::mutex> lk(g_reg_mu);
+  for (const auto& kv : g_plans)
+    if (kv.second == p) return true;
+  return false;
+}
+
+// ------------------------------------------------------------------ layout
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  }
+};
+
+static uint32_t ceil_log2(uint32_t n) {
+  uint32_t b = 0;
+  while ((1ull << b) < n) ++b;
+  return b;
+}
+
+static uint32_t pick_tile(uint64_t G) {
+  uint32_t tile = 256;
+  while (tile < 4096 && G / ((uint64_t)tile * 2) >= 2048) tile *= 2;
+  return tile;
+}
+
+int plan_layout(const pw_plan_desc& d, Layout& L) {
+  L = Layout{};
+  Carver c;
+  L.ctl = c.take(256);
+  switch (d.kind) {
+    case PW_GRAPH_EXCHANGE:
+    case PW_GRAPH_MOE: {
+      const uint32_t N = d.num_shards;
+      const uint32_t S = d.num_src_shards ? d.num_src_shards : d.num_shards;
+      const uint64_t fan = d.kind == PW_GRAPH_MOE ? d.top_k : 1;
+      L.G = (uint64_t)S * d.tuples_per_shard * fan;
+      L.tile = pick_tile(L.G);
+      L.num_tiles = (uint32_t)std::max<uint64_t>(1, (L.G + L.tile - 1) / L.tile);
+      L.width = std::max<uint32_t>(std::max(N, S), 1);
+      L.fut = c.take((size_t)kNodes * L.width * 4);
+      L.fires = c.take((size_t)kNodes * L.width * 4);
+      if (d.flags & PW_FLAG_TRACE) L.stamps = c.take((size_t)kNodes * L.width * 8);
+      L.arrived = c.take((size_t)N * 4);
+      L.expected = c.take((size_t)N * 4);
+      L.b_arrived = c.take((size_t)N * 4);
+      L.seg = c.take((size_t)(N + 1) * 8);
+      L.tile_base = c.take((size_t)N * L.num_tiles * 4);
+      if (d.kind == PW_GRAPH_MOE) {
+        const uint64_t tokens = (uint64_t)S * d.tuples_per_shard;
+        L.experts = c.take(tokens * d.top_k * 4);
+        L.gates = c.take(tokens * d.top_k * 4);
+        L.slot_of = c.take(L.G * 4);
+        L.hidden_act = c.take(L.G * (uint64_t)d.hidden * 2);
+      }
+      break;
+    }
+    case PW_GRAPH_CHAIN: {
+      L.width = d.num_shards;
+      L.fut = c.take((size_t)kNodes * L.width * 4);
+      L.fires = c.take((size_t)kNodes * L.width * 4);
+      if (d.flags & PW_FLAG_TRACE) L.stamps = c.take((size_t)kNodes * L.width * 8);
+      L.a_buf = c.take((size_t)d.num_shards * d.tuples_per_shard * 4);
+      break;
+    }
+    case PW_GRAPH_PIPELINE: {
+      L.width = d.num_shards * d.microbatches;
+      L.fut = c.take((size_t)kNodes * L.width * 4);
+      L.fires = c.take((size_t)kNodes * L.width * 4);
+      if (d.flags & PW_FLAG_TRACE) L.stamps = c.take((size_t)kNodes * L.width * 8);
+      L.pipe_ctl = c.take(4096);
+      break;
+    }
+    default:
+      return fail(PW_ERR_INVALID, "unknown graph kind %u", d.kind);
+  }
+  L.total = c.off;
+  return PW_OK;
+}
+
+static int validate_op(const pw_op& op, bool allow_rowsum, const char* which) {
+  if (op.kind > PW_OP_ROWSUM) return fail(PW_ERR_INVALID, "%s: unknown op kind %u", which, op.kind);
+  if (op.kind == PW_OP_ROWSUM && !allow_rowsum) return fail(PW_ERR_INVALID, "%s: ROWSUM is only a B body", which);
+  return PW_OK;
+}
+
+int validate_desc(const pw_plan_desc* d) {
+  if (!d) return fail(PW_ERR_INVALID, "descriptor is NULL");
+  if (d->abi_version != PW_ABI_VERSION)
+    return fail(PW_ERR_INVALID, "abi_version %u != %u", d->abi_version, PW_ABI_VERSION);
+  if (d->flags & ~(PW_FLAG_TRACE | PW_FLAG_TIMING)) return fail(PW_ERR_INVALID, "unknown flags 0x%x", d->flags);
+  switch (d->kind) {
+    case PW_GRAPH_EXCHANGE: {
+      // the scatter keeps 5 words per destination in LDS (160 KiB per CU)
+      if (d->num_shards == 0 || d->num_shards > 8192) return fail(PW_ERR_INVALID, "num_shards must be in [1, 8192]");
+      const uint64_t S = d->num_src_shards ? d->num_src_shards : d->num_shards;
+      const uint64_t G = S * d->tuples_per_shard;
+      if (G > 0x7fffffffull) return fail(PW_ERR_INVALID, "more than 2^31-1 tuples");
+      if (d->dtype != PW_F32 && d->dtype != PW_BF16) return fail(PW_ERR_INVALID, "unknown dtype %u", d->dtype);
+      const uint64_t esz = d->dtype == PW_F32 ? 4 : 2;
+      if (d->payload_elems == 0) return fail(PW_ERR_INVALID, "payload_elems must be > 0");
+      const uint64_t row = esz * d->payload_elems;
+      if (row % 4 != 0 || row > (1u << 20)) return fail(PW_ERR_INVALID, "payload row must be a multiple of 4 bytes, <= 1 MiB");
+      int st;
+      if ((st = validate_op(d->a_op, false, "a_op"))) return st;
+      if ((st = validate_op(d->b_op, true, "b_op"))) return st;
+      if (d->dtype != PW_F32 && (d->a_op.kind != PW_OP_IDENTITY || d->b_op.kind != PW_OP_IDENTITY))
+        return fail(PW_ERR_INVALID, "A/B bodies other than IDENTITY need fp32 payloads");
+      if ((uint64_t)d->num_shards * std::max<uint64_t>(1, (G + 255) / 256) > (1ull << 31))
+        return fail(PW_ERR_INVALID, "destination x tile table too large");
+      return PW_OK;
+    }
+    case PW_GRAPH_CHAIN:
+    case PW_GRAPH_MOE:
+    case PW_GRAPH_PIPELINE:
+      return validate_desc_more(d);
+    default:
+      return fail(PW_ERR_INVALID, "unknown graph kind %u", d->kind);
+  }
+}
+
+// ---------------------------------------------------------------- timing
+void Plan::launch_begin(const char* name, hipStream_t s) {
+  if (!(desc.flags & PW_FLAG_TIMING)) return;
+  Pending p;
+  p.name = name;
+  p.e0 = get_event();
+  p.e1 = get_event();
+  (void)hipEventRecord(p.e0, s);
+  pending.push_back(p);
+}
+
+void Plan::launch_end(hipStream_t s) {
+  if (!(desc.flags & PW_FLAG_TIMING) || pending.empty()) return;
+  (void)hipEventRecord(pending.back().e1, s);
+  if (pending.size() > 4096) resolve_times();
+}
+
+hipEvent_t Plan::get_event() {
+  if (!event_pool.empty()) {
+    hipEvent_t e = event_pool.back();
+    event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  (void)hipEventCreate(&e);
+  return e;
+}
+
+void Plan::resolve_times() {
+  for (auto& p : pending) {
+    (void)hipEventSynchronize(p.e1);
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, p.e0, p.e1);
+    auto& t = times[p.name];
+    t.launches += 1;
+    t.total_ms += ms;
+    event_pool.push_back(p.e0);
+    event_pool.push_back(p.e1);
+  }
+  pending.clear();
+}
+
+// --------------------------------------------------------- call bookkeeping
+int Plan::begin_call(hipStream_t s) {
+  if (device < 0) {
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  }
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (cur != device) return fail(PW_ERR_STATE, "plan built on device %d, current device is %d", device, cur);
+  (void)s;
+  return PW_OK;
+}
+
+int Plan::end_call(hipStream_t s, uint64_t epoch_hi) {
+  hipEvent_t e = nullptr;
+  if (!done_pool.empty()) {
+    e = done_pool.back();
+    done_pool.pop_back();
+  } else {
+    hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+  }
+  hipError_t err = hipEventRecord(e, s);
+  if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+  done.push_back({epoch_hi, e});
+  while (done.size() > 16) {
+    done_pool.push_back(done.front().event);
+    done.pop_front();
+  }
+  return PW_OK;
+}
+
+hipEvent_t Plan::event_for(uint64_t epoch) const {
+  for (const auto& d : done)
+    if (d.epoch_hi >= epoch) return d.event;
+  return done.empty() ? nullptr : done.back().event;
+}
+
+Futures Plan::futures() const {
+  Futures f{};
+  auto* base = static_cast<unsigned char*>(ws);
+  f.status = reinterpret_cast<uint32_t*>(base + L.ctl);
+  f.epoch = reinterpret_cast<uint32_t*>(base + L.fut);
+  f.fires = reinterpret_cast<uint32_t*>(base + L.fires);
+  f.stamps = (desc.flags & PW_FLAG_TRACE) ? reinterpret_cast<uint64_t*>(base + L.stamps) : nullptr;
+  f.width = L.width;
+  const uint64_t ns = desc.spin_limit_ns ? desc.spin_limit_ns : 2000000000ull;
+  f.spin_ticks = (uint32_t)std::min<uint64_t>(0xffffffffull, ns / 10);  // 100 MHz wall clock
+  return f;
+}
+
+int Plan::read_status(uint32_t* status, bool clear) {
+  if (!aux) {
+    hipError_t e = hipStreamCreateWithFlags(&aux, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreate");
+  }
+  uint32_t* st = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + L.ctl);
+  hipError_t e = hipMemcpyAsync(status, st, 4, hipMemcpyDeviceToHost, aux);
+  if (e == hipSuccess) e = hipStreamSynchronize(aux);
+  if (e != hipSuccess) return hip_fail(e, "reading the status word");
+  if (clear && *status) {
+    e = hipMemsetAsync(st, 0, 4, aux);
+    if (e == hipSuccess) e = hipStreamSynchronize(aux);
+    if (e != hipSuccess) return hip_fail(e, "clearing the status word");
+  }
+  return PW_OK;
+}
+
+int Plan::read_epoch(uint32_t node, uint32_t shard, uint32_t* v) {
+  if (node >= kNodes || shard >= L.width) return fail(PW_ERR_INVALID, "future (%u, %u) outside the table", node, shard);
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<unsigned char*>(ws) + L.fut) + node * L.width + shard;
+  hipError_t e = hipMemcpyAsync(v, p, 4, hipMemcpyDeviceToHost, aux);
+  if (e == hipSuccess) e = hipStreamSynchronize(aux);
+  if (e != hipSuccess) return hip_fail(e, "reading the future table");
+  return PW_OK;
+}
+
+static int status_to_code(uint32_t st) {
+  switch (st) {
+    case ST_OK: return PW_OK;
+    case ST_BAD_DEST: return fail(PW_ERR_BAD_DEST, "a tuple named a destination outside [0, N)");
+    case ST_TIMEOUT: return fail(PW_ERR_TIMEOUT, "a device-side wait on a future expired");
+    default: return fail(PW_ERR_DEVICE, "unknown device status %u", st);
+  }
+}
+
+// ------------------------------------------------------------ exchange call
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done) {
+  const pw_plan_desc& d = p->desc;
+  const Layout& L = p->L;
+  const uint32_t N = d.num_shards;
+  const uint32_t S = d.num_src_shards ? d.num_src_shards : N;
+  const uint32_t esz = d.dtype == PW_F32 ? 4 : 2;
+  const uint32_t row = esz * d.payload_elems;
+  if (L.G && (!io->src.base || !io->dest || !io->dst.base)) return fail(PW_ERR_INVALID, "src, dest and dst are required");
+  if (io->src.num_tuples != L.G || io->src.elems_per_tuple != d.payload_elems || io->src.dtype != d.dtype)
+    return fail(PW_ERR_INVALID, "src does not match the plan (tuples %llu, elems %u, dtype %u)",
+                (unsigned long long)io->src.num_tuples, io->src.elems_per_tuple, io->src.dtype);
+  if (io->src.shard_offsets) return fail(PW_ERR_UNSUPPORTED, "non-uniform source shards");
+  if (io->dst.num_tuples < L.G || io->dst.elems_per_tuple != d.payload_elems || io->dst.dtype != d.dtype)
+    return fail(PW_ERR_INVALID, "dst does not match the plan");
+  if (!aligned16(io->src.base) || !aligned16(io->dst.base)) return fail(PW_ERR_INVALID, "src/dst must be 16-byte aligned");
+  if (d.b_op.kind != PW_OP_IDENTITY && !io->b_out) return fail(PW_ERR_INVALID, "b_out is required when B is not IDENTITY");
+  int st = p->begin_call(s);
+  if (st) return st;
+
+  ExchangeArgs a{};
+  auto* base = static_cast<unsigned char*>(p->ws);
+  a.src = static_cast<const unsigned char*>(io->src.base);
+  a.dest = io->dest;
+  a.dst = static_cast<unsigned char*>(io->dst.base);
+  a.src_index = io->src_index;
+  a.slot_of = nullptr;
+  a.counts = io->counts;
+  a.offsets_out = io->dst.shard_offsets;
+  a.b_out = io->b_out;
+  a.G = L.G;
+  a.T = d.tuples_per_shard;
+  a.N = N;
+  a.num_src = S;
+  a.row_bytes = row;
+  a.fanout = 1;
+  a.tile = L.tile;
+  a.num_tiles = L.num_tiles;
+  a.nbits = ceil_log2(N);
+  a.is_f32 = d.dtype == PW_F32;
+  a.a_kind = d.a_op.kind; a.a_a = d.a_op.a; a.a_b = d.a_op.b;
+  a.b_kind = d.b_op.kind; a.b_a = d.b_op.a; a.b_b = d.b_op.b;
+  a.epoch = (uint32_t)(p->epoch + 1);
+  a.b_gated = d.b_op.kind != PW_OP_IDENTITY;
+  a.f = p->futures();
+  a.arrived = reinterpret_cast<uint32_t*>(base + L.arrived);
+  a.expected = reinterpret_cast<uint32_t*>(base + L.expected);
+  a.b_arrived = reinterpret_cast<uint32_t*>(base + L.b_arrived);
+  a.ctl = reinterpret_cast<uint32_t*>(base + L.ctl + 64);
+  a.tile_base = reinterpret_cast<uint32_t*>(base + L.tile_base);
+  a.seg = reinterpret_cast<int64_t*>(base + L.seg);
+
+  hipError_t e = hipSuccess;
+  if (io->counts) {
+    p->launch_begin("src_counts", s);
+    e = launch_src_counts(a, s);
+    p->launch_end(s);
+    if (e != hipSuccess) return hip_fail(e, "launch src_counts");
+  }
+  p->launch_begin("hist", s);
+  e = launch_hist(a, s);
+  p->launch_end(s);
+  if (e != hipSuccess) return hip_fail(e, "launch hist");
+  p->launch_begin("scan", s);
+  e = launch_scan(a, s);
+  p->launch_end(s);
+  if (e != hipSuccess) return hip_fail(e, "launch scan");
+  p->launch_begin("scatter", s);
+  e = launch_scatter(a, s);
+  p->launch_end(s);
+  if (e != hipSuccess) return hip_fail(e, "launch scatter");
+  if (a.b_gated) {
+    p->launch_begin("b", s);
+    e = launch_b(a, s);
+    p->launch_end(s);
+    if (e != hipSuccess) return hip_fail(e, "launch b");
+  }
+  p->epoch += 1;
+  st = p->end_call(s, p->epoch);
+  if (st) return st;
+  if (done) *done = pw_future_t{p->id, PW_NODE_RESULT, -1, p->epoch};
+  return PW_OK;
+}
+
+}  // namespace pw
+
+// ======================================================================= ABI
+using namespace pw;
+
+extern "C" {
+
+uint32_t pw_abi_version(void) { return PW_ABI_VERSION; }
+
+const char* pw_strerror(int status) {
+  switch (status) {
+    case PW_OK: return "ok";
+    case PW_ERR_INVALID: return "invalid argument";
+    case PW_ERR_NOMEM: return "workspace too small";
+    case PW_ERR_DEVICE: return "HIP runtime error";
+    case PW_ERR_TIMEOUT: return "timed out";
+    case PW_ERR_BAD_DEST: return "destination out of range";
+    case PW_ERR_STATE: return "invalid state";
+    case PW_ERR_UNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+  }
+}
+
+const char* pw_last_error(void) { return g_last_error.c_str(); }
+
+int pw_plan(const pw_plan_desc* d, void* ws, size_t ws_bytes, size_t* ws_required, pw_plan_t* out) {
+  g_last_error.clear();
+  int st = validate_desc(d);
+  if (st) return st;
+  Layout L;
+  if ((st = plan_layout(*d, L))) return st;
+  if (ws_required) *ws_required = L.total;
+  if (!ws) {
+    if (out) *out = nullptr;
+    return PW_OK;
+  }
+  if (!out) return fail(PW_ERR_INVALID, "out is NULL");
+  if (((uintptr_t)ws & 255u) != 0) return fail(PW_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(PW_ERR_NOMEM, "workspace has %zu bytes, the plan needs %zu", ws_bytes, L.total);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipMemset(ws, 0, L.total);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "clearing the workspace");
+  Plan* p = new Plan();
+  p->desc = *d;
+  p->L = L;
+  p->ws = ws;
+  p->ws_bytes = ws_bytes;
+  p->device = dev;
+  {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    p->id = g_next_id++;
+    g_plans[p->id] = p;
+  }
+  st = plan_init_kind(p);
+  if (st) {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    g_plans.erase(p->id);
+    delete p;
+    return st;
+  }
+  *out = reinterpret_cast<pw_plan_t>(p);
+  return PW_OK;
+}
+
+int pw_plan_destroy(pw_plan_t plan) {
+  g_last_error.clear();
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (!is_live(p)) return fail(PW_ERR_STATE, "not a live plan");
+  if (!p->done.empty()) {
+    hipError_t e = hipEventQuery(p->done.back().event);
+    if (e == hipErrorNotReady) return fail(PW_ERR_STATE, "the plan's last call is still running");
+  }
+  p->resolve_times();
+  {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    g_plans.erase(p->id);
+  }
+  for (auto& dn : p->done) (void)hipEventDestroy(dn.event);
+  for (auto e : p->done_pool) (void)hipEventDestroy(e);
+  for (auto e : p->event_pool) (void)hipEventDestroy(e);
+  if (p->aux) (void)hipStreamDestroy(p->aux);
+  plan_release_kind(p);
+  delete p;
+  return PW_OK;
+}
+
+int pw_exchange(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done) {
+  g_last_error.clear();
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (!is_live(p)) return fail(PW_ERR_STATE, "not a live plan");
+  if (!io) return fail(PW_ERR_INVALID, "io is NULL");
+  std::lock_guard<std::mutex> lk(p->mu);
+  if (p->desc.kind == PW_GRAPH_EXCHANGE) return run_exchange(p, io, static_cast<hipStream_t>(stream), done);
+  if (p->desc.kind == PW_GRAPH_MOE) return run_moe(p, io, static_cast<hipStream_t>(stream), done);
+  return fail(PW_ERR_INVALID, "pw_exchange needs an EXCHANGE or MOE plan");
+}
+
+int pw_chain_run(pw_plan_t plan, uint64_t steps, pw_sharded_buf* state, void* aux, void* stream, pw_future_t* done) {
+  g_last_error.clear();
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (!is_live(p)) return fail(PW_ERR_STATE, "not a live plan");
+  std::lock_guard<std::mutex> lk(p->mu);
+  if (p->desc.kind == PW_GRAPH_CHAIN) return run_chain(p, steps, state, aux, static_cast<hipStream_t>(stream), done);
+  if (p->desc.kind == PW_GRAPH_PIPELINE) return run_pipeline(p, steps, state, aux, static_cast<hipStream_t>(stream), done);
+  return fail(PW_ERR_INVALID, "pw_chain_run needs a CHAIN or PIPELINE plan");
+}
+
+static int future_common(pw_future_t f, Plan** out) {
+  Plan* p = lookup(f.plan_id);
+  if (!p) return fail(PW_ERR_STATE, "future of plan %llu: no such live plan", (unsigned long long)f.plan_id);
+  if (f.epoch == 0 || f.epoch > p->epoch) return fail(PW_ERR_STATE, "epoch %llu was never launched", (unsigned long long)f.epoch);
+  if (f.node >= kNodes) return fail(PW_ERR_INVALID, "node %u", f.node);
+  *out = p;
+  return PW_OK;
+}
+
+static int check_fired(Plan* p, pw_future_t f) {
+  uint32_t st = 0;
+  int rc = p->read_status(&st, true);
+  if (rc) return rc;
+  if (st) return status_to_code(st);
+  const uint32_t shard = f.shard < 0 ? 0u : (uint32_t)f.shard;
+  uint32_t v = 0;
+  if ((rc = p->read_epoch(f.node, shard, &v))) return rc;
+  if ((int32_t)(v - (uint32_t)f.epoch) < 0)
+    return fail(PW_ERR_STATE, "future (%u, %d) holds epoch %u < %llu after its call completed", f.node, f.shard, v,
+                (unsigned long long)f.epoch);
+  return PW_OK;
+}
+
+int pw_future_wait(pw_future_t f, int64_t timeout_ns) {
+  g_last_error.clear();
+  Plan* p = nullptr;
+  int rc = future_common(f, &p);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(p->mu);
+  hipEvent_t e = p->event_for(f.epoch);
+  if (!e) return fail(PW_ERR_STATE, "no call recorded");
+  if (timeout_ns < 0) {
+    hipError_t err = hipEventSynchronize(e);
+    if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
+  } else {
+    const auto t0 = std::chrono::steady_clock::now();
+    while (true) {
+      hipError_t err = hipEventQuery(e);
+      if (err == hipSuccess) break;
+      if (err != hipErrorNotReady) return hip_fail(err, "hipEventQuery");
+      const auto el = std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count();
+      if (el >= timeout_ns) return fail(PW_ERR_TIMEOUT, "future not fired within %lld ns", (long long)timeout_ns);
+      std::this_thread::sleep_for(std::chrono::microseconds(20));
+    }
+  }
+  return check_fired(p, f);
+}
+
+int pw_future_query(pw_future_t f, int* fired) {
+  g_last_error.clear();
+  if (!fired) return fail(PW_ERR_INVALID, "fired is NULL");
+  *fired = 0;
+  Plan* p = nullptr;
+  int rc = future_common(f, &p);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(p->mu);
+  hipEvent_t e = p->event_for(f.epoch);
+  hipError_t err = hipEventQuery(e);
+  if (err == hipErrorNotReady) return PW_OK;
+  if (err != hipSuccess) return hip_fail(err, "hipEventQuery");
+  rc = check_fired(p, f);
+  if (rc == PW_OK) *fired = 1;
+  return rc;
+}
+
+int pw_plan_read_futures(pw_plan_t plan, uint32_t* epochs, uint32_t* fires, uint64_t* stamps, size_t capacity,
+                         uint32_t* nodes, uint32_t* width) {
+  g_last_error.clear();
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (!is_live(p)) return fail(PW_ERR_STATE, "not a live plan");
+  std::lock_guard<std::mutex> lk(p->mu);
+  if (nodes) *nodes = kNodes;
+  if (width) *width = p->L.width;
+  const size_t n = (size_t)kNodes * p->L.width;
+  if ((epochs || fires || stamps) && capacity < n) return fail(PW_ERR_INVALID, "capacity %zu < %zu", capacity, n);
+  if (!p->done.empty()) {
+    hipError_t e = hipEventSynchronize(p->done.back().event);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  if (!p->aux) {
+    hipError_t e = hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreate");
+  }
+  auto* base = static_cast<unsigned char*>(p->ws);
+  hipError_t e = hipSuccess;
+  if (epochs) e = hipMemcpyAsync(epochs, base + p->L.fut, n * 4, hipMemcpyDeviceToHost, p->aux);
+  if (e == hipSuccess && fires) e = hipMemcpyAsync(fires, base + p->L.fires, n * 4, hipMemcpyDeviceToHost, p->aux);
+  if (e == hipSuccess && stamps) {
+    if (!(p->desc.flags & PW_FLAG_TRACE)) return fail(PW_ERR_INVALID, "stamps need PW_FLAG_TRACE");
+    e = hipMemcpyAsync(stamps, base + p->L.stamps, n * 8, hipMemcpyDeviceToHost, p->aux);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(p->aux);
+  if (e != hipSuccess) return hip_fail(e, "reading the future table");
+  return PW_OK;
+}
+
+int pw_plan_kernel_times(pw_plan_t plan, pw_kernel_time* out, int max, int* n) {
+  g_last_error.clear();
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (!is_live(p)) return fail(PW_ERR_STATE, "not a live plan");
+  std::lock_guard<std::mutex> lk(p->mu);
+  p->resolve_times();
+  int i = 0;
+  for (auto& kv : p->times) {
+    if (out && i < max) {
+      pw_kernel_time t{};
+      snprintf(t.name, sizeof(t.name), "%s", kv.first.c_str());
+      t.launches = kv.second.launches;
+      t.total_ms = kv.second.total_ms;
+      out[i] = t;
+    }
+    ++i;
+  }
+  if (n) *n = i;
+  return PW_OK;
+}
+
+int pw_plan_reset_times(pw_plan_t plan) {
+  g_last_error.clear();
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (!is_live(p)) return fail(PW_ERR_STATE, "not a live plan");
+  std::lock_guard<std::mutex> lk(p->mu);
+  p->resolve_times();
+  p->times.clear();
+  return PW_OK;
+}
+
+}  // extern "C"

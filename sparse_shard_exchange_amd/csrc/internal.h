@@ -1,0 +1,69 @@
+// Internal host/device declarations of the pw library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pw {
+
+// Device status codes latched in the plan's status word (first error wins).
+enum : uint32_t { ST_OK = 0, ST_BAD_DEST = 1, ST_TIMEOUT = 2 };
+
+// Future-table rows. The table is [kNodes][width] of u32 epochs, a parallel
+// [kNodes][width] of u32 fire counts and, when tracing, of u64 stamps.
+enum : uint32_t { NODE_ARG = 0, NODE_A = 1, NODE_EXCH = 2, NODE_B = 3, NODE_RESULT = 4, NODE_STAGE = 5 };
+constexpr uint32_t kNodes = 6;
+
+enum : uint32_t { OP_IDENTITY = 0, OP_AFFINE = 1, OP_ROWSUM = 2 };
+
+struct Futures {
+  uint32_t* status;     // 1 word
+  uint32_t* epoch;      // [kNodes][width]
+  uint32_t* fires;      // [kNodes][width]
+  uint64_t* stamps;     // [kNodes][width] or nullptr
+  uint32_t width;
+  uint32_t spin_ticks;  // bound of a device wait, in wall-clock ticks (100 MHz)
+};
+
+// Arguments of the exchange kernels (passed by value).
+struct ExchangeArgs {
+  const unsigned char* src;   // payload rows
+  const int32_t* dest;        // [G]
+  unsigned char* dst;         // [G] rows, exchange order
+  int32_t* src_index;         // [G] or null
+  int32_t* slot_of;           // [G] inverse of src_index or null
+  int32_t* counts;            // [num_src][N] or null
+  int64_t* offsets_out;       // [N+1] or null
+  void* b_out;                // B output or null
+  uint64_t G;                 // tuples
+  uint64_t T;                 // tuples per source shard
+  uint32_t N;                 // destinations
+  uint32_t num_src;
+  uint32_t row_bytes;         // payload bytes per tuple
+  uint32_t fanout;            // payload row of tuple g is g / fanout
+  uint32_t tile;              // tuples per workgroup tile (multiple of 256)
+  uint32_t num_tiles;
+  uint32_t nbits;             // bits needed to tell destinations apart
+  uint32_t is_f32;
+  uint32_t a_kind; float a_a, a_b;
+  uint32_t b_kind; float b_a, b_b;
+  uint32_t epoch;
+  uint32_t b_gated;           // 1 if a B kernel follows and fires B futures itself
+  Futures f;
+  uint32_t* arrived;          // [N]
+  uint32_t* expected;         // [N]
+  uint32_t* b_arrived;        // [N]
+  uint32_t* ctl;              // [0] result count, [1] scan done count
+  uint32_t* tile_base;        // [N][num_tiles]
+  int64_t* seg;               // [N+1]
+};
+
+// Launchers (exchange.hip).
+hipError_t launch_hist(const ExchangeArgs& a, hipStream_t s);
+hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s);
+hipError_t launch_src_counts(const ExchangeArgs& a, hipStream_t s);
+hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s);
+hipError_t launch_b(const ExchangeArgs& a, hipStream_t s);
+size_t scatter_lds_bytes(uint32_t N);
+
+}  // namespace pw

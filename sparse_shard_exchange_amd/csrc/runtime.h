@@ -1,0 +1,90 @@
+// Host-side plan object of the pw library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <deque>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/pw.h"
+#include "internal.h"
+
+namespace pw {
+
+// Byte offsets of the tables a plan keeps in the caller's workspace.
+struct Layout {
+  size_t ctl = 0;         // 256 B: [0] status word, [64..] control counters
+  size_t fut = 0;         // [kNodes][width] u32 epochs
+  size_t fires = 0;       // [kNodes][width] u32 fire counts
+  size_t stamps = 0;      // [kNodes][width] u64 (PW_FLAG_TRACE)
+  size_t arrived = 0, expected = 0, b_arrived = 0;  // [N] u32
+  size_t seg = 0;         // [N+1] i64 segment offsets
+  size_t tile_base = 0;   // [N][num_tiles] u32
+  size_t experts = 0, gates = 0, slot_of = 0, hidden_act = 0;  // MOE
+  size_t a_buf = 0;       // CHAIN: A's output buffer
+  size_t pipe_ctl = 0;    // PIPELINE: ticket counters
+  size_t total = 0;
+  uint64_t G = 0;         // tuples per exchange
+  uint32_t tile = 0, num_tiles = 0, width = 0;
+};
+
+struct Plan {
+  uint64_t id = 0;
+  pw_plan_desc desc{};
+  Layout L;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int device = -1;
+  uint64_t epoch = 0;     // last epoch launched
+  std::mutex mu;
+
+  struct Done {
+    uint64_t epoch_hi;
+    hipEvent_t event;
+  };
+  std::deque<Done> done;  // completion events of the latest calls
+  std::vector<hipEvent_t> done_pool;
+  hipStream_t aux = nullptr;  // non-blocking stream for small read-backs
+
+  struct Pending {
+    const char* name;
+    hipEvent_t e0, e1;
+  };
+  struct Acc {
+    uint64_t launches = 0;
+    double total_ms = 0;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> event_pool;
+  std::map<std::string, Acc> times;
+
+  void* kind_state = nullptr;  // per-kind host state
+
+  void launch_begin(const char* name, hipStream_t s);
+  void launch_end(hipStream_t s);
+  hipEvent_t get_event();
+  void resolve_times();
+  int begin_call(hipStream_t s);
+  int end_call(hipStream_t s, uint64_t epoch_hi);
+  hipEvent_t event_for(uint64_t epoch) const;
+  Futures futures() const;
+  int read_status(uint32_t* status, bool clear);
+  int read_epoch(uint32_t node, uint32_t shard, uint32_t* v);
+  unsigned char* base() const { return static_cast<unsigned char*>(ws); }
+};
+
+int fail(int code, const char* fmt, ...);
+int hip_fail(hipError_t e, const char* what);
+
+// graphs.cpp: the CHAIN, MOE and PIPELINE programs.
+int validate_desc_more(const pw_plan_desc* d);
+int plan_init_kind(Plan* p);
+void plan_release_kind(Plan* p);
+int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done);
+int run_chain(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStream_t s, pw_future_t* done);
+int run_pipeline(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStream_t s, pw_future_t* done);
+
+}  // namespace pw
