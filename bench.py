@@ -70,12 +70,43 @@ def traffic_for(kernel_src: str, kernel: str, launches_g: int):
     return rec.get("bytes_per_launch")
 
 
+def chain_sweep(pw, torch, pw_inputs, steps):
+    """Chained Arg -> A -> B -> Result steps (A = x + 1, B = x / 2, 128 fp32 per
+    shard) per second against N, for the three submission modes."""
+    modes = {"chained": pw.PW_CHAIN_CHAINED, "opbyop": pw.PW_CHAIN_OPBYOP, "fused": pw.PW_CHAIN_FUSED}
+    out = {"steps": steps, "elems_per_shard": 128, "steps_per_s": {}, "ns_per_node": {}}
+    for name, mode in modes.items():
+        out["steps_per_s"][name] = {}
+        out["ns_per_node"][name] = {}
+        for n in (8, 64, 256, 2048):
+            ch = pw.Chain(n, 128, mode=mode)
+            st = torch.from_numpy(pw_inputs.chain_state(n, 128)).cuda()
+            pw.future_wait(ch.run(st, min(steps, 1000)), 60_000_000_000)
+            torch.cuda.synchronize()
+            s = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            t0 = time.perf_counter()
+            f = ch.run(st, steps)
+            e1.record(s)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            pw.future_wait(f, 60_000_000_000)
+            sec = max(e0.elapsed_time(e1) * 1e-3, wall)
+            out["steps_per_s"][name][n] = steps / sec
+            out["ns_per_node"][name][n] = sec / (2 * steps) * 1e9
+            ch.plan.destroy()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chain", action="store_true", help="skip the chained-steps sweep")
+    ap.add_argument("--chain-steps", type=int, default=10000)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 plain elementwise copies of 1 GiB (torch.neg) to scale HBM counters")
     args = ap.parse_args()
@@ -162,6 +193,10 @@ def main():
             "traffic": traffic,
         },
     }
+
+    if not args.no_chain:
+        log("chain sweep")
+        result["chain"] = chain_sweep(pw, torch, pw_inputs, args.chain_steps)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)

@@ -300,3 +300,19 @@ class Exchange:
 
     def step(self, x, dest, stream=None) -> pw_future_t:
         return self.plan.exchange(self.io(x, dest), stream)
+
+
+class Chain:
+    """One CHAIN plan: N shards of E fp32, A and B elementwise, run in
+    Chained, OpByOp or Fused mode."""
+
+    def __init__(self, num_shards, elems, a_op=None, b_op=None, mode=PW_CHAIN_CHAINED, flags=0,
+                 spin_limit_ns=0, device="cuda"):
+        self.N, self.E = num_shards, elems
+        self.desc = desc(PW_GRAPH_CHAIN, num_shards, elems, 0, PW_F32,
+                         a_op=a_op or op(PW_OP_AFFINE, 1.0, 1.0), b_op=b_op or op(PW_OP_AFFINE, 0.5, 0.0),
+                         chain_mode=mode, flags=flags, spin_limit_ns=spin_limit_ns)
+        self.plan = Plan(self.desc, device)
+
+    def run(self, state, steps, aux=None, stream=None) -> pw_future_t:
+        return self.plan.chain_run(steps, sharded(state, self.N, self.E, PW_F32), aux, stream)

@@ -1,0 +1,192 @@
+// Chained execution of Arg -> A -> B -> Result over N shards, K steps.
+//
+// PATHWAYS page ("PATHWAYS: Asynchronous Distributed Dataflow for ML"),
+// section 5.1 "Single-controller dispatch overheads": a trivial computation
+// repeated with each result fed into the next, submitted one call per
+// computation (OpByOp), as one call for a whole chain (Chained), or as one
+// node looping internally (Fused). Section 4.5: with static shapes all host
+// work for the chain is done before it runs and the whole subgraph is handed
+// over in one message; section 4.3: under data parallelism each of the N
+// shards sends one tuple to the same shard of the next node.
+//
+// Device mapping: one wave per shard. The plan fixes the placement before the
+// chain starts, so the producer of every future (A[i] of step k, B[i] of step
+// k) and its consumer (B[i] of step k, A[i] of step k + 1) run on the same
+// wave: the gate is a load of the HBM future table ordered after the
+// producer's stores by program order, with no cross-CU fence. Node outputs
+// live in HBM buffers (state for B, a_buf for A), as the page's object store
+// keeps them in accelerator memory.
+#include "device.h"
+
+namespace pw {
+
+namespace {
+
+__device__ __forceinline__ float body(uint32_t kind, float a, float b, float x) {
+  return kind == OP_AFFINE ? fmaf(a, x, b) : x;
+}
+
+// Gate on a future this wave produced itself. Lane 0 both fires and reads
+// every future of its shard, so program order makes the fire visible to the
+// read and a relaxed load suffices; each lane only reads payload elements it
+// wrote itself. The result is broadcast to the wave. Bounded like every
+// device wait.
+__device__ __forceinline__ bool await_local_lane0(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
+  const uint32_t* p = &f.epoch[node * f.width + shard];
+  if (epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT), epoch)) return true;
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    if (epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT), epoch)) return true;
+    if (wall_clock64() - t0 > f.spin_ticks) {
+      latch(f.status, ST_TIMEOUT);
+      return false;
+    }
+  }
+}
+
+__device__ __forceinline__ bool await_local(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch,
+                                            uint32_t lane) {
+  bool ok = true;
+  if (lane == 0) ok = await_local_lane0(f, node, shard, epoch);
+  return __shfl((int)ok, 0, 64) != 0;
+}
+
+__device__ __forceinline__ void finish_wave(const ChainArgs& a, uint32_t lane) {
+  if (lane == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(a.done_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == a.done_target) fire(a.f, NODE_RESULT, 0, a.epoch0 + a.steps, false);
+  }
+}
+
+// One node (A or B) of one shard: out[e] = body(in[e]), E elements, lanes
+// striding by 64 with two elements in flight per lane.
+__device__ __forceinline__ void node_body(const float* in, float* out, uint32_t E, uint32_t lane, uint32_t kind,
+                                          float ca, float cb) {
+  uint32_t e = lane;
+  for (; e + 64 < E; e += 128) {
+    const float x0 = in[e], x1 = in[e + 64];
+    out[e] = body(kind, ca, cb, x0);
+    out[e + 64] = body(kind, ca, cb, x1);
+  }
+  if (e < E) out[e] = body(kind, ca, cb, in[e]);
+}
+
+// Fire a future whose only consumer is this wave (lane 0 calls it): a plain
+// store; the fire count and the stamp are kept in registers by the caller and
+// written once when the launch ends.
+__device__ __forceinline__ void fire_local(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
+  __hip_atomic_store(&f.epoch[node * f.width + shard], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// One node of one shard with the gate folded in: lane 0 reads the input
+// future while every lane reads its input elements; the elements are used
+// only once the future is known to have fired (else they are read again
+// after the wait).
+__device__ __forceinline__ bool gated_node(const ChainArgs& a, uint32_t in_node, uint32_t shard, uint32_t need,
+                                           const float* in, float* out, uint32_t lane, uint32_t kind, float ca,
+                                           float cb) {
+  uint32_t v = need;
+  if (lane == 0) v = __hip_atomic_load(&a.f.epoch[in_node * a.f.width + shard], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
+  if (a.E == 128) {
+    float2 x = reinterpret_cast<const float2*>(in)[lane];
+    const bool ready = __shfl((int)epoch_reached(v, need), 0, 64) != 0;
+    if (!ready) {
+      if (!await_local(a.f, in_node, shard, need, lane)) return false;
+      x = reinterpret_cast<const float2*>(in)[lane];
+    }
+    x.x = body(kind, ca, cb, x.x);
+    x.y = body(kind, ca, cb, x.y);
+    reinterpret_cast<float2*>(out)[lane] = x;
+    return true;
+  }
+  const bool ready = __shfl((int)epoch_reached(v, need), 0, 64) != 0;
+  if (!ready && !await_local(a.f, in_node, shard, need, lane)) return false;
+  node_body(in, out, a.E, lane, kind, ca, cb);
+  return true;
+}
+
+__global__ __launch_bounds__(256) void k_chain_chained(ChainArgs a) {
+  const uint32_t i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (i >= a.N) return;  // whole waves only; no workgroup barrier below
+  float* st = a.state + (uint64_t)i * a.E;
+  float* ab = a.abuf + (uint64_t)i * a.E;
+  uint32_t done = 0;
+  for (uint32_t j = 1; j <= a.steps; ++j) {
+    const uint32_t k = a.epoch0 + j;
+    // A of step k consumes the Result of step k - 1 (B[i]; epoch0 = the Arg)
+    if (!gated_node(a, NODE_B, i, k - 1, st, ab, lane, a.a_kind, a.a_a, a.a_b)) break;
+    if (lane == 0) fire_local(a.f, NODE_A, i, k);
+    if (!gated_node(a, NODE_A, i, k, ab, st, lane, a.b_kind, a.b_a, a.b_b)) break;
+    if (lane == 0) fire_local(a.f, NODE_B, i, k);
+    done = j;
+  }
+  if (lane == 0 && done) {
+    for (uint32_t node : {NODE_A, NODE_B}) {
+      const uint32_t idx = node * a.f.width + i;
+      __hip_atomic_fetch_add(&a.f.fires[idx], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.f.stamps) a.f.stamps[idx] = wall_clock64();
+    }
+  }
+  finish_wave(a, lane);
+}
+
+// OpByOp: one launch per node per step. The input future was fired by the
+// previous launch, so stream order already made it (and its buffer) visible.
+__global__ __launch_bounds__(256) void k_chain_node(ChainArgs a) {
+  const uint32_t i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (i >= a.N) return;
+  const uint32_t k = a.epoch0 + a.steps;  // the step this node belongs to
+  float* st = a.state + (uint64_t)i * a.E;
+  float* ab = a.abuf + (uint64_t)i * a.E;
+  if (a.node == NODE_A) {
+    if (!await_local(a.f, NODE_B, i, k - 1, lane)) return;
+    node_body(st, ab, a.E, lane, a.a_kind, a.a_a, a.a_b);
+    if (lane == 0) fire(a.f, NODE_A, i, k, false);
+  } else {
+    if (!await_local(a.f, NODE_A, i, k, lane)) return;
+    node_body(ab, st, a.E, lane, a.b_kind, a.b_a, a.b_b);
+    if (lane == 0) fire(a.f, NODE_B, i, k, false);
+    if (a.done_ctr) finish_wave(a, lane);
+  }
+}
+
+// Fused: one node per shard looping over every step in registers; only the
+// final buffers and futures are written.
+__global__ __launch_bounds__(256) void k_chain_fused(ChainArgs a) {
+  const uint32_t i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (i >= a.N) return;
+  float* st = a.state + (uint64_t)i * a.E;
+  float* ab = a.abuf + (uint64_t)i * a.E;
+  if (!await_local(a.f, NODE_B, i, a.epoch0, lane)) return;
+  for (uint32_t e = lane; e < a.E; e += 64) {
+    float x = st[e], y = x;
+    for (uint32_t j = 0; j < a.steps; ++j) {
+      y = body(a.a_kind, a.a_a, a.a_b, x);
+      x = body(a.b_kind, a.b_a, a.b_b, y);
+    }
+    ab[e] = y;
+    st[e] = x;
+  }
+  if (lane == 0) {
+    fire(a.f, NODE_A, i, a.epoch0 + a.steps, false);
+    fire(a.f, NODE_B, i, a.epoch0 + a.steps, false);
+  }
+  finish_wave(a, lane);
+}
+
+}  // namespace
+
+hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s) {
+  const dim3 grid((a.N + 3) / 4), block(256);
+  if (mode == 0)
+    hipLaunchKernelGGL(k_chain_chained, grid, block, 0, s, a);
+  else if (mode == 2)
+    hipLaunchKernelGGL(k_chain_fused, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(k_chain_node, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pw

@@ -58,6 +58,21 @@ struct ExchangeArgs {
   int64_t* seg;               // [N+1]
 };
 
+// Arguments of the chain kernels (chain.hip).
+struct ChainArgs {
+  float* state;      // [N][E]: Arg of step 1, Result of the last step
+  float* abuf;       // [N][E]: A's output
+  uint32_t N, E;
+  float a_a, a_b, b_a, b_b;
+  uint32_t a_kind, b_kind;
+  uint32_t epoch0;   // epoch (step) before this call
+  uint32_t steps;
+  uint32_t node;     // OpByOp: NODE_A or NODE_B
+  uint32_t done_target;  // Result fires when the done counter reaches it
+  uint32_t* done_ctr;
+  Futures f;
+};
+
 // Launchers (exchange.hip).
 hipError_t launch_hist(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s);
@@ -65,5 +80,7 @@ hipError_t launch_src_counts(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_b(const ExchangeArgs& a, hipStream_t s);
 size_t scatter_lds_bytes(uint32_t N);
+// mode: 0 chained (one launch, all steps), 1 one node (OpByOp), 2 fused.
+hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);
 
 }  // namespace pw

@@ -107,3 +107,21 @@ def test_calls_on_dead_plans_and_futures():
     assert pw.lib.pw_exchange(None, C.byref(io), None, C.byref(fut)) == pw.PW_ERR_STATE
     st = pw.pw_sharded_buf()
     assert pw.lib.pw_chain_run(None, 1, C.byref(st), None, None, C.byref(fut)) == pw.PW_ERR_STATE
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_shards=0), dict(tuples_per_shard=0), dict(dtype=pw.PW_BF16),
+    dict(a_op=pw.op(pw.PW_OP_ROWSUM)), dict(chain_mode=7),
+])
+def test_chain_validation(bad):
+    base = dict(kind=pw.PW_GRAPH_CHAIN, num_shards=2048, tuples_per_shard=128,
+                a_op=pw.op(pw.PW_OP_AFFINE, 1, 1), b_op=pw.op(pw.PW_OP_AFFINE, 0.5, 0))
+    base.update(bad)
+    with pytest.raises(pw.PwError) as e:
+        pw.workspace_size(pw.desc(**base))
+    assert e.value.code == pw.PW_ERR_INVALID
+
+
+def test_chain_sizing():
+    d = pw.desc(pw.PW_GRAPH_CHAIN, 2048, 128, a_op=pw.op(pw.PW_OP_AFFINE, 1, 1))
+    assert pw.workspace_size(d) >= 2048 * 128 * 4

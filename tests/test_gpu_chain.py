@@ -1,0 +1,88 @@
+"""GPU parity of the chained Arg -> A -> B -> Result executor (PATHWAYS page,
+section 5.1, chained and fused submission; sections 4.4-4.5, futures) against
+the CPU oracle, in all three modes. A = x + 1 and B = x / 2 are single fp32
+roundings, so every step is bit-exact; the Result after 10,000 steps is 1.0
+everywhere (the fp32 fixed point)."""
+import numpy as np
+import pytest
+import torch
+
+import pw_inputs
+from oracle import chain as oc
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["chained", "opbyop", "fused"]
+
+
+def _mode(pw, name):
+    return {"chained": pw.PW_CHAIN_CHAINED, "opbyop": pw.PW_CHAIN_OPBYOP, "fused": pw.PW_CHAIN_FUSED}[name]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("n,e", [(1, 128), (8, 128), (64, 1), (256, 100), (2048, 128), (300, 200)])
+def test_chain_steps_bit_exact(gpu, mode, n, e):
+    pw = gpu
+    print(f"chain {mode} N={n} E={e}", flush=True)
+    x0 = pw_inputs.chain_state(n, e)
+    ref = oc.chain(x0, 40, record=40)
+    ch = pw.Chain(n, e, mode=_mode(pw, mode))
+    st = torch.from_numpy(x0).cuda()
+    # one step per call for the first 8 steps, then 32 steps in one call
+    for k in range(8):
+        f = ch.run(st, 1)
+        pw.future_wait(f, 10_000_000_000)
+        assert np.array_equal(st.cpu().numpy().view(np.uint32), ref.history[k].view(np.uint32)), k
+    f = ch.run(st, 32)
+    pw.future_wait(f, 10_000_000_000)
+    assert f.epoch == 40
+    assert np.array_equal(st.cpu().numpy().view(np.uint32), ref.state.view(np.uint32))
+    ep, fi, _ = ch.plan.read_futures()
+    assert np.all(ep[pw.PW_NODE_A, :n] == 40) and np.all(ep[pw.PW_NODE_B, :n] == 40)
+    calls = 9
+    want = calls if mode == "fused" else 40
+    assert np.all(fi[pw.PW_NODE_A, :n] == want) and np.all(fi[pw.PW_NODE_B, :n] == want)
+    assert ep[pw.PW_NODE_RESULT, 0] == 40 and fi[pw.PW_NODE_RESULT, 0] == calls
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chain_full_size_10000_steps(gpu, mode):
+    """2048 shards x 128 fp32, 10,000 steps: bit-exact with the oracle (all 1.0)."""
+    pw = gpu
+    x0 = pw_inputs.chain_state(2048, 128)
+    ref = oc.chain(x0, 10000)
+    ch = pw.Chain(2048, 128, mode=_mode(pw, mode), flags=pw.PW_FLAG_TRACE)
+    st = torch.from_numpy(x0).cuda()
+    f = ch.run(st, 10000)
+    pw.future_wait(f, 60_000_000_000)
+    out = st.cpu().numpy()
+    assert np.array_equal(out.view(np.uint32), ref.state.view(np.uint32))
+    assert np.all(out == np.float32(1.0))
+    ep, fi, stamps = ch.plan.read_futures(trace=True)
+    assert np.all(ep[pw.PW_NODE_B, :2048] == 10000)
+    if mode != "fused":
+        assert np.all(fi[pw.PW_NODE_A, :2048] == 10000) and np.all(fi[pw.PW_NODE_B, :2048] == 10000)
+        # the last A of each shard fired before its last B, both before Result
+        assert np.all(stamps[pw.PW_NODE_A, :2048] <= stamps[pw.PW_NODE_B, :2048])
+        assert np.all(stamps[pw.PW_NODE_B, :2048] <= stamps[pw.PW_NODE_RESULT, 0])
+
+
+def test_chain_aux_receives_last_a(gpu):
+    pw = gpu
+    x0 = pw_inputs.chain_state(16, 64)
+    ref = oc.chain(x0, 3, record=3)
+    ch = pw.Chain(16, 64)
+    st = torch.from_numpy(x0).cuda()
+    aux = torch.empty_like(st)
+    pw.future_wait(ch.run(st, 3, aux=aux), 10_000_000_000)
+    last_a = (ref.history[1] + np.float32(1))           # A of step 3 reads the Result of step 2
+    assert np.array_equal(aux.cpu().numpy().view(np.uint32), last_a.view(np.uint32))
+
+
+def test_chain_rejects_bad_state(gpu):
+    pw = gpu
+    ch = pw.Chain(8, 128)
+    st = torch.zeros((8, 64), device="cuda")
+    with pytest.raises(pw.PwError) as e:
+        ch.run(st, 1)
+    assert e.value.code == pw.PW_ERR_INVALID
