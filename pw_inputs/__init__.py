@@ -157,11 +157,16 @@ def moe(tokens: int = 131072, d: int = 1024, experts: int = 64, hidden: int = 40
     """Tokens ~ N(0, 1), router and expert weights ~ N(0, 0.02), all bf16
     (drawn in fp32, then torch's round-to-nearest-even cast)."""
     key = (tokens, d, experts, hidden, variant)
-    x = _bf16(rng_for(4, 0, *key).standard_normal(size=(tokens, d), dtype=np.float32))
+    normal = lambda r, o: r.standard_normal(size=o.shape, dtype=np.float32, out=o)
+    x = _bf16(_fill_chunked((tokens, d), 4, (0, *key), normal))
     wr = _bf16(rng_for(4, 1, *key).standard_normal(size=(d, experts), dtype=np.float32) * np.float32(0.02))
     if with_experts:
-        w1 = _bf16(rng_for(4, 2, *key).standard_normal(size=(experts, d, hidden), dtype=np.float32) * np.float32(0.02))
-        w2 = _bf16(rng_for(4, 3, *key).standard_normal(size=(experts, hidden, d), dtype=np.float32) * np.float32(0.02))
+        w1 = _fill_chunked((experts * d, hidden), 4, (2, *key), normal)
+        w1 *= np.float32(0.02)
+        w1 = _bf16(w1).reshape(experts, d, hidden)
+        w2 = _fill_chunked((experts * hidden, d), 4, (3, *key), normal)
+        w2 *= np.float32(0.02)
+        w2 = _bf16(w2).reshape(experts, hidden, d)
     else:
         w1 = w2 = None
     return MoEInputs(x, wr, w1, w2, meta={"workload": "moe", "key": key})
@@ -178,6 +183,8 @@ def pipeline(stages: int = 16, microbatches: int = 64, rows: int = 2048, d: int 
              variant: int = 0) -> PipelineInputs:
     """Microbatches ~ N(0, 1), per-stage weights ~ N(0, 0.02), all bf16."""
     key = (stages, microbatches, rows, d, variant)
-    x = _bf16(rng_for(5, 0, *key).standard_normal(size=(microbatches, rows, d), dtype=np.float32))
+    x = _fill_chunked((microbatches * rows, d), 5, (0, *key),
+                      lambda r, o: r.standard_normal(size=o.shape, dtype=np.float32, out=o))
+    x = _bf16(x).reshape(microbatches, rows, d)
     w = _bf16(rng_for(5, 1, *key).standard_normal(size=(stages, d, d), dtype=np.float32) * np.float32(0.02))
     return PipelineInputs(x, w, meta={"workload": "pipeline", "key": key})

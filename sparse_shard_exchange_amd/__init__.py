@@ -316,3 +316,66 @@ class Chain:
 
     def run(self, state, steps, aux=None, stream=None) -> pw_future_t:
         return self.plan.chain_run(steps, sharded(state, self.N, self.E, PW_F32), aux, stream)
+
+
+class Pipeline:
+    """One PIPELINE plan: S stages of h = bf16(GELU(h . W_s)) over M microbatches
+    of rows x d bf16, GPipe fill/drain, one launch per pass. W is [S][d][d]
+    bf16, stored [in][out] (borrowed: keep it alive while the plan lives)."""
+
+    def __init__(self, w, microbatches, rows, flags=0, spin_limit_ns=0, device="cuda"):
+        import torch
+        assert w.dtype == torch.bfloat16 and w.dim() == 3 and w.shape[1] == w.shape[2]
+        self.w = w
+        self.S, self.d = w.shape[0], w.shape[1]
+        self.M, self.R = microbatches, rows
+        self.desc = desc(PW_GRAPH_PIPELINE, self.S, rows, self.d, PW_BF16, microbatches=microbatches,
+                         flags=flags, spin_limit_ns=spin_limit_ns, w1=w)
+        self.plan = Plan(self.desc, device)
+
+    def run(self, x, acts, stream=None) -> pw_future_t:
+        """x: [M][rows][d] bf16; acts: [S][M][rows][d] bf16 receives every stage output."""
+        return self.plan.chain_run(1, sharded(x, self.M, self.d, PW_BF16), acts, stream)
+
+
+class MoE:
+    """One MOE plan: router d x E + top-2 softmax gate, dispatch exchange to E
+    expert shards, expert FFN d -> hidden -> d with GELU, gated combine.
+    Weights (bf16, stored [in][out]) are borrowed: keep them alive."""
+
+    def __init__(self, w_router, w1, w2, tokens, num_src_shards=64, flags=0, spin_limit_ns=0,
+                 want_logits=True, want_counts=False, device="cuda"):
+        import torch
+        self.d, self.E = w_router.shape
+        self.hidden = w1.shape[2]
+        assert tokens % num_src_shards == 0
+        self.T, self.S = tokens, num_src_shards
+        self.w = (w_router, w1, w2)
+        self.desc = desc(PW_GRAPH_MOE, self.E, tokens // num_src_shards, self.d, PW_BF16,
+                         num_src_shards=num_src_shards, top_k=2, hidden=self.hidden, flags=flags,
+                         spin_limit_ns=spin_limit_ns, w_router=w_router, w1=w1, w2=w2)
+        self.plan = Plan(self.desc, device)
+        bf = torch.bfloat16
+        self.xd = torch.empty((2 * tokens, self.d), dtype=bf, device=device)
+        self.y = torch.empty((2 * tokens, self.d), dtype=bf, device=device)
+        self.out = torch.empty((tokens, self.d), dtype=bf, device=device)
+        self.offsets = torch.empty(self.E + 1, dtype=torch.int64, device=device)
+        self.src_index = torch.empty(2 * tokens, dtype=torch.int32, device=device)
+        self.experts = torch.empty((tokens, 2), dtype=torch.int32, device=device)
+        self.gates = torch.empty((tokens, 2), dtype=torch.float32, device=device)
+        self.logits = torch.empty((tokens, self.E), dtype=torch.float32, device=device) if want_logits else None
+        self.counts = torch.empty((num_src_shards, self.E), dtype=torch.int32, device=device) if want_counts else None
+
+    def step(self, x, stream=None) -> pw_future_t:
+        io = pw_exchange_io()
+        io.src = sharded(x, self.S, self.d, PW_BF16)
+        io.dest = None
+        io.dst = sharded(self.xd, self.E, self.d, PW_BF16, self.offsets)
+        io.src_index = _ptr(self.src_index)
+        io.counts = _ptr(self.counts)
+        io.b_out = _ptr(self.y)
+        io.result = _ptr(self.out)
+        io.logits = _ptr(self.logits)
+        io.experts = _ptr(self.experts)
+        io.gates = _ptr(self.gates)
+        return self.plan.exchange(io, stream)

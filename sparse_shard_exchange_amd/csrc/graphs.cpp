@@ -1,6 +1,9 @@
 // CHAIN, MOE and PIPELINE programs of the pw library (host side).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "runtime.h"
 
 namespace pw {
@@ -8,7 +11,8 @@ namespace pw {
 namespace {
 
 struct KindState {
-  uint64_t calls = 0;  // completed-call counter target of the device done counter
+  uint64_t calls = 0;  // calls launched so far (targets of the cumulative device counters)
+  uint32_t grid = 0;   // PIPELINE: persistent workgroups (one per CU)
 };
 
 }  // namespace
@@ -28,16 +32,65 @@ int validate_desc_more(const pw_plan_desc* d) {
       if (d->chain_mode > PW_CHAIN_FUSED) return fail(PW_ERR_INVALID, "CHAIN: unknown chain_mode %u", d->chain_mode);
       return PW_OK;
     }
-    case PW_GRAPH_MOE:
-    case PW_GRAPH_PIPELINE:
-      return fail(PW_ERR_UNSUPPORTED, "graph kind %u is not built yet", d->kind);
+    case PW_GRAPH_PIPELINE: {
+      if (d->num_shards == 0 || d->num_shards > 255) return fail(PW_ERR_INVALID, "PIPELINE: stages must be in [1, 255]");
+      if (d->microbatches == 0 || d->microbatches > 255) return fail(PW_ERR_INVALID, "PIPELINE: microbatches must be in [1, 255]");
+      if (d->tuples_per_shard == 0 || d->tuples_per_shard > 255 * 256)
+        return fail(PW_ERR_INVALID, "PIPELINE: rows per microbatch must be in [1, 65280]");
+      if (d->payload_elems == 0 || d->payload_elems % 256 || d->payload_elems > 255 * 256)
+        return fail(PW_ERR_INVALID, "PIPELINE: width d must be a positive multiple of 256");
+      if (d->dtype != PW_BF16) return fail(PW_ERR_INVALID, "PIPELINE: activations and weights are bf16");
+      if (!d->w1) return fail(PW_ERR_INVALID, "PIPELINE: stage weights (w1) are required");
+      const uint64_t elems = (uint64_t)d->num_shards * d->microbatches * d->tuples_per_shard * d->payload_elems;
+      if (elems > (1ull << 40)) return fail(PW_ERR_INVALID, "PIPELINE: too large");
+      return PW_OK;
+    }
+    case PW_GRAPH_MOE: {
+      if (d->num_shards < 2 || d->num_shards > 64) return fail(PW_ERR_INVALID, "MOE: experts must be in [2, 64]");
+      if (d->top_k != 2) return fail(PW_ERR_UNSUPPORTED, "MOE: only top-2 routing is built");
+      const uint64_t S = d->num_src_shards ? d->num_src_shards : d->num_shards;
+      const uint64_t tokens = S * d->tuples_per_shard;
+      if (tokens == 0 || tokens > (1ull << 28)) return fail(PW_ERR_INVALID, "MOE: token count must be in [1, 2^28]");
+      if (d->payload_elems == 0 || d->payload_elems % 256 || d->payload_elems > 16384)
+        return fail(PW_ERR_INVALID, "MOE: d must be a positive multiple of 256, <= 16384");
+      if (d->hidden == 0 || d->hidden % 256 || d->hidden > 65536)
+        return fail(PW_ERR_INVALID, "MOE: hidden must be a positive multiple of 256");
+      if (d->dtype != PW_BF16) return fail(PW_ERR_INVALID, "MOE: tokens and weights are bf16");
+      if (!d->w_router || !d->w1 || !d->w2) return fail(PW_ERR_INVALID, "MOE: w_router, w1 and w2 are required");
+      if ((uint64_t)d->payload_elems * d->hidden * 2 > 0xffffffffull)
+        return fail(PW_ERR_INVALID, "MOE: one expert weight must stay below 4 GiB");
+      return PW_OK;
+    }
     default:
       return fail(PW_ERR_INVALID, "unknown graph kind %u", d->kind);
   }
 }
 
 int plan_init_kind(Plan* p) {
-  p->kind_state = new KindState();
+  auto* ks = new KindState();
+  p->kind_state = ks;
+  if (p->desc.kind == PW_GRAPH_PIPELINE) {
+    // GPipe lock-step claim order: tick t = s + m ascending, then stage,
+    // row block, column block. Uploaded once with the plan.
+    const pw_plan_desc& d = p->desc;
+    const uint32_t S = d.num_shards, M = d.microbatches;
+    const uint32_t RB = (uint32_t)((d.tuples_per_shard + 255) / 256), CT = d.payload_elems / 256;
+    std::vector<uint32_t> order;
+    order.reserve((size_t)S * M * RB * CT);
+    for (uint32_t t = 0; t + 1 < S + M; ++t)
+      for (uint32_t s = 0; s < S; ++s) {
+        if (t < s || t - s >= M) continue;
+        const uint32_t m = t - s;
+        for (uint32_t r = 0; r < RB; ++r)
+          for (uint32_t c = 0; c < CT; ++c) order.push_back(s | m << 8 | r << 16 | c << 24);
+      }
+    hipError_t e = hipMemcpy(p->base() + p->L.order, order.data(), order.size() * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "uploading the pipeline order");
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    ks->grid = (uint32_t)std::max(1, cus);
+  }
   return PW_OK;
 }
 
@@ -46,8 +99,106 @@ void plan_release_kind(Plan* p) {
   p->kind_state = nullptr;
 }
 
-int run_moe(Plan*, const pw_exchange_io*, hipStream_t, pw_future_t*) {
-  return fail(PW_ERR_UNSUPPORTED, "MOE is not built yet");
+// -------------------------------------------------------------------- MOE
+int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done) {
+  const pw_plan_desc& d = p->desc;
+  const Layout& L = p->L;
+  const uint32_t E = d.num_shards;
+  const uint32_t S = d.num_src_shards ? d.num_src_shards : E;
+  const uint64_t tokens = (uint64_t)S * d.tuples_per_shard;
+  const uint32_t D = d.payload_elems;
+  if (!io->src.base || io->src.num_tuples != tokens || io->src.elems_per_tuple != D || io->src.dtype != PW_BF16)
+    return fail(PW_ERR_INVALID, "src must be %llu tokens x %u bf16", (unsigned long long)tokens, D);
+  if (!io->dst.base || io->dst.num_tuples < 2 * tokens || io->dst.elems_per_tuple != D || io->dst.dtype != PW_BF16)
+    return fail(PW_ERR_INVALID, "dst must hold 2 x %llu dispatched rows of %u bf16", (unsigned long long)tokens, D);
+  if (!io->b_out || !io->result) return fail(PW_ERR_INVALID, "b_out (expert outputs) and result are required");
+  if (io->dest) return fail(PW_ERR_INVALID, "MOE routes with its router: dest must be NULL");
+  const uintptr_t al = (uintptr_t)io->src.base | (uintptr_t)io->dst.base | (uintptr_t)io->b_out | (uintptr_t)io->result;
+  if (al & 15u) return fail(PW_ERR_INVALID, "buffers must be 16-byte aligned");
+  int st = p->begin_call(s);
+  if (st) return st;
+  unsigned char* base = p->base();
+
+  MoeArgs m{};
+  m.x = static_cast<const __bf16*>(io->src.base);
+  m.w_router = static_cast<const __bf16*>(d.w_router);
+  m.w1 = static_cast<const __bf16*>(d.w1);
+  m.w2 = static_cast<const __bf16*>(d.w2);
+  m.xd = static_cast<__bf16*>(io->dst.base);
+  m.h = reinterpret_cast<__bf16*>(base + L.hidden_act);
+  m.y = static_cast<__bf16*>(io->b_out);
+  m.out = static_cast<__bf16*>(io->result);
+  m.logits = io->logits;
+  m.experts = io->experts ? io->experts : reinterpret_cast<int32_t*>(base + L.experts);
+  m.gates = io->gates ? io->gates : reinterpret_cast<float*>(base + L.gates);
+  m.slot_of = reinterpret_cast<int32_t*>(base + L.slot_of);
+  m.tokens = tokens;
+  m.d = D;
+  m.hidden = d.hidden;
+  m.E = E;
+  m.max_row_blocks = (uint32_t)((2 * tokens + 255) / 256 + E);
+  m.seg = reinterpret_cast<const int64_t*>(base + L.seg);
+  m.rb_start = reinterpret_cast<uint32_t*>(base + L.rb_start);
+  m.b_done = reinterpret_cast<uint32_t*>(base + L.b_done);
+  m.ctl = reinterpret_cast<uint32_t*>(base + L.ctl + 64);
+  m.epoch = (uint32_t)(p->epoch + 1);
+  m.f = p->futures();
+
+  ExchangeArgs a{};
+  a.src = static_cast<const unsigned char*>(io->src.base);
+  a.dest = m.experts;
+  a.dst = static_cast<unsigned char*>(io->dst.base);
+  a.src_index = io->src_index;
+  a.slot_of = m.slot_of;
+  a.counts = io->counts;
+  a.offsets_out = io->dst.shard_offsets;
+  a.b_out = nullptr;
+  a.G = L.G;
+  a.T = 2 * d.tuples_per_shard;
+  a.N = E;
+  a.num_src = S;
+  a.row_bytes = 2 * D;
+  a.fanout = 2;
+  a.tile = L.tile;
+  a.num_tiles = L.num_tiles;
+  a.nbits = 0;
+  while ((1u << a.nbits) < E) ++a.nbits;
+  a.is_f32 = 0;
+  a.a_kind = OP_IDENTITY;
+  a.b_kind = OP_IDENTITY;
+  a.epoch = m.epoch;
+  a.b_gated = 1;  // the expert FFN fires B
+  a.f = m.f;
+  a.arrived = reinterpret_cast<uint32_t*>(base + L.arrived);
+  a.expected = reinterpret_cast<uint32_t*>(base + L.expected);
+  a.b_arrived = reinterpret_cast<uint32_t*>(base + L.b_arrived);
+  a.ctl = m.ctl;
+  a.tile_base = reinterpret_cast<uint32_t*>(base + L.tile_base);
+  a.seg = reinterpret_cast<int64_t*>(base + L.seg);
+
+  hipError_t e = hipSuccess;
+#define PW_STEP(label, call)           \
+  do {                                 \
+    p->launch_begin(label, s);         \
+    e = (call);                        \
+    p->launch_end(s);                  \
+    if (e != hipSuccess) return hip_fail(e, "launch " label); \
+  } while (0)
+  PW_STEP("router", launch_router(m, s));
+  if (io->counts) PW_STEP("src_counts", launch_src_counts(a, s));
+  PW_STEP("hist", launch_hist(a, s));
+  PW_STEP("scan", launch_scan(a, s));
+  PW_STEP("scatter", launch_scatter(a, s));
+  PW_STEP("moe_prefix", launch_moe_prefix(m, s));
+  PW_STEP("ffn1", launch_ffn(m, false, s));
+  PW_STEP("ffn2", launch_ffn(m, true, s));
+  PW_STEP("combine", launch_combine(m, s));
+#undef PW_STEP
+  p->epoch += 1;
+  st = p->end_call(s, p->epoch);
+  if (st) return st;
+  if (done) *done = pw_future_t{p->id, PW_NODE_RESULT, -1, p->epoch};
+  return PW_OK;
 }
 
 // ------------------------------------------------------------------ CHAIN
@@ -110,8 +261,49 @@ int run_chain(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStre
   return PW_OK;
 }
 
-int run_pipeline(Plan*, uint64_t, pw_sharded_buf*, void*, hipStream_t, pw_future_t*) {
-  return fail(PW_ERR_UNSUPPORTED, "PIPELINE is not built yet");
+// --------------------------------------------------------------- PIPELINE
+int run_pipeline(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStream_t s, pw_future_t* done) {
+  const pw_plan_desc& d = p->desc;
+  const uint32_t S = d.num_shards, M = d.microbatches, R = (uint32_t)d.tuples_per_shard, D = d.payload_elems;
+  if (steps != 1) return fail(PW_ERR_INVALID, "PIPELINE runs one pass per call (steps = 1)");
+  if (!state || !state->base || !aux) return fail(PW_ERR_INVALID, "state (microbatches) and aux (stage outputs) are required");
+  if (state->num_tuples != (uint64_t)M * R || state->elems_per_tuple != D || state->dtype != PW_BF16)
+    return fail(PW_ERR_INVALID, "state must be %u microbatches x %u rows x %u bf16", M, R, D);
+  if (((uintptr_t)state->base | (uintptr_t)aux) & 15u) return fail(PW_ERR_INVALID, "buffers must be 16-byte aligned");
+  int st = p->begin_call(s);
+  if (st) return st;
+  auto* ks = static_cast<KindState*>(p->kind_state);
+  const uint32_t RB = (R + 255) / 256, CT = D / 256;
+  const uint32_t total = S * M * RB * CT;
+  const uint64_t call = ks->calls + 1;
+
+  PipeArgs a{};
+  a.x = static_cast<const __bf16*>(state->base);
+  a.acts = static_cast<__bf16*>(aux);
+  a.w = static_cast<const __bf16*>(d.w1);
+  a.order = reinterpret_cast<const uint32_t*>(p->base() + p->L.order);
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(p->base() + p->L.pipe_ctl);
+  a.ticket = ctl;
+  a.done_ctr = ctl + 1;
+  a.ticket_base = (uint32_t)(ks->calls * (uint64_t)total);
+  a.rb_ctr = reinterpret_cast<uint32_t*>(p->base() + p->L.rb_ctr);
+  a.item_ctr = reinterpret_cast<uint32_t*>(p->base() + p->L.item_ctr);
+  a.rb_target = (uint32_t)(call * CT);
+  a.item_target = (uint32_t)(call * RB);
+  a.done_target = (uint32_t)(call * total);
+  a.S = S; a.M = M; a.rows = R; a.d = D; a.RB = RB; a.CT = CT; a.total_tiles = total;
+  a.epoch = (uint32_t)(p->epoch + 1);
+  a.f = p->futures();
+  p->launch_begin("pipeline", s);
+  hipError_t e = launch_pipeline(a, s);
+  p->launch_end(s);
+  if (e != hipSuccess) return hip_fail(e, "launch pipeline");
+  ks->calls += 1;
+  p->epoch += 1;
+  st = p->end_call(s, p->epoch);
+  if (st) return st;
+  if (done) *done = pw_future_t{p->id, PW_NODE_RESULT, -1, p->epoch};
+  return PW_OK;
 }
 
 }  // namespace pw

@@ -23,7 +23,7 @@
 #include <unordered_map>
 #include <vector>
 
-#include "../../include/pw.h"
+#include "pw.h"
 #include "internal.h"
 #include "runtime.h"
 
@@ -119,6 +119,8 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
         L.gates = c.take(tokens * d.top_k * 4);
         L.slot_of = c.take(L.G * 4);
         L.hidden_act = c.take(L.G * (uint64_t)d.hidden * 2);
+        L.rb_start = c.take((size_t)(N + 1) * 4);
+        L.b_done = c.take((size_t)N * 4);
       }
       break;
     }
@@ -131,11 +133,16 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
       break;
     }
     case PW_GRAPH_PIPELINE: {
-      L.width = d.num_shards * d.microbatches;
+      const uint64_t S = d.num_shards, M = d.microbatches;
+      const uint64_t RB = (d.tuples_per_shard + 255) / 256, CT = d.payload_elems / 256;
+      L.width = (uint32_t)(S * M);
       L.fut = c.take((size_t)kNodes * L.width * 4);
       L.fires = c.take((size_t)kNodes * L.width * 4);
       if (d.flags & PW_FLAG_TRACE) L.stamps = c.take((size_t)kNodes * L.width * 8);
-      L.pipe_ctl = c.take(4096);
+      L.pipe_ctl = c.take(256);
+      L.rb_ctr = c.take(S * M * RB * 4);
+      L.item_ctr = c.take(S * M * 4);
+      L.order = c.take(S * M * RB * CT * 4);
       break;
     }
     default:

@@ -73,6 +73,48 @@ struct ChainArgs {
   Futures f;
 };
 
+// Arguments of the persistent pipeline kernel (pipeline.hip).
+struct PipeArgs {
+  const __bf16* x;        // [M][rows][d] microbatch inputs
+  __bf16* acts;           // [S][M][rows][d] stage outputs
+  const __bf16* w;        // [S][d][d], stored [in][out]
+  const uint32_t* order;  // [total_tiles] claim order, s | m << 8 | r << 16 | c << 24
+  uint32_t* ticket;       // claim counter (cumulative over calls)
+  uint32_t ticket_base;   // claims made by earlier calls
+  uint32_t* rb_ctr;       // [S][M][RB] column tiles finished per row block (cumulative)
+  uint32_t* item_ctr;     // [S][M] row blocks finished (cumulative)
+  uint32_t* done_ctr;     // tiles finished (cumulative)
+  uint32_t rb_target, item_target, done_target;
+  uint32_t S, M, rows, d, RB, CT, total_tiles;
+  uint32_t epoch;
+  Futures f;
+};
+
+// Arguments of the mixture-of-experts kernels (moe.hip).
+struct MoeArgs {
+  const __bf16* x;         // [tokens][d]
+  const __bf16* w_router;  // [d][E]
+  const __bf16* w1;        // [E][d][hidden]
+  const __bf16* w2;        // [E][hidden][d]
+  __bf16* xd;              // [2 tokens][d] dispatched rows (exchange output)
+  __bf16* h;               // [2 tokens][hidden] FFN hidden activations
+  __bf16* y;               // [2 tokens][d] expert outputs
+  __bf16* out;             // [tokens][d] combined output
+  float* logits;           // [tokens][E] or null
+  int32_t* experts;        // [tokens][2]
+  float* gates;            // [tokens][2]
+  int32_t* slot_of;        // [2 tokens] dispatched slot of tuple g
+  uint64_t tokens;
+  uint32_t d, hidden, E;
+  uint32_t max_row_blocks;  // upper bound of the expert row blocks (grid sizing)
+  const int64_t* seg;      // [E+1] expert segment offsets (from the exchange)
+  uint32_t* rb_start;      // [E+1] row-block prefix
+  uint32_t* b_done;        // [E] finished FFN2 tiles
+  uint32_t* ctl;           // [2] combine done counter
+  uint32_t epoch;
+  Futures f;
+};
+
 // Launchers (exchange.hip).
 hipError_t launch_hist(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s);
@@ -82,5 +124,10 @@ hipError_t launch_b(const ExchangeArgs& a, hipStream_t s);
 size_t scatter_lds_bytes(uint32_t N);
 // mode: 0 chained (one launch, all steps), 1 one node (OpByOp), 2 fused.
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);
+hipError_t launch_pipeline(const PipeArgs& a, hipStream_t s);
+hipError_t launch_router(const MoeArgs& a, hipStream_t s);
+hipError_t launch_moe_prefix(const MoeArgs& a, hipStream_t s);
+hipError_t launch_ffn(const MoeArgs& a, bool second, hipStream_t s);
+hipError_t launch_combine(const MoeArgs& a, hipStream_t s);
 
 }  // namespace pw

@@ -1,0 +1,264 @@
+// Mixture-of-experts step: router + top-2 gate (A), dispatch exchange, expert
+// FFN (B) gated on each expert's future, gated combine (Result).
+//
+// PATHWAYS page ("PATHWAYS: Asynchronous Distributed Dataflow for ML"),
+// section 6.3 "Data-dependent vectorized control flow": sub-examples are
+// routed by a learned function to the accelerators that hold different
+// weights (mixture of experts), which needs fine-grained data-dependent
+// exchanges; section 4.3: the exchange with progress tracking; section 4.5:
+// when a node's resource needs depend on its predecessor's output the runtime
+// schedules it after that output exists. Here the expert segment sizes are
+// data dependent, so the FFN launches read them on the device (a row-block
+// prefix computed after the exchange) instead of the host sizing them.
+//
+// Token t emits tuples 2t (top-1 expert) and 2t + 1 (top-2 expert); the
+// exchange (exchange.hip) moves token rows into expert segments and records
+// slot_of[g], the inverse of the permutation, which the combine reads.
+#include "device.h"
+#include "gemm.h"
+
+namespace pw {
+
+namespace {
+
+constexpr int kRouterTokens = 256;  // tokens per router workgroup (4 waves x 64)
+constexpr int kMaxExperts = 64;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// logits[t][e] = sum_k x[t][k] w[k][e] with bf16 products and fp32
+// accumulation (v_mfma_f32_32x32x16_bf16), then per token: the two largest
+// logits (ties to the lower expert id), gates = softmax over those two.
+// LDS holds W^T ([64][d], k contiguous, 16-byte chunks swizzled by row), then
+// is reused for the logits of the workgroup's tokens.
+__global__ __launch_bounds__(256, 1) void k_router(MoeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int d = (int)a.d, E = (int)a.E;
+  const int chunks = d / 8;  // 16-byte chunks per W^T row
+  // W [d][E] -> LDS W^T [64][d]; experts >= E are zero rows. Rows of W are
+  // read 8 experts (16 bytes) at a time and scattered into LDS as 2-byte stores.
+  for (int i = tid; i < kMaxExperts * chunks; i += 256) {  // zero the table
+    *reinterpret_cast<bf16x8*>(lds + (int64_t)i * 16) = bf16x8{};
+  }
+  __syncthreads();
+  const int groups = (E + 7) / 8;  // 8-expert groups per row of W
+  for (int i = tid; i < d * groups; i += 256) {
+    const int k = i / groups, e8 = (i - k * groups) * 8;
+    const __bf16* src = a.w_router + (int64_t)k * E + e8;
+    const int ch = k >> 3, kk = k & 7;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e8 + j;
+      if (e < E) {
+        __bf16* dst = reinterpret_cast<__bf16*>(lds + ((int64_t)e * chunks + (ch ^ (e & 7))) * 16) + kk;
+        *dst = src[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens + w * 64;  // this wave's 64 tokens
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  const int64_t r0 = min<int64_t>(t0 + (lane & 31), a.tokens - 1);
+  const int64_t r1 = min<int64_t>(t0 + 32 + (lane & 31), a.tokens - 1);
+  const __bf16* x0 = a.x + r0 * d;
+  const __bf16* x1 = a.x + r1 * d;
+  for (int k = 0; k < d; k += 16) {
+    const int ch = (k >> 3) + (lane >> 5);
+    const bf16x8 av0 = *reinterpret_cast<const bf16x8*>(x0 + ch * 8);
+    const bf16x8 av1 = *reinterpret_cast<const bf16x8*>(x1 + ch * 8);
+    bf16x8 bv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = j * 32 + (lane & 31);
+      bv[j] = *reinterpret_cast<const bf16x8*>(lds + ((int64_t)e * chunks + (ch ^ (e & 7))) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0, bv[j], acc[0][j], 0, 0, 0);
+      acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1, bv[j], acc[1][j], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with W^T: reuse LDS for logits
+  float* lg = reinterpret_cast<float*>(lds);  // [256 tokens][65] (padded row)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = w * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = j * 32 + (lane & 31);
+        lg[row * 65 + col] = acc[i][j][r];
+      }
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kRouterTokens + tid;
+  if (t < a.tokens) {
+    const float* row = lg + tid * 65;
+    int e0 = 0, e1 = -1;
+    float l0 = row[0], l1 = 0.f;
+    for (int e = 1; e < E; ++e) {
+      const float v = row[e];
+      if (v > l0) {  // strictly larger: ties keep the lower id
+        e1 = e0; l1 = l0;
+        e0 = e; l0 = v;
+      } else if (e1 < 0 || v > l1) {
+        e1 = e; l1 = v;
+      }
+    }
+    const float z = expf(l1 - l0);  // <= 1
+    const float g0 = 1.0f / (1.0f + z), g1 = z / (1.0f + z);
+    a.experts[t * 2] = e0;
+    a.experts[t * 2 + 1] = e1;
+    a.gates[t * 2] = g0;
+    a.gates[t * 2 + 1] = g1;
+    if (a.logits)
+      for (int e = 0; e < E; ++e) a.logits[t * E + e] = row[e];
+  }
+}
+
+// Row-block prefix of the expert segments (data-dependent sizes), and the
+// per-call reset of the FFN and combine counters. One workgroup.
+__global__ void k_moe_prefix(MoeArgs a) {
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (uint32_t e = 0; e < a.E; ++e) {
+      a.rb_start[e] = run;
+      const int64_t n = a.seg[e + 1] - a.seg[e];
+      run += (uint32_t)((n + mm::BM - 1) / mm::BM);
+      a.b_done[e] = 0;
+    }
+    a.rb_start[a.E] = run;
+    a.ctl[2] = 0;  // combine done counter
+  }
+}
+
+// Largest e with rb_start[e] <= v.
+__device__ __forceinline__ uint32_t expert_of(const uint32_t* rb_start, uint32_t E, uint32_t v) {
+  uint32_t lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    if (rb_start[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One 256 x 256 tile of an expert FFN GEMM: rows of expert e's segment.
+// kSecond: input H, weights W2 [E][hidden][d], output Y (no activation);
+// otherwise input dispatched rows, W1 [E][d][hidden], output H through GELU.
+template <bool kSecond>
+__global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  __shared__ uint32_t go;
+  const uint32_t CT = (kSecond ? a.d : a.hidden) / mm::BN;
+  const uint32_t rbg = blockIdx.x / CT, c = blockIdx.x - rbg * CT;
+  const uint32_t total_rb = a.rb_start[a.E];
+  if (rbg >= total_rb) return;  // grid is sized for the worst case
+  const uint32_t e = expert_of(a.rb_start, a.E, rbg);
+  const uint32_t rb = rbg - a.rb_start[e];
+  const int64_t seg0 = a.seg[e], n_e = a.seg[e + 1] - seg0;
+  const int64_t row0 = seg0 + (int64_t)rb * mm::BM;
+  const int rows = (int)min<int64_t>(mm::BM, n_e - (int64_t)rb * mm::BM);
+  if (threadIdx.x == 0) go = await(a.f, NODE_EXCH, e, a.epoch);  // the expert's input is complete
+  __syncthreads();
+  if (!go) return;
+  mm::Tile tile;
+  const uint32_t K = kSecond ? a.hidden : a.d, N = kSecond ? a.d : a.hidden;
+  const __bf16* in = kSecond ? a.h : a.xd;
+  tile.A = in + row0 * K;
+  tile.lda = K;
+  tile.rows = rows;
+  tile.B = (kSecond ? a.w2 : a.w1) + (int64_t)e * K * N + (int64_t)c * mm::BN;
+  tile.ldb = N;
+  tile.K = (int)K;
+  mm::f32x16 acc[4][4];
+  mm::tile_mma(tile, lds, acc);
+  __bf16* out = (kSecond ? a.y : a.h) + row0 * N + (int64_t)c * mm::BN;
+  mm::store_tile<!kSecond>(acc, out, N, rows);
+  if (kSecond) {  // B[e] completes with the last tile of its segment
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t tiles_e = (uint32_t)((n_e + mm::BM - 1) / mm::BM) * CT;
+      const uint32_t old = __hip_atomic_fetch_add(&a.b_done[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + 1 == tiles_e) fire(a.f, NODE_B, e, a.epoch, false);
+    }
+  }
+}
+
+// out[t] = bf16(g0 * Y[slot(2t)] + g1 * Y[slot(2t + 1)]), fp32 sum with the
+// top-1 term first; one wave per token, 16-byte chunks.
+__global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  bool ok = true;
+  if (t < a.tokens) {
+    const int e0 = a.experts[t * 2], e1 = a.experts[t * 2 + 1];
+    if (lane == 0) ok = await(a.f, NODE_B, e0, a.epoch) && await(a.f, NODE_B, e1, a.epoch);
+    ok = __shfl((int)ok, 0, 64) != 0;
+    if (ok) {
+      const float g0 = a.gates[t * 2], g1 = a.gates[t * 2 + 1];
+      const bf16x8* y0 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)a.slot_of[t * 2] * a.d);
+      const bf16x8* y1 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)a.slot_of[t * 2 + 1] * a.d);
+      bf16x8* o = reinterpret_cast<bf16x8*>(a.out + t * a.d);
+      for (uint32_t ch = lane; ch < a.d / 8; ch += 64) {
+        const bf16x8 u = y0[ch], v = y1[ch];
+        bf16x8 r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = (__bf16)fmaf(g1, (float)v[j], g0 * (float)u[j]);
+        o[ch] = r;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&a.ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == gridDim.x) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+  }
+}
+
+}  // namespace
+
+size_t router_lds_bytes(uint32_t d) { return (size_t)kMaxExperts * d * 2 > (size_t)kRouterTokens * 65 * 4 ? (size_t)kMaxExperts * d * 2 : (size_t)kRouterTokens * 65 * 4; }
+
+hipError_t launch_router(const MoeArgs& a, hipStream_t s) {
+  const size_t lds = router_lds_bytes(a.d);
+  hipError_t e = hipFuncSetAttribute((const void*)k_router, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const uint64_t blocks = (a.tokens + kRouterTokens - 1) / kRouterTokens;
+  hipLaunchKernelGGL(k_router, dim3((uint32_t)blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_prefix(const MoeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_moe_prefix, dim3(1), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn(const MoeArgs& a, bool second, hipStream_t s) {
+  const uint32_t CT = (second ? a.d : a.hidden) / mm::BN;
+  const uint64_t blocks = (uint64_t)a.max_row_blocks * CT;
+  if (second) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_ffn<true>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ffn<true>, dim3((uint32_t)blocks), dim3(mm::NT), mm::kLdsBytes, s, a);
+  } else {
+    hipError_t e = hipFuncSetAttribute((const void*)k_ffn<false>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ffn<false>, dim3((uint32_t)blocks), dim3(mm::NT), mm::kLdsBytes, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
+  const uint64_t blocks = (a.tokens + 3) / 4;
+  hipLaunchKernelGGL(k_combine, dim3((uint32_t)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pw

@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/pw.h"
+#include "pw.h"
 #include "internal.h"
 
 namespace pw {
@@ -24,8 +24,10 @@ struct Layout {
   size_t seg = 0;         // [N+1] i64 segment offsets
   size_t tile_base = 0;   // [N][num_tiles] u32
   size_t experts = 0, gates = 0, slot_of = 0, hidden_act = 0;  // MOE
+  size_t rb_start = 0, b_done = 0;                              // MOE
   size_t a_buf = 0;       // CHAIN: A's output buffer
-  size_t pipe_ctl = 0;    // PIPELINE: ticket counters
+  size_t pipe_ctl = 0;    // PIPELINE: [0] ticket, [1] done counter
+  size_t rb_ctr = 0, item_ctr = 0, order = 0;  // PIPELINE tables
   size_t total = 0;
   uint64_t G = 0;         // tuples per exchange
   uint32_t tile = 0, num_tiles = 0, width = 0;

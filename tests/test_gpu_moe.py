@@ -1,0 +1,164 @@
+"""GPU parity of the mixture-of-experts step (PATHWAYS page, section 6.3:
+data-dependent routing of sub-examples to experts; section 4.3: the
+exchange) against the CPU oracle, through the C ABI.
+
+Bars:
+  * router logits: |g - o| <= gamma_K (|x| . |W_r|) + 1e-30, gamma_K = K 2^-24
+    (fp32 summation of exact bf16 products in any order, K = d);
+  * routing, conditionally: the oracle's top-2, gates, exchange (counts,
+    offsets, source index) recomputed from the GPU's own fp32 logits must
+    match: experts and indices bit-exact, gates within 1e-6 relative, the
+    dispatched rows bit-exact copies of the token rows;
+  * expert outputs Y: within 1e-2 + 2e-2 |o| of the oracle's FFN on the same
+    rows, and within one bf16 ulp + the fp32 summation bounds of both GEMMs
+    (2^-7 |Y| + (2^-7 + gamma_H) (|H| . |W2|) + gamma_d 1.13 (|x| . |W1|) . |W2|);
+  * combine, conditionally on the GPU's Y and gates: one bf16 ulp of the
+    value + 2^-23 (|g0 y0| + |g1 y1|) (the fp32 product rounded before the
+    fused add; it matters when the two terms cancel);
+  * end to end from the tokens, on tokens the oracle routes the same way:
+    within 1e-2 + 2e-2 |o|. Tokens whose 2nd and 3rd logits nearly tie may
+    route differently; they are counted and must be near ties.
+"""
+import numpy as np
+import pytest
+import torch
+
+import pw_inputs
+from oracle import invariants as inv
+from oracle import moe as om
+from oracle import numerics as nm
+
+pytestmark = pytest.mark.gpu
+
+
+def run(pw, tokens, d, experts, hidden, shards, flags=0):
+    inp = pw_inputs.moe(tokens, d, experts, hidden)
+    wr, w1, w2 = inp.w_router.cuda(), inp.w1.cuda(), inp.w2.cuda()
+    m = pw.MoE(wr, w1, w2, tokens, num_src_shards=shards, flags=flags, want_counts=True)
+    f = m.step(inp.x.cuda())
+    pw.future_wait(f, 120_000_000_000)
+    return inp, m
+
+
+def check_logits(x, wr, lg_gpu, rows=None):
+    ref = om.router_logits(x, wr).astype(np.float64)
+    summ = np.abs(x.astype(np.float64)) @ np.abs(wr.astype(np.float64))
+    bound = x.shape[1] * 2.0 ** -24 * summ + 1e-30
+    err = np.abs(lg_gpu.astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+    return ref
+
+
+def check_expert_rows(xrows, w1e, w2e, y_gpu):
+    """Y rows of one expert against the oracle's FFN on the same input rows."""
+    ref = om.expert_ffn(xrows, w1e, w2e).astype(np.float64)
+    a1 = np.abs(xrows.astype(np.float64)) @ np.abs(w1e.astype(np.float64))
+    h = nm.to_bf16(nm.to_f32(nm.gelu(nm.to_f32(xrows.astype(np.float64) @ w1e.astype(np.float64))))).astype(np.float64)
+    w2a = np.abs(w2e.astype(np.float64))
+    K1, K2 = w1e.shape[0], w2e.shape[0]
+    bound = (2.0 ** -7 * np.maximum(np.abs(ref), np.abs(y_gpu)) + (2.0 ** -7 + K2 * 2.0 ** -24) * (np.abs(h) @ w2a)
+             + K1 * 2.0 ** -24 * 1.13 * (a1 @ w2a))
+    g = y_gpu.astype(np.float64)
+    assert np.all(np.abs(g - ref) <= 1e-2 + 2e-2 * np.abs(ref)), float(np.abs(g - ref).max())
+    assert np.all(np.abs(g - ref) <= bound), float((np.abs(g - ref) / (bound + 1e-30)).max())
+
+
+@pytest.mark.parametrize("tokens,d,experts,hidden,shards", [
+    (512, 256, 8, 512, 4), (300, 512, 64, 256, 3), (1000, 256, 2, 256, 8), (64, 256, 5, 768, 1)])
+def test_moe_small(gpu, tokens, d, experts, hidden, shards):
+    pw = gpu
+    print(f"moe T={tokens} d={d} E={experts} H={hidden} S={shards}", flush=True)
+    inp, m = run(pw, tokens, d, experts, hidden, shards, flags=pw.PW_FLAG_TRACE)
+    x = inp.x.float().numpy()
+    wr = inp.w_router.float().numpy()
+    w1 = inp.w1.float().numpy()
+    w2 = inp.w2.float().numpy()
+    lg = m.logits.cpu().numpy()
+    check_logits(x, wr, lg)
+    # routing recomputed by the oracle from the GPU's logits
+    cond = om.moe_step(x, wr, w1, w2, num_src=shards, logits=lg, with_ffn=False)
+    assert np.array_equal(m.experts.cpu().numpy(), cond.experts.astype(np.int32))
+    g = m.gates.cpu().numpy()
+    assert np.all(np.abs(g - cond.gates) <= 1e-6 * np.abs(cond.gates))
+    assert np.array_equal(m.offsets.cpu().numpy(), cond.offsets)
+    assert np.array_equal(m.counts.cpu().numpy(), cond.counts.astype(np.int32))
+    si = m.src_index.cpu().numpy()
+    assert np.array_equal(si, cond.src_index.astype(np.int32))
+    inv.check_exchange(cond.dest, experts, si, cond.offsets, cond.counts)
+    xd = m.xd.float().cpu().numpy()
+    assert np.array_equal(xd.view(np.uint32), x[si // 2].view(np.uint32))
+    # expert outputs, per expert segment
+    y = m.y.float().cpu().numpy()
+    offs = cond.offsets
+    for e in range(experts):
+        if offs[e + 1] > offs[e]:
+            check_expert_rows(xd[offs[e]:offs[e + 1]], w1[e], w2[e], y[offs[e]:offs[e + 1]])
+    # combine, conditionally on the GPU's Y and gates
+    pos = np.empty(2 * tokens, np.int64)
+    pos[si] = np.arange(2 * tokens)
+    y0, y1 = y[pos[0::2]].astype(np.float64), y[pos[1::2]].astype(np.float64)
+    comb = om.combine_rows(g, y[pos[0::2]], y[pos[1::2]]).astype(np.float64)
+    out = m.out.float().cpu().numpy().astype(np.float64)
+    terms = np.abs(g[:, :1] * y0) + np.abs(g[:, 1:] * y1)
+    assert np.all(np.abs(out - comb) <= 2.0 ** -7 * np.maximum(np.abs(comb), np.abs(out)) + 2.0 ** -23 * terms + 1e-30)
+    # end to end from the tokens
+    full = om.moe_step(x, wr, w1, w2, num_src=shards)
+    same = np.all(full.experts == cond.experts, axis=1)
+    o = full.out.astype(np.float64)
+    assert np.all(np.abs(out[same] - o[same]) <= 1e-2 + 2e-2 * np.abs(o[same]))
+    if not same.all():
+        srt = np.sort(full.logits.astype(np.float64), axis=1)[:, ::-1]
+        gaps = np.minimum(srt[:, 0] - srt[:, 1], srt[:, 1] - srt[:, 2])
+        assert np.all(gaps[~same] < 1e-4), gaps[~same]
+    # futures: every expert's exchange and FFN fired once, Result once
+    ep, fi, st = m.plan.read_futures(trace=True)
+    assert np.all(fi[pw.PW_NODE_EXCHANGE, :experts] == 1) and np.all(fi[pw.PW_NODE_B, :experts] == 1)
+    assert fi[pw.PW_NODE_RESULT, 0] == 1
+    assert np.all(st[pw.PW_NODE_EXCHANGE, :experts] <= st[pw.PW_NODE_B, :experts])
+    assert np.all(st[pw.PW_NODE_B, :experts] <= st[pw.PW_NODE_RESULT, 0])
+
+
+def test_moe_full_size_sampled(gpu):
+    """131072 tokens x 1024, 64 experts, FFN 1024 -> 4096 -> 1024: routing and
+    the exchange in full (conditionally on the GPU's logits), logits, expert
+    outputs and combined outputs on sampled tokens."""
+    pw = gpu
+    tokens, d, experts, hidden = 131072, 1024, 64, 4096
+    inp, m = run(pw, tokens, d, experts, hidden, 64)
+    print("full-size moe: step done", flush=True)
+    lg = m.logits.cpu().numpy()
+    x_t = inp.x
+    rng = np.random.default_rng(9)
+    sample = np.sort(rng.choice(tokens, size=48, replace=False))
+    xs = x_t[torch.from_numpy(sample)].float().numpy()
+    wr = inp.w_router.float().numpy()
+    check_logits(xs, wr, lg[sample])
+    experts_c, gates_c, dest_c, counts_c, offsets_c, si_c = om.route(lg, experts, 64)
+    assert np.array_equal(m.experts.cpu().numpy(), experts_c.astype(np.int32))
+    g = m.gates.cpu().numpy()
+    assert np.all(np.abs(g - gates_c) <= 1e-6 * np.abs(gates_c))
+    assert np.array_equal(m.offsets.cpu().numpy(), offsets_c)
+    assert np.array_equal(m.counts.cpu().numpy(), counts_c.astype(np.int32))
+    si = m.src_index.cpu().numpy()
+    assert np.array_equal(si, si_c.astype(np.int32))
+    print("full-size moe: routing and exchange exact", flush=True)
+    # expert outputs and combine for the sampled tokens (both slots)
+    w1 = inp.w1
+    w2 = inp.w2
+    pos = np.empty(2 * tokens, np.int64)
+    pos[si] = np.arange(2 * tokens)
+    y_rows = m.y[torch.from_numpy(np.concatenate([pos[2 * sample], pos[2 * sample + 1]])).cuda()].float().cpu().numpy()
+    for i, t in enumerate(sample):
+        for j in range(2):
+            e = int(experts_c[t, j])
+            check_expert_rows(xs[i:i + 1], w1[e].float().numpy(), w2[e].float().numpy(), y_rows[j * len(sample) + i:j * len(sample) + i + 1])
+    out = m.out[torch.from_numpy(sample).cuda()].float().cpu().numpy().astype(np.float64)
+    ref = []
+    for i, t in enumerate(sample):
+        ys = []
+        for j in range(2):
+            e = int(experts_c[t, j])
+            ys.append(om.expert_ffn(xs[i:i + 1], w1[e].float().numpy(), w2[e].float().numpy())[0])
+        ref.append(om.combine_rows(gates_c[t:t + 1], ys[0][None], ys[1][None])[0])
+    ref = np.array(ref, dtype=np.float64)
+    assert np.all(np.abs(out - ref) <= 1e-2 + 2e-2 * np.abs(ref)), float(np.abs(out - ref).max())

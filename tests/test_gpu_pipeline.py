@@ -1,0 +1,114 @@
+"""GPU parity of the GPipe pipeline (PATHWAYS page, section 5.3 and Table 2;
+NEST page, Algorithm 1) against the CPU oracle.
+
+Each stage is bf16(GELU(h . W_s)) with fp32 accumulation on MFMA.
+
+End to end (oracle run from the inputs through every stage), per stage:
+  |g - o| <= 1e-2 + 2e-2 |o| elementwise and ||g - o||_2 <= 2e-2 ||o||_2.
+Activations shrink about 3x per stage, so the absolute term says little
+after a few stages; the arithmetic of every stage is therefore also checked
+on its own, conditionally: the oracle's stage s applied to the GPU's own
+stage s-1 output must match the GPU's stage s output within
+  one bf16 ulp of the value (2^-7 |v|: the two roundings may straddle a
+  rounding boundary) + 1e-4 (|h| . |W|)
+where the second term bounds fp32 summation over K = d <= 1024 terms in any
+order (gamma_K = K 2^-24 < 6.2e-5, times GELU's slope <= 1.13).
+"""
+import numpy as np
+import pytest
+import torch
+
+import pw_inputs
+from oracle import pipeline as op
+
+pytestmark = pytest.mark.gpu
+
+
+def check_stage(g, o, where):
+    """End-to-end bound for one stage output."""
+    g = g.astype(np.float64)
+    o = o.astype(np.float64)
+    err = np.abs(g - o)
+    assert np.all(err <= 1e-2 + 2e-2 * np.abs(o)), (where, float(err.max()))
+    assert np.linalg.norm(g - o) <= 2e-2 * np.linalg.norm(o), (where, np.linalg.norm(g - o) / np.linalg.norm(o))
+
+
+def check_conditional(h_prev, w, g, where):
+    """The oracle's stage on the GPU's own input, against the GPU's output."""
+    ref = op.stage(h_prev, w).astype(np.float64)
+    g = g.astype(np.float64)
+    summ = np.abs(h_prev.astype(np.float64)) @ np.abs(w.astype(np.float64))
+    bound = 2.0 ** -7 * np.maximum(np.abs(g), np.abs(ref)) + 1e-4 * summ
+    err = np.abs(g - ref)
+    assert np.all(err <= bound), (where, float((err / (bound + 1e-30)).max()))
+    return int((err > 0).sum())
+
+
+def run(pw, s, m, rows, d, flags=0):
+    inp = pw_inputs.pipeline(s, m, rows, d)
+    w = inp.w.cuda()
+    pipe = pw.Pipeline(w, m, rows, flags=flags)
+    x = inp.x.cuda()
+    acts = torch.empty((s, m, rows, d), dtype=torch.bfloat16, device="cuda")
+    f = pipe.run(x, acts)
+    pw.future_wait(f, 120_000_000_000)
+    return inp, pipe, acts, f
+
+
+@pytest.mark.parametrize("s,m,rows,d", [(1, 1, 256, 256), (3, 4, 300, 256), (2, 3, 512, 512), (4, 2, 100, 768)])
+def test_pipeline_small_all_outputs(gpu, s, m, rows, d):
+    pw = gpu
+    print(f"pipeline S={s} M={m} rows={rows} d={d}", flush=True)
+    inp, pipe, acts, f = run(pw, s, m, rows, d, flags=pw.PW_FLAG_TRACE)
+    x = inp.x.float().numpy()
+    w = inp.w.float().numpy()
+    got = acts.float().cpu().numpy()
+    for mb in range(m):
+        ref = op.forward(x[mb], w, keep_all=True)
+        for st in range(s):
+            check_stage(got[st, mb], ref[st], (st, mb))
+            check_conditional(x[mb] if st == 0 else got[st - 1, mb], w[st], got[st, mb], (st, mb))
+    ep, fi, stamps = pipe.plan.read_futures(trace=True)
+    n = s * m
+    assert np.all(ep[pw.PW_NODE_STAGE, :n] == 1) and np.all(fi[pw.PW_NODE_STAGE, :n] == 1)
+    assert fi[pw.PW_NODE_RESULT, 0] == 1
+    st = stamps[pw.PW_NODE_STAGE, :n].reshape(s, m)
+    assert np.all(st[1:] > st[:-1])            # stage s of microbatch m completes after stage s-1
+
+
+def test_pipeline_repeat_is_deterministic(gpu):
+    pw = gpu
+    inp, pipe, acts, f = run(pw, 2, 3, 300, 256)
+    first = acts.clone()
+    acts.fill_(0)
+    f2 = pipe.run(inp.x.cuda(), acts)
+    pw.future_wait(f2, 60_000_000_000)
+    assert f2.epoch == 2
+    assert torch.equal(first, acts)
+    ep, fi, _ = pipe.plan.read_futures()
+    assert np.all(fi[pw.PW_NODE_STAGE, :6] == 2) and fi[pw.PW_NODE_RESULT, 0] == 2
+
+
+def test_pipeline_full_size_sampled(gpu):
+    """16 stages x 64 microbatches x 2048 x 1024: every stage output of sampled
+    rows of sampled microbatches against the oracle; GPipe dependency order."""
+    pw = gpu
+    s, m, rows, d = 16, 64, 2048, 1024
+    inp, pipe, acts, f = run(pw, s, m, rows, d, flags=pw.PW_FLAG_TRACE)
+    x = inp.x
+    w = inp.w.float().numpy()
+    rng = np.random.default_rng(5)
+    for mb in (0, 17, 63):
+        rws = np.sort(rng.choice(rows, size=12, replace=False))
+        ref = op.forward(x[mb, rws].float().numpy(), w, keep_all=True)
+        got = acts[:, mb, torch.from_numpy(rws).cuda()].float().cpu().numpy()
+        xin = x[mb, rws].float().numpy()
+        flips = 0
+        for st in range(s):
+            check_stage(got[st], ref[st], (st, mb))
+            flips += check_conditional(xin if st == 0 else got[st - 1], w[st], got[st], (st, mb))
+        print(f"microbatch {mb}: {flips} of {s * len(rws) * d} stage outputs differ by one bf16 rounding", flush=True)
+    ep, fi, stamps = pipe.plan.read_futures(trace=True)
+    st = stamps[pw.PW_NODE_STAGE, : s * m].reshape(s, m)
+    assert np.all(fi[pw.PW_NODE_STAGE, : s * m] == 1)
+    assert np.all(st[1:] > st[:-1])
