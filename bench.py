@@ -132,6 +132,35 @@ def pipeline_bench(pw, torch, pw_inputs, passes=3):
             "flop_per_pass": flops, "gpipe_bubble_lockstep": (s - 1) / (m + s - 1)}
 
 
+def moe_bench(pw, torch, pw_inputs, steps=3):
+    """MoE step: 131072 tokens x 1024 bf16, router 1024 x 64 + top-2, dispatch
+    exchange to 64 experts, FFN 1024 -> 4096 -> 1024 GELU, gated combine."""
+    tokens, d, experts, hidden = 131072, 1024, 64, 4096
+    inp = pw_inputs.moe(tokens, d, experts, hidden)
+    wr, w1, w2 = inp.w_router.cuda(), inp.w1.cuda(), inp.w2.cuda()
+    x = inp.x.cuda()
+    m = pw.MoE(wr, w1, w2, tokens, num_src_shards=64, flags=pw.PW_FLAG_TIMING, want_logits=False)
+    pw.future_wait(m.step(x), 60_000_000_000)
+    m.plan.reset_times()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        f = m.step(x)
+    e1.record(st)
+    torch.cuda.synchronize()
+    pw.future_wait(f, 60_000_000_000)
+    ms = e0.elapsed_time(e1) / steps
+    kt = {k: v[1] / v[0] for k, v in m.plan.kernel_times().items()}
+    ffn_ms = kt["ffn1"] + kt["ffn2"]
+    flops = 2.0 * 2 * tokens * (d * hidden + hidden * d)
+    tf = flops / (ffn_ms * 1e-3) / 1e12
+    return {"workload": "MoE: 131072 tokens x 1024 bf16, 64 experts, top-2, FFN 1024->4096->1024 GELU",
+            "ms_per_step": ms, "kernel_ms": kt, "expert_tflops": tf, "expert_frac_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+            "expert_flop": flops}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +169,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chain", action="store_true", help="skip the chained-steps sweep")
     ap.add_argument("--no-pipeline", action="store_true", help="skip the pipeline measurement")
+    ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts measurement")
     ap.add_argument("--chain-steps", type=int, default=10000)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 plain elementwise copies of 1 GiB (torch.neg) to scale HBM counters")
@@ -231,6 +261,10 @@ def main():
     if not args.no_pipeline:
         log("pipeline")
         result["pipeline"] = pipeline_bench(pw, torch, pw_inputs)
+
+    if not args.no_moe:
+        log("moe")
+        result["moe"] = moe_bench(pw, torch, pw_inputs)
 
     if not args.no_chain:
         log("chain sweep")
