@@ -115,7 +115,10 @@ typedef struct {
   uint32_t reserved0;
   uint64_t spin_limit_ns;    /* bound of every device-side wait (0 = 2 s); an expired wait
                                 latches PW_ERR_TIMEOUT and the waiting work is skipped        */
-  const void* w_router;      /* MOE: device bf16 [d][E] (borrowed)                             */
+  /* Weights are stored [in][out], row-major. They are read once, when the plan is built
+     (pw_plan with ws != NULL packs them K-contiguous into the workspace); later changes
+     to these buffers are not seen by the plan. */
+  const void* w_router;      /* MOE: device bf16 [d][E]                                        */
   const void* w1;            /* MOE: device bf16 [E][d][hidden]; PIPELINE: bf16 [S][d][d]      */
   const void* w2;            /* MOE: device bf16 [E][hidden][d]                                */
 } pw_plan_desc;
@@ -199,7 +202,8 @@ const char* pw_last_error(void);
  * memory of ws_bytes >= *ws_required, 256-byte aligned, caller-owned, kept
  * alive until pw_plan_destroy) it lays out the tables in ws, clears them,
  * and returns an opaque handle in *out. ws_bytes too small -> PW_ERR_NOMEM.
- * The plan holds host metadata only; weights in `d` are borrowed pointers.
+ * The plan holds host metadata only; weights in `d` are packed into the
+ * workspace during this second call (device work, synchronised before return).
  */
 int pw_plan(const pw_plan_desc* d, void* ws, size_t ws_bytes, size_t* ws_required, pw_plan_t* out);
 

@@ -70,4 +70,22 @@ __device__ __forceinline__ bool await(const Futures& f, uint32_t node, uint32_t 
   }
 }
 
+// Wait on a future fired by an EARLIER launch on the same stream: the kernel
+// boundary already orders the producer's writes before this launch, so the
+// check is a relaxed read (an agent-scope acquire would invalidate the L2 of
+// this XCD on every call). Same bound and latch as await().
+__device__ __forceinline__ bool await_prior(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
+  const uint32_t* p = &f.epoch[node * f.width + shard];
+  if (epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    if (epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
+    if (wall_clock64() - t0 > f.spin_ticks) {
+      latch(f.status, ST_TIMEOUT);
+      return false;
+    }
+  }
+}
+
 }  // namespace pw

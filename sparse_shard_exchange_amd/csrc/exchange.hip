@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
   if (threadIdx.x == 0) {
     const uint32_t d0 = segment_of(a.seg, a.N, s0), d1 = segment_of(a.seg, a.N, s1 - 1);
     bool ok = true;
-    for (uint32_t d = d0; d <= d1 && ok; ++d) ok = await(a.f, NODE_EXCH, d, a.epoch);
+    for (uint32_t d = d0; d <= d1 && ok; ++d) ok = await_prior(a.f, NODE_EXCH, d, a.epoch);
     range[0] = d0;
     range[1] = d1;
     go = ok;

@@ -1,17 +1,25 @@
 // bf16 MFMA GEMM tile core for gfx950: C[256 x 256] (fp32) = A[256 x K] . B[K x 256].
 //
-// A is row-major [rows][K] (activations, K contiguous); B is row-major [K][N]
-// (weights stored [in][out], N contiguous). One workgroup of 4 waves owns a
-// 256 x 256 output tile; wave w computes the 128 x 128 quadrant
-// (w >> 1, w & 1) as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16.
+// Operands are both K-contiguous: A is row-major [rows][K] (activations) and
+// the weights come pre-packed as B^T [N][K] (pack.hip turns the stored
+// [in][out] weights around once, when the plan is built). One workgroup of 4
+// waves owns a 256 x 256 output tile; wave w computes the 128 x 128 quadrant
+// (w >> 1, w & 1) as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, accumulators
+// in AGPRs. The MFMA is fed B^T as its first operand and A as its second, so
+// each block accumulates C^T: a lane then holds 4 consecutive output columns
+// of one row per register quad, and the epilogue writes 8 bytes at a time.
 //
-// K advances 64 at a time through double-buffered LDS (2 x 64 KiB). A goes
-// to LDS as [row][k]; B is transposed on the way in (each thread turns an
-// 8 x 8 block of bf16 around in registers) to [n][k], so both MFMA operands
-// are single 16-byte LDS reads: lane l reads row (l % 32) at k-chunk l / 32.
-// The 16-byte chunks of every 128-byte LDS row are XOR-swizzled with
-// (row ^ row >> 3) & 7, which keeps the row-wise reads of the MFMA operands
-// and the transposed writes of B free of bank conflicts.
+// K streams through a ring of 4 LDS stages of 32 columns (A 256 x 32 and
+// B^T 256 x 32 bf16 = 32 KiB per stage, 128 KiB in all) filled by direct
+// global-to-LDS loads (global_load_lds_dwordx4: no staging registers), three
+// stages ahead of the one being multiplied. Each wave-wide load writes 1 KiB
+// of LDS contiguously (16 bytes per lane), so the 16-byte chunks of each
+// 64-byte LDS row are permuted by picking which global chunk each lane
+// fetches: chunk c of row r sits at slot c ^ ((r >> 2) & 3), which makes the
+// MFMA operand reads (lane l reads row l % 32, chunk l / 32 of the k-step)
+// free of LDS bank conflicts. Ring slots are recycled behind raw workgroup
+// barriers with explicit vector-memory counter waits, so three stages stay in
+// flight across the barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,78 +30,84 @@ namespace mm {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
-constexpr int kTileBytes = BM * BK * 2;            // one operand tile, 32 KiB
-constexpr int kLdsBytes = 2 * 2 * kTileBytes;      // A and B, double buffered: 128 KiB
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256, kStages = 4;
+constexpr int kHalf = BM * BK * 2;              // one operand block of a stage: 16 KiB
+constexpr int kStageBytes = 2 * kHalf;          // 32 KiB
+constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
 
+// Byte offsets inside a tile (rows x K of A, 256 x K of B^T, the output tile)
+// must stay below 4 GiB: they are 32-bit.
 struct Tile {
-  const __bf16* A;  // first row of the tile, column 0
-  int64_t lda;
-  int rows;         // valid rows (<= BM); the rest read as zero and are not stored
-  const __bf16* B;  // row 0, first column of the tile
-  int64_t ldb;
-  int K;            // multiple of BK
+  const __bf16* A;   // first row of the tile; rows are K-contiguous
+  int64_t lda;       // elements between rows of A
+  int rows;          // valid rows (1..BM); the rest are read from row rows-1 and never stored
+  const __bf16* Bt;  // first row (output column) of the tile in B^T; K-contiguous
+  int64_t ldb;       // elements between rows of B^T
+  int K;             // multiple of BK
 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) { return (row * 8 + (chunk ^ swz(row))) * 16; }
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-struct Stage {
-  u32x4 a[8];
-  u32x4 b[8];
-};
+// Chunk permutation of 64-byte LDS rows. gfx950 serves a 16-byte-per-lane
+// LDS read 16 lanes (256 bytes) at a time; lanes reading 16 consecutive rows
+// at one logical chunk land in 16 distinct 16-byte bank groups with this
+// permutation (measured: as fast as contiguous reads; (row >> 1) & 3 is ~20%
+// slower, no permutation ~2.3x slower).
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-// Global -> registers for k columns [k0, k0 + 64). Addresses are 32-bit byte
-// offsets from the tile's (wave-uniform) base pointers.
-__device__ __forceinline__ void load_stage(const Tile& t, int k0, Stage& s) {
-  const int tid = threadIdx.x;
-  const unsigned char* A = reinterpret_cast<const unsigned char*>(t.A);
-  const unsigned char* B = reinterpret_cast<const unsigned char*>(t.B);
-  const uint32_t lda2 = (uint32_t)t.lda * 2u, ldb2 = (uint32_t)t.ldb * 2u;
-  const uint32_t ch = tid & 7, row0 = tid >> 3;
-  const uint32_t a_off = row0 * lda2 + (uint32_t)(k0 + ch * 8) * 2u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t row = row0 + i * (NT / 8);
-    if ((int)row < t.rows)
-      s.a[i] = *reinterpret_cast<const u32x4*>(A + a_off + (uint32_t)i * (NT / 8) * lda2);
-    else
-      s.a[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  const uint32_t nb = tid & 31, kg = tid >> 5;
-  const uint32_t b_off = (uint32_t)(k0 + kg * 8) * ldb2 + nb * 16u;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) s.b[r] = *reinterpret_cast<const u32x4*>(B + b_off + (uint32_t)r * ldb2);
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (n in {0, 8, 16}); encodes vmcnt with expcnt and lgkmcnt left at their maxima.
+template <int n>
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Registers -> LDS; B's 8 x 8 block (rows k, columns n) is written as 8 rows n.
-__device__ __forceinline__ void store_stage(unsigned char* As, unsigned char* Bs, const Stage& s) {
-  const int tid = threadIdx.x;
-  const int ch = tid & 7, row0 = tid >> 3;
+// Per-lane byte offsets (32-bit, from the tile's wave-uniform base pointers)
+// of the global chunks this lane moves into LDS, for k0 = 0.
+struct Lanes {
+  uint32_t a[4], b[4];
+};
+
+__device__ __forceinline__ Lanes lane_offsets(const Tile& t) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  Lanes o;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = row0 + i * (NT / 8);
-    *reinterpret_cast<u32x4*>(As + lds_off(row, ch)) = s.a[i];
+  for (int i = 0; i < 4; ++i) {
+    const int row = (w * 4 + i) * 16 + (lane >> 2);  // 16 rows per wave-wide load
+    const int c = (lane & 3) ^ swz(row);             // the chunk this lane's slot holds
+    const int ra = row < t.rows ? row : t.rows - 1;
+    o.a[i] = (uint32_t)ra * (uint32_t)t.lda * 2u + (uint32_t)c * 16u;
+    o.b[i] = (uint32_t)row * (uint32_t)t.ldb * 2u + (uint32_t)c * 16u;
   }
-  const int nb = tid & 31, kg = tid >> 5;
+  return o;
+}
+
+// Issue the direct-to-LDS loads of K columns [k0, k0 + 32) into one stage:
+// 4 loads of A and 4 of B^T per lane (8 vector-memory operations).
+__device__ __forceinline__ void issue_stage(const Tile& t, const Lanes& o, int k0, unsigned char* stage) {
+  const int w = threadIdx.x >> 6;
+  const unsigned char* A = reinterpret_cast<const unsigned char*>(t.A) + (uint32_t)k0 * 2u;
+  const unsigned char* B = reinterpret_cast<const unsigned char*>(t.Bt) + (uint32_t)k0 * 2u;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u32x4 w;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = s.b[2 * p][j >> 1], hi = s.b[2 * p + 1][j >> 1];
-      w[p] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-    *reinterpret_cast<u32x4*>(Bs + lds_off(nb * 8 + j, kg)) = w;
+  for (int i = 0; i < 4; ++i) {
+    const int group = w * 4 + i;
+    __builtin_amdgcn_global_load_lds(A + o.a[i], (lds_ptr)(stage + group * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(B + o.b[i], (lds_ptr)(stage + kHalf + group * 1024), 16, 0, 0);
   }
 }
 
-// Byte offsets (chunk 0 and the row's swizzle) of this lane's 4 A and 4 B
-// fragment rows; chunk c of row k is at base + ((c ^ sw) << 4).
+// A workgroup barrier that the compiler may not move memory accesses across
+// and that adds no wait of its own (the vector-memory waits are explicit).
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Byte offsets of this lane's fragment rows inside an operand block.
 struct Frag {
-  uint32_t a_base[4], a_sw[4], b_base[4], b_sw[4];
+  int a_row[4], a_sw[4], b_row[4], b_sw[4];
 };
 
 __device__ __forceinline__ Frag frag_offsets() {
@@ -103,90 +117,180 @@ __device__ __forceinline__ Frag frag_offsets() {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra = wm + i * 32 + (lane & 31), rb = wn + i * 32 + (lane & 31);
-    f.a_base[i] = ra * 128;
+    f.a_row[i] = ra * 64;
     f.a_sw[i] = swz(ra);
-    f.b_base[i] = rb * 128;
+    f.b_row[i] = rb * 64;
     f.b_sw[i] = swz(rb);
   }
   return f;
 }
 
-__device__ __forceinline__ void compute_stage(const unsigned char* As, const unsigned char* Bs, const Frag& f,
-                                              f32x16 (&acc)[4][4]) {
-  const int lane = threadIdx.x & 63;
+// Read the 8 fragments (4 of A, 4 of B^T) of k-step kk of a stage.
+__device__ __forceinline__ void read_frags(const unsigned char* stage, const Frag& f, int kk, bf16x8 (&a)[4],
+                                           bf16x8 (&b)[4]) {
+  const int c = 2 * kk + ((threadIdx.x & 63) >> 5);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const uint32_t ch = 2 * kk + (lane >> 5);
-    bf16x8 a[4], b[4];
+  for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(stage + f.a_row[i] + ((c ^ f.a_sw[i]) << 4));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(As + f.a_base[i] + ((ch ^ f.a_sw[i]) << 4));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Bs + f.b_base[j] + ((ch ^ f.b_sw[j]) << 4));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+  for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(stage + kHalf + f.b_row[j] + ((c ^ f.b_sw[j]) << 4));
 }
 
-// The whole K loop of one tile. `lds` holds kLdsBytes.
+// 16 MFMAs of one k-step; the 8 fragment reads issued just before are spread
+// between the first 8 of them, so their latency hides under the matrix core.
+__device__ __forceinline__ void mfma_step(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+}
+
+// The whole K loop of one tile. `lds` holds kLdsBytes. Stage ks is consumed
+// in two halves: the MFMAs of its first k-step run while its second k-step's
+// fragments are read; then (while those MFMAs drain) the next stage is
+// awaited, the barrier is passed and the ring slot freed by the previous
+// stage is refilled; then the second k-step's MFMAs run while the next
+// stage's first fragments are read. On return every wave has finished reading
+// LDS and every load has landed.
 __device__ __forceinline__ void tile_mma(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  unsigned char* As[2] = {lds, lds + 2 * kTileBytes};
-  unsigned char* Bs[2] = {lds + kTileBytes, lds + 3 * kTileBytes};
-  Stage st;
   const Frag f = frag_offsets();
+  const Lanes o = lane_offsets(t);
   const int nk = t.K / BK;
-  load_stage(t, 0, st);
-  store_stage(As[0], Bs[0], st);
-  __syncthreads();
+  for (int s = 0; s < kStages - 1 && s < nk; ++s) issue_stage(t, o, s * BK, lds + s * kStageBytes);
+  // stage 0 landed: at most stages 1 and 2 (16 operations) still in flight
+  if (nk >= 3)
+    wait_vmem<16>();
+  else if (nk == 2)
+    wait_vmem<8>();
+  else
+    wait_vmem<0>();
+  ring_barrier();
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  read_frags(lds, f, 0, a0, b0);
   for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < nk) load_stage(t, (ks + 1) * BK, st);
-    compute_stage(As[cur], Bs[cur], f, acc);
-    if (ks + 1 < nk) store_stage(As[cur ^ 1], Bs[cur ^ 1], st);
-    __syncthreads();
+    const unsigned char* stage = lds + (ks & (kStages - 1)) * kStageBytes;
+    read_frags(stage, f, 1, a1, b1);
+    mfma_step(a0, b0, acc);
+    interleave_reads_with_mfma();
+    // stage ks+1 landed: stage ks+2 (issued last iteration) may remain in flight
+    if (ks + 2 < nk)
+      wait_vmem<8>();
+    else
+      wait_vmem<0>();
+    ring_barrier();  // every wave: stage ks+1 visible, done reading stage ks-1
+    if (ks + kStages - 1 < nk)
+      issue_stage(t, o, (ks + kStages - 1) * BK, lds + ((ks + kStages - 1) & (kStages - 1)) * kStageBytes);
+    // first fragments of the next stage (on the last stage, harmlessly this
+    // one again: the reads stay unconditional so their wait is exact)
+    const int nxt = ks + 1 < nk ? ks + 1 : ks;
+    read_frags(lds + (nxt & (kStages - 1)) * kStageBytes, f, 0, a0, b0);
+    mfma_step(a1, b1, acc);
+    interleave_reads_with_mfma();
   }
+  ring_barrier();
 }
 
-// Row / column (inside the tile) of accumulator register r of block (i, j).
-__device__ __forceinline__ int acc_row(int i, int r) {
+// Block (i, j) holds C^T: register r of a lane is output row
+// acc_row(i) = wm + 32 i + lane % 32 and column acc_col(j, r) =
+// wn + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4.
+__device__ __forceinline__ int acc_row(int i) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  return (w >> 1) * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+  return (w >> 1) * 128 + i * 32 + (lane & 31);
 }
-__device__ __forceinline__ int acc_col(int j) {
+__device__ __forceinline__ int acc_col(int j, int q) {  // first of the 4 columns of quad q
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  return (w & 1) * 128 + j * 32 + (lane & 31);
+  return (w & 1) * 128 + j * 32 + q * 8 + (lane >> 5) * 4;
 }
 
-// Exact GELU in fp32 with the device erff: z * Phi(z).
-__device__ __forceinline__ float gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// GELU(z) = z Phi(z) with Phi from erfc by Abramowitz & Stegun formula
+// 7.1.26 (erfc(x) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+// t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7): Phi(z) = erfc(|z| / sqrt 2) / 2
+// for z < 0 and 1 - erfc(z / sqrt 2) / 2 otherwise, so negative inputs keep
+// their relative accuracy.
+__device__ __forceinline__ float gelu(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  const float half_erfc = 0.5f * poly * t * __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);
+  const float phi = z < 0.0f ? half_erfc : 1.0f - half_erfc;
+  return z * phi;
+}
+
+// Epilogue staging: 128 rows of fp32 at a time, rows padded by 16 bytes so
+// that the 32 lanes writing one column quad of 32 different rows hit
+// different LDS banks.
+constexpr int kEpiStride = BN + 4;                  // floats per staged row
+constexpr int kEpiBytes = 128 * kEpiStride * 4;     // 133,120 bytes
+constexpr int kLdsTotal = kEpiBytes > kLdsBytes ? kEpiBytes : kLdsBytes;
 
 // Store the tile as bf16 (round to nearest even), optionally through GELU.
+// The accumulators go to LDS straight from AGPRs (4 consecutive columns of a
+// row per register quad), in two halves of 128 rows; then every thread reads
+// 4 consecutive values of a row, applies the epilogue and writes 8 bytes, so
+// each wave stores one whole 512-byte row per instruction. `lds` holds kLdsTotal bytes and is
+// free (tile_mma ends with a barrier).
 template <bool kGelu>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], __bf16* out, int64_t ldo, int rows) {
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], unsigned char* lds, __bf16* out, int64_t ldo,
+                                           int rows) {
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  float* L = reinterpret_cast<float*>(lds);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  unsigned char* base = reinterpret_cast<unsigned char*>(out);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int h = 0; h < 2; ++h) {
+    // wave rows wm + 64 h + [0, 64) -> staged rows (w >> 1) * 64 + [0, 64)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * h + ii;
+      const int lrow = (w >> 1) * 64 + 32 * ii + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = acc_row(i, r);
-        if (m < rows) {
-          float v = acc[i][j][r];
-          if (kGelu) v = gelu(v);
-          out[(int64_t)m * ldo + acc_col(j)] = (__bf16)v;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(L + lrow * kEpiStride + acc_col(j, q)) = v;
         }
+    }
+    __syncthreads();
+    // consecutive lanes read consecutive 16-byte chunks of a staged row
+    for (int k = threadIdx.x; k < 128 * (BN / 4); k += NT) {
+      const int lrow = k >> 6, ch = k & 63;
+      const int orow = (lrow >> 6) * 128 + 64 * h + (lrow & 63);
+      if (orow < rows) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(L + lrow * kEpiStride + ch * 4);
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(kGelu ? gelu(a[e]) : a[e]);
+        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+        // streaming store: the output is not re-read by this workgroup
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, o),
+                                    reinterpret_cast<u32x2*>(base + (uint32_t)orow * (uint32_t)ldo * 2u + (uint32_t)ch * 8u));
       }
+    }
+    __syncthreads();
+  }
 }
 
 // Every wave's global stores have completed (vmcnt = 0) before the caller's
 // barrier, so one thread's agent-scope release afterwards covers the
 // workgroup's output.
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_stores() { wait_vmem<0>(); }
 
 }  // namespace mm
 }  // namespace pw

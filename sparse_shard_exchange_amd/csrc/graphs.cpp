@@ -10,6 +10,8 @@ namespace pw {
 
 namespace {
 
+constexpr uint32_t kQueues = 8;  // one claim queue per XCD
+
 struct KindState {
   uint64_t calls = 0;  // calls launched so far (targets of the cumulative device counters)
   uint32_t grid = 0;   // PIPELINE: persistent workgroups (one per CU)
@@ -70,26 +72,62 @@ int plan_init_kind(Plan* p) {
   auto* ks = new KindState();
   p->kind_state = ks;
   if (p->desc.kind == PW_GRAPH_PIPELINE) {
-    // GPipe lock-step claim order: tick t = s + m ascending, then stage,
-    // row block, column block. Uploaded once with the plan.
+    // Items in GPipe lock-step order (tick t = s + m ascending, then stage)
+    // are dealt round-robin to one queue per XCD; an item's tiles (row block,
+    // then column block) stay together in its queue. Uploaded once.
     const pw_plan_desc& d = p->desc;
     const uint32_t S = d.num_shards, M = d.microbatches;
     const uint32_t RB = (uint32_t)((d.tuples_per_shard + 255) / 256), CT = d.payload_elems / 256;
-    std::vector<uint32_t> order;
-    order.reserve((size_t)S * M * RB * CT);
+    std::vector<std::vector<uint32_t>> queues(kQueues);
+    uint32_t item = 0;
     for (uint32_t t = 0; t + 1 < S + M; ++t)
       for (uint32_t s = 0; s < S; ++s) {
         if (t < s || t - s >= M) continue;
         const uint32_t m = t - s;
+        auto& q = queues[item++ % kQueues];
         for (uint32_t r = 0; r < RB; ++r)
-          for (uint32_t c = 0; c < CT; ++c) order.push_back(s | m << 8 | r << 16 | c << 24);
+          for (uint32_t c = 0; c < CT; ++c) q.push_back(s | m << 8 | r << 16 | c << 24);
       }
+    std::vector<uint32_t> order, head(kQueues), len(kQueues);
+    order.reserve((size_t)S * M * RB * CT);
+    for (uint32_t q = 0; q < kQueues; ++q) {
+      head[q] = (uint32_t)order.size();
+      len[q] = (uint32_t)queues[q].size();
+      order.insert(order.end(), queues[q].begin(), queues[q].end());
+    }
+    hipError_t e0 = hipMemcpy(p->base() + p->L.pipe_ctl + 64, head.data(), kQueues * 4, hipMemcpyHostToDevice);
+    if (e0 == hipSuccess) e0 = hipMemcpy(p->base() + p->L.pipe_ctl + 128, len.data(), kQueues * 4, hipMemcpyHostToDevice);
+    if (e0 != hipSuccess) return hip_fail(e0, "uploading the pipeline queues");
     hipError_t e = hipMemcpy(p->base() + p->L.order, order.data(), order.size() * 4, hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "uploading the pipeline order");
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     ks->grid = (uint32_t)std::max(1, cus);
+    // stage weights [S][d][d] -> packed W_s^T, once
+    e = hipDeviceSynchronize();
+    if (e == hipSuccess)
+      e = launch_pack_t(static_cast<const __bf16*>(d.w1), reinterpret_cast<__bf16*>(p->base() + p->L.w1t), S,
+                        d.payload_elems, d.payload_elems, d.payload_elems, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "packing the stage weights");
+  }
+  if (p->desc.kind == PW_GRAPH_MOE) {
+    // expert and router weights -> packed K-contiguous copies, once
+    const pw_plan_desc& d = p->desc;
+    const uint32_t E = d.num_shards, D = d.payload_elems, H = d.hidden;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess)
+      e = launch_pack_t(static_cast<const __bf16*>(d.w1), reinterpret_cast<__bf16*>(p->base() + p->L.w1t), E, D, H, H,
+                        nullptr);
+    if (e == hipSuccess)
+      e = launch_pack_t(static_cast<const __bf16*>(d.w2), reinterpret_cast<__bf16*>(p->base() + p->L.w2t), E, H, D, D,
+                        nullptr);
+    if (e == hipSuccess)
+      e = launch_pack_t(static_cast<const __bf16*>(d.w_router), reinterpret_cast<__bf16*>(p->base() + p->L.wrt), 1, D,
+                        E, 64, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "packing the expert weights");
   }
   return PW_OK;
 }
@@ -121,9 +159,9 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done)
 
   MoeArgs m{};
   m.x = static_cast<const __bf16*>(io->src.base);
-  m.w_router = static_cast<const __bf16*>(d.w_router);
-  m.w1 = static_cast<const __bf16*>(d.w1);
-  m.w2 = static_cast<const __bf16*>(d.w2);
+  m.w1t = reinterpret_cast<const __bf16*>(base + L.w1t);
+  m.w2t = reinterpret_cast<const __bf16*>(base + L.w2t);
+  m.wrt = reinterpret_cast<const __bf16*>(base + L.wrt);
   m.xd = static_cast<__bf16*>(io->dst.base);
   m.h = reinterpret_cast<__bf16*>(base + L.hidden_act);
   m.y = static_cast<__bf16*>(io->b_out);
@@ -280,22 +318,24 @@ int run_pipeline(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipS
   PipeArgs a{};
   a.x = static_cast<const __bf16*>(state->base);
   a.acts = static_cast<__bf16*>(aux);
-  a.w = static_cast<const __bf16*>(d.w1);
+  a.wt = reinterpret_cast<const __bf16*>(p->base() + p->L.w1t);
   a.order = reinterpret_cast<const uint32_t*>(p->base() + p->L.order);
   uint32_t* ctl = reinterpret_cast<uint32_t*>(p->base() + p->L.pipe_ctl);
-  a.ticket = ctl;
-  a.done_ctr = ctl + 1;
-  a.ticket_base = (uint32_t)(ks->calls * (uint64_t)total);
+  a.done_ctr = ctl;
+  a.qctr = ctl + 4;
+  a.qstart = ctl + 16;
+  a.qlen = ctl + 32;
+  a.nq = kQueues;
   a.rb_ctr = reinterpret_cast<uint32_t*>(p->base() + p->L.rb_ctr);
   a.item_ctr = reinterpret_cast<uint32_t*>(p->base() + p->L.item_ctr);
   a.rb_target = (uint32_t)(call * CT);
   a.item_target = (uint32_t)(call * RB);
-  a.done_target = (uint32_t)(call * total);
+  a.done_target = (uint32_t)(call * ks->grid);
   a.S = S; a.M = M; a.rows = R; a.d = D; a.RB = RB; a.CT = CT; a.total_tiles = total;
   a.epoch = (uint32_t)(p->epoch + 1);
   a.f = p->futures();
   p->launch_begin("pipeline", s);
-  hipError_t e = launch_pipeline(a, s);
+  hipError_t e = launch_pipeline(a, ks->grid, s);
   p->launch_end(s);
   if (e != hipSuccess) return hip_fail(e, "launch pipeline");
   ks->calls += 1;

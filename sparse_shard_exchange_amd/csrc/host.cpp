@@ -121,6 +121,9 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
         L.hidden_act = c.take(L.G * (uint64_t)d.hidden * 2);
         L.rb_start = c.take((size_t)(N + 1) * 4);
         L.b_done = c.take((size_t)N * 4);
+        L.w1t = c.take((size_t)N * d.hidden * d.payload_elems * 2);
+        L.w2t = c.take((size_t)N * d.hidden * d.payload_elems * 2);
+        L.wrt = c.take((size_t)64 * d.payload_elems * 2);
       }
       break;
     }
@@ -143,6 +146,7 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
       L.rb_ctr = c.take(S * M * RB * 4);
       L.item_ctr = c.take(S * M * 4);
       L.order = c.take(S * M * RB * CT * 4);
+      L.w1t = c.take(S * d.payload_elems * d.payload_elems * 2);
       break;
     }
     default:

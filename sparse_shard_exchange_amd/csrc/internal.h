@@ -77,13 +77,15 @@ struct ChainArgs {
 struct PipeArgs {
   const __bf16* x;        // [M][rows][d] microbatch inputs
   __bf16* acts;           // [S][M][rows][d] stage outputs
-  const __bf16* w;        // [S][d][d], stored [in][out]
-  const uint32_t* order;  // [total_tiles] claim order, s | m << 8 | r << 16 | c << 24
-  uint32_t* ticket;       // claim counter (cumulative over calls)
-  uint32_t ticket_base;   // claims made by earlier calls
+  const __bf16* wt;       // [S][d][d] packed W_s^T ([out][in], K-contiguous)
+  const uint32_t* order;  // [total_tiles] tiles by queue, s | m << 8 | r << 16 | c << 24
+  const uint32_t* qstart; // [nq] first order index of each queue
+  const uint32_t* qlen;   // [nq] tiles in each queue
+  uint32_t* qctr;         // [nq] claim counters (cleared before each pass)
+  uint32_t nq;
   uint32_t* rb_ctr;       // [S][M][RB] column tiles finished per row block (cumulative)
   uint32_t* item_ctr;     // [S][M] row blocks finished (cumulative)
-  uint32_t* done_ctr;     // tiles finished (cumulative)
+  uint32_t* done_ctr;     // workgroups finished (cumulative)
   uint32_t rb_target, item_target, done_target;
   uint32_t S, M, rows, d, RB, CT, total_tiles;
   uint32_t epoch;
@@ -93,9 +95,9 @@ struct PipeArgs {
 // Arguments of the mixture-of-experts kernels (moe.hip).
 struct MoeArgs {
   const __bf16* x;         // [tokens][d]
-  const __bf16* w_router;  // [d][E]
-  const __bf16* w1;        // [E][d][hidden]
-  const __bf16* w2;        // [E][hidden][d]
+  const __bf16* w1t;       // [E][hidden][d] packed W1^T
+  const __bf16* w2t;       // [E][d][hidden] packed W2^T
+  const __bf16* wrt;       // [64][d] packed W_r^T, experts >= E zero
   __bf16* xd;              // [2 tokens][d] dispatched rows (exchange output)
   __bf16* h;               // [2 tokens][hidden] FFN hidden activations
   __bf16* y;               // [2 tokens][d] expert outputs
@@ -124,10 +126,12 @@ hipError_t launch_b(const ExchangeArgs& a, hipStream_t s);
 size_t scatter_lds_bytes(uint32_t N);
 // mode: 0 chained (one launch, all steps), 1 one node (OpByOp), 2 fused.
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);
-hipError_t launch_pipeline(const PipeArgs& a, hipStream_t s);
+hipError_t launch_pipeline(const PipeArgs& a, uint32_t grid, hipStream_t s);
 hipError_t launch_router(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_prefix(const MoeArgs& a, hipStream_t s);
 hipError_t launch_ffn(const MoeArgs& a, bool second, hipStream_t s);
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s);
+hipError_t launch_pack_t(const __bf16* in, __bf16* out, uint32_t batch, uint32_t K, uint32_t N_in, uint32_t N_out,
+                         hipStream_t s);
 
 }  // namespace pw

@@ -30,32 +30,18 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 // logits[t][e] = sum_k x[t][k] w[k][e] with bf16 products and fp32
 // accumulation (v_mfma_f32_32x32x16_bf16), then per token: the two largest
 // logits (ties to the lower expert id), gates = softmax over those two.
-// LDS holds W^T ([64][d], k contiguous, 16-byte chunks swizzled by row), then
-// is reused for the logits of the workgroup's tokens.
+// LDS holds the packed W^T ([64][d], k contiguous, 16-byte chunks swizzled by
+// row), then is reused for the logits of the workgroup's tokens.
 __global__ __launch_bounds__(256, 1) void k_router(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int d = (int)a.d, E = (int)a.E;
   const int chunks = d / 8;  // 16-byte chunks per W^T row
-  // W [d][E] -> LDS W^T [64][d]; experts >= E are zero rows. Rows of W are
-  // read 8 experts (16 bytes) at a time and scattered into LDS as 2-byte stores.
-  for (int i = tid; i < kMaxExperts * chunks; i += 256) {  // zero the table
-    *reinterpret_cast<bf16x8*>(lds + (int64_t)i * 16) = bf16x8{};
-  }
-  __syncthreads();
-  const int groups = (E + 7) / 8;  // 8-expert groups per row of W
-  for (int i = tid; i < d * groups; i += 256) {
-    const int k = i / groups, e8 = (i - k * groups) * 8;
-    const __bf16* src = a.w_router + (int64_t)k * E + e8;
-    const int ch = k >> 3, kk = k & 7;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = e8 + j;
-      if (e < E) {
-        __bf16* dst = reinterpret_cast<__bf16*>(lds + ((int64_t)e * chunks + (ch ^ (e & 7))) * 16) + kk;
-        *dst = src[j];
-      }
-    }
+  // packed W_r^T [64][d] (experts >= E are zero rows) -> LDS, 16-byte chunks
+  for (int i = tid; i < kMaxExperts * chunks; i += 256) {
+    const int e = i / chunks, ch = i - e * chunks;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(a.wrt + (int64_t)e * d + ch * 8);
+    *reinterpret_cast<bf16x8*>(lds + ((int64_t)e * chunks + (ch ^ (e & 7))) * 16) = v;
   }
   __syncthreads();
 
@@ -165,7 +151,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a) {
   const int64_t seg0 = a.seg[e], n_e = a.seg[e + 1] - seg0;
   const int64_t row0 = seg0 + (int64_t)rb * mm::BM;
   const int rows = (int)min<int64_t>(mm::BM, n_e - (int64_t)rb * mm::BM);
-  if (threadIdx.x == 0) go = await(a.f, NODE_EXCH, e, a.epoch);  // the expert's input is complete
+  if (threadIdx.x == 0) go = await_prior(a.f, NODE_EXCH, e, a.epoch);  // the expert's input is complete
   __syncthreads();
   if (!go) return;
   mm::Tile tile;
@@ -174,13 +160,13 @@ __global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a) {
   tile.A = in + row0 * K;
   tile.lda = K;
   tile.rows = rows;
-  tile.B = (kSecond ? a.w2 : a.w1) + (int64_t)e * K * N + (int64_t)c * mm::BN;
-  tile.ldb = N;
+  tile.Bt = (kSecond ? a.w2t : a.w1t) + (int64_t)e * K * N + (int64_t)c * mm::BN * K;
+  tile.ldb = K;
   tile.K = (int)K;
   mm::f32x16 acc[4][4];
   mm::tile_mma(tile, lds, acc);
   __bf16* out = (kSecond ? a.y : a.h) + row0 * N + (int64_t)c * mm::BN;
-  mm::store_tile<!kSecond>(acc, out, N, rows);
+  mm::store_tile<!kSecond>(acc, lds, out, N, rows);
   if (kSecond) {  // B[e] completes with the last tile of its segment
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -199,7 +185,7 @@ __global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
   bool ok = true;
   if (t < a.tokens) {
     const int e0 = a.experts[t * 2], e1 = a.experts[t * 2 + 1];
-    if (lane == 0) ok = await(a.f, NODE_B, e0, a.epoch) && await(a.f, NODE_B, e1, a.epoch);
+    if (lane == 0) ok = await_prior(a.f, NODE_B, e0, a.epoch) && await_prior(a.f, NODE_B, e1, a.epoch);
     ok = __shfl((int)ok, 0, 64) != 0;
     if (ok) {
       const float g0 = a.gates[t * 2], g1 = a.gates[t * 2 + 1];
@@ -244,13 +230,13 @@ hipError_t launch_ffn(const MoeArgs& a, bool second, hipStream_t s) {
   const uint32_t CT = (second ? a.d : a.hidden) / mm::BN;
   const uint64_t blocks = (uint64_t)a.max_row_blocks * CT;
   if (second) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_ffn<true>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsBytes);
+    hipError_t e = hipFuncSetAttribute((const void*)k_ffn<true>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsTotal);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ffn<true>, dim3((uint32_t)blocks), dim3(mm::NT), mm::kLdsBytes, s, a);
+    hipLaunchKernelGGL(k_ffn<true>, dim3((uint32_t)blocks), dim3(mm::NT), mm::kLdsTotal, s, a);
   } else {
-    hipError_t e = hipFuncSetAttribute((const void*)k_ffn<false>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsBytes);
+    hipError_t e = hipFuncSetAttribute((const void*)k_ffn<false>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsTotal);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ffn<false>, dim3((uint32_t)blocks), dim3(mm::NT), mm::kLdsBytes, s, a);
+    hipLaunchKernelGGL(k_ffn<false>, dim3((uint32_t)blocks), dim3(mm::NT), mm::kLdsTotal, s, a);
   }
   return hipGetLastError();
 }
