@@ -11,15 +11,23 @@
 //
 // K streams through a ring of 4 LDS stages of 32 columns (A 256 x 32 and
 // B^T 256 x 32 bf16 = 32 KiB per stage, 128 KiB in all) filled by direct
-// global-to-LDS loads (global_load_lds_dwordx4: no staging registers), three
-// stages ahead of the one being multiplied. Each wave-wide load writes 1 KiB
-// of LDS contiguously (16 bytes per lane), so the 16-byte chunks of each
-// 64-byte LDS row are permuted by picking which global chunk each lane
-// fetches: chunk c of row r sits at slot c ^ ((r >> 2) & 3), which makes the
-// MFMA operand reads (lane l reads row l % 32, chunk l / 32 of the k-step)
-// free of LDS bank conflicts. Ring slots are recycled behind raw workgroup
-// barriers with explicit vector-memory counter waits, so three stages stay in
-// flight across the barrier.
+// global-to-LDS loads (global_load_lds_dwordx4: no staging registers). Each
+// wave-wide load writes 1 KiB of LDS contiguously (16 bytes per lane), so the
+// 16-byte chunks of each 64-byte LDS row are permuted by picking which global
+// chunk each lane fetches: chunk c of row r sits at slot c ^ ((r >> 2) & 3),
+// which makes the MFMA operand reads (lane l reads row l % 32, chunk l / 32 of
+// the k-step) free of LDS bank conflicts.
+//
+// A stage is consumed in two halves (its two k-steps of 16). One workgroup
+// barrier per stage, between the halves, publishes the next stage and frees
+// the ring slot of the previous one. Stage j is loaded in two halves spread
+// between the MFMAs of the second half of stage j - 3 and the first half of
+// stage j - 2. Issued as one burst after the barrier, the 32 loads of the
+// workgroup would queue up in the address unit and stall each wave's MFMA
+// stream until its own loads were taken; spread out, they are accepted while
+// the matrix core is busy. Waits on the vector-memory counter are explicit
+// and exact: the loop is peeled so that every wait, load and fragment read is
+// unconditional and the compiler can interleave them with the MFMAs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,15 +91,16 @@ __device__ __forceinline__ Lanes lane_offsets(const Tile& t) {
   return o;
 }
 
-// Issue the direct-to-LDS loads of K columns [k0, k0 + 32) into one stage:
-// 4 loads of A and 4 of B^T per lane (8 vector-memory operations).
-__device__ __forceinline__ void issue_stage(const Tile& t, const Lanes& o, int k0, unsigned char* stage) {
+// Issue half h (0 or 1) of the direct-to-LDS loads of K columns [k0, k0 + 32)
+// into one stage: loads 2h and 2h + 1 of A and of B^T (4 vector-memory
+// operations per lane).
+__device__ __forceinline__ void issue_half(const Tile& t, const Lanes& o, int k0, unsigned char* stage, int h) {
   const int w = threadIdx.x >> 6;
   const unsigned char* A = reinterpret_cast<const unsigned char*>(t.A) + (uint32_t)k0 * 2u;
   const unsigned char* B = reinterpret_cast<const unsigned char*>(t.Bt) + (uint32_t)k0 * 2u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int group = w * 4 + i;
+  for (int ii = 0; ii < 2; ++ii) {
+    const int i = 2 * h + ii, group = w * 4 + i;
     __builtin_amdgcn_global_load_lds(A + o.a[i], (lds_ptr)(stage + group * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(B + o.b[i], (lds_ptr)(stage + kHalf + group * 1024), 16, 0, 0);
   }
@@ -135,8 +144,7 @@ __device__ __forceinline__ void read_frags(const unsigned char* stage, const Fra
   for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(stage + kHalf + f.b_row[j] + ((c ^ f.b_sw[j]) << 4));
 }
 
-// 16 MFMAs of one k-step; the 8 fragment reads issued just before are spread
-// between the first 8 of them, so their latency hides under the matrix core.
+// 16 MFMAs of one k-step.
 __device__ __forceinline__ void mfma_step(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -144,22 +152,66 @@ __device__ __forceinline__ void mfma_step(const bf16x8 (&a)[4], const bf16x8 (&b
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
 }
 
-__device__ __forceinline__ void interleave_reads_with_mfma() {
+// Instruction order inside one half stage: the 8 fragment reads (of the next
+// half) each follow an MFMA, so their latency hides under the matrix core;
+// with kLoads, the 4 loads of a half ring stage sit between the remaining 8
+// MFMAs. Scheduling-group masks: 0x008 MFMA, 0x100 LDS read, 0x020
+// vector-memory read.
+template <bool kLoads>
+__device__ __forceinline__ void schedule_half() {
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  if (kLoads) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // nothing crosses into the next half
 }
 
-// The whole K loop of one tile. `lds` holds kLdsBytes. Stage ks is consumed
-// in two halves: the MFMAs of its first k-step run while its second k-step's
-// fragments are read; then (while those MFMAs drain) the next stage is
-// awaited, the barrier is passed and the ring slot freed by the previous
-// stage is refilled; then the second k-step's MFMAs run while the next
-// stage's first fragments are read. On return every wave has finished reading
-// LDS and every load has landed.
+__device__ __forceinline__ unsigned char* ring_slot(unsigned char* lds, int stage) {
+  return lds + (stage & (kStages - 1)) * kStageBytes;
+}
+
+// One stage ks of the K loop. On entry a0/b0 hold its first k-step's
+// fragments; on exit they hold the first k-step's fragments of stage ks + 1.
+// Stage j is loaded in two halves: the first during the second half of stage
+// j - 3 (into the slot the barrier there freed), the second during the first
+// half of stage j - 2. kLoad2 / kLoad3: issue the second half of stage ks + 2
+// / the first half of stage ks + 3. kWait: vector-memory operations allowed
+// in flight once stage ks + 1 has landed (those issued after it).
+template <bool kLoad2, bool kLoad3, int kWait>
+__device__ __forceinline__ void k_stage(const Tile& t, const Lanes& o, const Frag& f, unsigned char* lds, int ks,
+                                        bf16x8 (&a0)[4], bf16x8 (&b0)[4], bf16x8 (&a1)[4], bf16x8 (&b1)[4],
+                                        f32x16 (&acc)[4][4]) {
+  read_frags(ring_slot(lds, ks), f, 1, a1, b1);
+  // loads after the reads in program order: the compiler keeps LDS-writing
+  // loads behind earlier LDS reads (these go to another slot)
+  if (kLoad2) issue_half(t, o, (ks + 2) * BK, ring_slot(lds, ks + 2), 1);
+  mfma_step(a0, b0, acc);
+  schedule_half<kLoad2>();
+  wait_vmem<kWait>();
+  ring_barrier();  // every wave: stage ks+1 visible, done reading stage ks-1
+  __builtin_amdgcn_sched_barrier(0);
+  // (on the last stage this reads a stale slot, harmlessly: the reads stay
+  // unconditional so that the counter waits stay exact)
+  read_frags(ring_slot(lds, ks + 1), f, 0, a0, b0);
+  if (kLoad3) issue_half(t, o, (ks + 3) * BK, ring_slot(lds, ks + 3), 0);
+  mfma_step(a1, b1, acc);
+  schedule_half<kLoad3>();
+}
+
+// The whole K loop of one tile; K / BK must be at least kStages. `lds` holds
+// kLdsBytes. On return every wave has finished reading LDS and every load has
+// landed.
 __device__ __forceinline__ void tile_mma(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -168,37 +220,20 @@ __device__ __forceinline__ void tile_mma(const Tile& t, unsigned char* lds, f32x
   const Frag f = frag_offsets();
   const Lanes o = lane_offsets(t);
   const int nk = t.K / BK;
-  for (int s = 0; s < kStages - 1 && s < nk; ++s) issue_stage(t, o, s * BK, lds + s * kStageBytes);
-  // stage 0 landed: at most stages 1 and 2 (16 operations) still in flight
-  if (nk >= 3)
-    wait_vmem<16>();
-  else if (nk == 2)
-    wait_vmem<8>();
-  else
-    wait_vmem<0>();
+  issue_half(t, o, 0, ring_slot(lds, 0), 0);
+  issue_half(t, o, 0, ring_slot(lds, 0), 1);
+  issue_half(t, o, BK, ring_slot(lds, 1), 0);
+  issue_half(t, o, BK, ring_slot(lds, 1), 1);
+  issue_half(t, o, 2 * BK, ring_slot(lds, 2), 0);
+  wait_vmem<12>();  // stage 0 landed
   ring_barrier();
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   read_frags(lds, f, 0, a0, b0);
-  for (int ks = 0; ks < nk; ++ks) {
-    const unsigned char* stage = lds + (ks & (kStages - 1)) * kStageBytes;
-    read_frags(stage, f, 1, a1, b1);
-    mfma_step(a0, b0, acc);
-    interleave_reads_with_mfma();
-    // stage ks+1 landed: stage ks+2 (issued last iteration) may remain in flight
-    if (ks + 2 < nk)
-      wait_vmem<8>();
-    else
-      wait_vmem<0>();
-    ring_barrier();  // every wave: stage ks+1 visible, done reading stage ks-1
-    if (ks + kStages - 1 < nk)
-      issue_stage(t, o, (ks + kStages - 1) * BK, lds + ((ks + kStages - 1) & (kStages - 1)) * kStageBytes);
-    // first fragments of the next stage (on the last stage, harmlessly this
-    // one again: the reads stay unconditional so their wait is exact)
-    const int nxt = ks + 1 < nk ? ks + 1 : ks;
-    read_frags(lds + (nxt & (kStages - 1)) * kStageBytes, f, 0, a0, b0);
-    mfma_step(a1, b1, acc);
-    interleave_reads_with_mfma();
-  }
+  int ks = 0;
+  for (; ks < nk - 3; ++ks) k_stage<true, true, 8>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
+  k_stage<true, false, 8>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
+  k_stage<false, false, 0>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
+  k_stage<false, false, 0>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
   ring_barrier();
 }
 
