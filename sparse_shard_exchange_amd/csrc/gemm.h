@@ -7,7 +7,8 @@
 // (w >> 1, w & 1) as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, accumulators
 // in AGPRs. The MFMA is fed B^T as its first operand and A as its second, so
 // each block accumulates C^T: a lane then holds 4 consecutive output columns
-// of one row per register quad, and the epilogue writes 8 bytes at a time.
+// of one row per register quad, and lanes l and l + 32 hold the two halves of
+// 8 consecutive columns, which the epilogue joins with one lane swap.
 //
 // K streams through a ring of 4 LDS stages of 32 columns (A 256 x 32 and
 // B^T 256 x 32 bf16 = 32 KiB per stage, 128 KiB in all) filled by direct
@@ -39,10 +40,13 @@ namespace mm {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256, kStages = 4;
+#ifndef PW_MM_STAGES
+#define PW_MM_STAGES 4
+#endif
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256, kStages = PW_MM_STAGES;
 constexpr int kHalf = BM * BK * 2;              // one operand block of a stage: 16 KiB
 constexpr int kStageBytes = 2 * kHalf;          // 32 KiB
-constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
+constexpr int kLdsBytes = kStages * kStageBytes;
 
 // Byte offsets inside a tile (rows x K of A, 256 x K of B^T, the output tile)
 // must stay below 4 GiB: they are 32-bit.
@@ -71,22 +75,37 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// threadIdx.x through an empty asm statement: values derived from it are
+// recomputed at each call instead of being hoisted out of a loop over tiles
+// and kept live across the K loop (per-lane offsets, 16+ registers).
+__device__ __forceinline__ uint32_t opaque_tid() {
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  return tid;
+}
+
 // Per-lane byte offsets (32-bit, from the tile's wave-uniform base pointers)
 // of the global chunks this lane moves into LDS, for k0 = 0.
 struct Lanes {
   uint32_t a[4], b[4];
 };
 
+// The row strides pass through an empty asm statement so that, in a loop
+// over tiles, the compiler recomputes these offsets per tile instead of
+// hoisting them (and keeping them live across the K loop).
 __device__ __forceinline__ Lanes lane_offsets(const Tile& t) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t tid = opaque_tid();
+  const int lane = tid & 63, w = tid >> 6;
+  uint32_t lda = (uint32_t)t.lda, ldb = (uint32_t)t.ldb;
+  asm volatile("" : "+s"(lda), "+s"(ldb));
   Lanes o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (w * 4 + i) * 16 + (lane >> 2);  // 16 rows per wave-wide load
     const int c = (lane & 3) ^ swz(row);             // the chunk this lane's slot holds
     const int ra = row < t.rows ? row : t.rows - 1;
-    o.a[i] = (uint32_t)ra * (uint32_t)t.lda * 2u + (uint32_t)c * 16u;
-    o.b[i] = (uint32_t)row * (uint32_t)t.ldb * 2u + (uint32_t)c * 16u;
+    o.a[i] = (uint32_t)ra * lda * 2u + (uint32_t)c * 16u;
+    o.b[i] = (uint32_t)row * ldb * 2u + (uint32_t)c * 16u;
   }
   return o;
 }
@@ -120,7 +139,8 @@ struct Frag {
 };
 
 __device__ __forceinline__ Frag frag_offsets() {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t tid = opaque_tid();
+  const int lane = tid & 63, w = tid >> 6;
   const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
   Frag f;
 #pragma unroll
@@ -178,41 +198,60 @@ __device__ __forceinline__ void schedule_half() {
 }
 
 __device__ __forceinline__ unsigned char* ring_slot(unsigned char* lds, int stage) {
-  return lds + (stage & (kStages - 1)) * kStageBytes;
+  return lds + (stage % kStages) * kStageBytes;
 }
 
 // One stage ks of the K loop. On entry a0/b0 hold its first k-step's
 // fragments; on exit they hold the first k-step's fragments of stage ks + 1.
 // Stage j is loaded in two halves: the first during the second half of stage
-// j - 3 (into the slot the barrier there freed), the second during the first
-// half of stage j - 2. kLoad2 / kLoad3: issue the second half of stage ks + 2
-// / the first half of stage ks + 3. kWait: vector-memory operations allowed
-// in flight once stage ks + 1 has landed (those issued after it).
-template <bool kLoad2, bool kLoad3, int kWait>
+// j - S + 1 (into the slot the barrier there freed), the second during the
+// first half of stage j - S + 2 (S = kStages). kLoadB / kLoadA: issue the
+// second half of stage ks + S - 2 / the first half of stage ks + S - 1.
+// kWait: vector-memory operations allowed in flight once stage ks + 1 has
+// landed (those issued after it).
+template <bool kLoadB, bool kLoadA, int kWait>
 __device__ __forceinline__ void k_stage(const Tile& t, const Lanes& o, const Frag& f, unsigned char* lds, int ks,
                                         bf16x8 (&a0)[4], bf16x8 (&b0)[4], bf16x8 (&a1)[4], bf16x8 (&b1)[4],
                                         f32x16 (&acc)[4][4]) {
   read_frags(ring_slot(lds, ks), f, 1, a1, b1);
   // loads after the reads in program order: the compiler keeps LDS-writing
   // loads behind earlier LDS reads (these go to another slot)
-  if (kLoad2) issue_half(t, o, (ks + 2) * BK, ring_slot(lds, ks + 2), 1);
+  if (kLoadB) issue_half(t, o, (ks + kStages - 2) * BK, ring_slot(lds, ks + kStages - 2), 1);
   mfma_step(a0, b0, acc);
-  schedule_half<kLoad2>();
+  schedule_half<kLoadB>();
   wait_vmem<kWait>();
   ring_barrier();  // every wave: stage ks+1 visible, done reading stage ks-1
   __builtin_amdgcn_sched_barrier(0);
   // (on the last stage this reads a stale slot, harmlessly: the reads stay
   // unconditional so that the counter waits stay exact)
   read_frags(ring_slot(lds, ks + 1), f, 0, a0, b0);
-  if (kLoad3) issue_half(t, o, (ks + 3) * BK, ring_slot(lds, ks + 3), 0);
+  if (kLoadA) issue_half(t, o, (ks + kStages - 1) * BK, ring_slot(lds, ks + kStages - 1), 0);
   mfma_step(a1, b1, acc);
-  schedule_half<kLoad3>();
+  schedule_half<kLoadA>();
 }
 
-// The whole K loop of one tile; K / BK must be at least kStages. `lds` holds
-// kLdsBytes. On return every wave has finished reading LDS and every load has
-// landed.
-__device__ __forceinline__ void tile_mma(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4]) {
+// The loads of the first stages of a tile (stage S - 2 only half): issued
+// ahead, e.g. while the previous tile's epilogue runs, once every wave has
+// finished reading the ring. tile_finish must follow with the same tile.
+__device__ __forceinline__ void tile_start(const Tile& t, unsigned char* lds) {
+  constexpr int S = kStages;
+  const Lanes o = lane_offsets(t);
+#pragma unroll
+  for (int s = 0; s < S - 2; ++s) {
+    issue_half(t, o, s * BK, ring_slot(lds, s), 0);
+    issue_half(t, o, s * BK, ring_slot(lds, s), 1);
+  }
+  issue_half(t, o, (S - 2) * BK, ring_slot(lds, S - 2), 0);
+}
+
+// The K loop of a tile whose first stages tile_start issued; K / BK must be
+// at least kStages. `lds` holds kLdsBytes. Vector-memory operations issued
+// between the two calls (epilogue stores) are allowed: loads complete in
+// order among themselves, so each wait still covers the stage it names, and
+// at worst it also waits for those stores. On return every wave has finished
+// reading LDS and every load has landed.
+__device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4]) {
+  constexpr int S = kStages, W = 8 * (S - 3);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -220,33 +259,22 @@ __device__ __forceinline__ void tile_mma(const Tile& t, unsigned char* lds, f32x
   const Frag f = frag_offsets();
   const Lanes o = lane_offsets(t);
   const int nk = t.K / BK;
-  issue_half(t, o, 0, ring_slot(lds, 0), 0);
-  issue_half(t, o, 0, ring_slot(lds, 0), 1);
-  issue_half(t, o, BK, ring_slot(lds, 1), 0);
-  issue_half(t, o, BK, ring_slot(lds, 1), 1);
-  issue_half(t, o, 2 * BK, ring_slot(lds, 2), 0);
-  wait_vmem<12>();  // stage 0 landed
+  wait_vmem<8 * (S - 3) + 4>();  // stage 0 landed (a half stage is 4 operations)
   ring_barrier();
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   read_frags(lds, f, 0, a0, b0);
   int ks = 0;
-  for (; ks < nk - 3; ++ks) k_stage<true, true, 8>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
-  k_stage<true, false, 8>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
+  for (; ks < nk - S + 1; ++ks) k_stage<true, true, W>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
+  k_stage<true, false, W>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);  // issues the last half (stage nk-1)
+  if (S == 5) k_stage<false, false, 8>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
   k_stage<false, false, 0>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
   k_stage<false, false, 0>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
   ring_barrier();
 }
 
-// Block (i, j) holds C^T: register r of a lane is output row
-// acc_row(i) = wm + 32 i + lane % 32 and column acc_col(j, r) =
-// wn + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4.
-__device__ __forceinline__ int acc_row(int i) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  return (w >> 1) * 128 + i * 32 + (lane & 31);
-}
-__device__ __forceinline__ int acc_col(int j, int q) {  // first of the 4 columns of quad q
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  return (w & 1) * 128 + j * 32 + q * 8 + (lane >> 5) * 4;
+__device__ __forceinline__ void tile_mma(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4]) {
+  tile_start(t, lds);
+  tile_finish(t, lds, acc);
 }
 
 // GELU(z) = z Phi(z) with Phi from erfc by Abramowitz & Stegun formula
@@ -266,59 +294,50 @@ __device__ __forceinline__ float gelu(float z) {
   return z * phi;
 }
 
-// Epilogue staging: 128 rows of fp32 at a time, rows padded by 16 bytes so
-// that the 32 lanes writing one column quad of 32 different rows hit
-// different LDS banks.
-constexpr int kEpiStride = BN + 4;                  // floats per staged row
-constexpr int kEpiBytes = 128 * kEpiStride * 4;     // 133,120 bytes
-constexpr int kLdsTotal = kEpiBytes > kLdsBytes ? kEpiBytes : kLdsBytes;
+constexpr int kLdsTotal = kLdsBytes;  // the epilogue needs no LDS
 
-// Store the tile as bf16 (round to nearest even), optionally through GELU.
-// The accumulators go to LDS straight from AGPRs (4 consecutive columns of a
-// row per register quad), in two halves of 128 rows; then every thread reads
-// 4 consecutive values of a row, applies the epilogue and writes 8 bytes, so
-// each wave stores one whole 512-byte row per instruction. `lds` holds kLdsTotal bytes and is
-// free (tile_mma ends with a barrier).
+// Store the tile as bf16 (round to nearest even), optionally through GELU,
+// straight from the accumulators; rows >= `rows` are not stored. Block (i, j)
+// holds C^T: register 4q + e of lane l is output row wm + 32 i + l % 32,
+// column wn + 32 j + 8 q + 4 (l / 32) + e. For each pair of quads (2p, 2p+1)
+// one v_permlane32_swap per packed dword hands lane l + 32's half of quad 2p
+// to lane l and lane l's half of quad 2p + 1 to lane l + 32, so that lane l
+// holds columns 16 p + [0, 8) and lane l + 32 columns 16 p + [8, 16) of the
+// row: one 16-byte store each, 32 contiguous bytes per row and instruction.
 template <bool kGelu>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], unsigned char* lds, __bf16* out, int64_t ldo,
-                                           int rows) {
-  typedef __attribute__((ext_vector_type(4))) float f32x4;
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], __bf16* out, int64_t ldo, int rows) {
   typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-  float* L = reinterpret_cast<float*>(lds);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const uint32_t tid = opaque_tid();
+  const int lane = tid & 63, w = tid >> 6;
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
   unsigned char* base = reinterpret_cast<unsigned char*>(out);
+  uint32_t ld = (uint32_t)ldo;  // opaque per call, as in lane_offsets
+  asm volatile("" : "+s"(ld));
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    // wave rows wm + 64 h + [0, 64) -> staged rows (w >> 1) * 64 + [0, 64)
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm + 32 * i + (lane & 31);
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * h + ii;
-      const int lrow = (w >> 1) * 64 + 32 * ii + (lane & 31);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int p = 0; p < 2; ++p) {
+        bf16x4 v0, v1;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(L + lrow * kEpiStride + acc_col(j, q)) = v;
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = acc[i][j][8 * p + e], x1 = acc[i][j][8 * p + 4 + e];
+          v0[e] = (__bf16)(kGelu ? gelu(x0) : x0);
+          v1[e] = (__bf16)(kGelu ? gelu(x1) : x1);
         }
-    }
-    __syncthreads();
-    // consecutive lanes read consecutive 16-byte chunks of a staged row
-    for (int k = threadIdx.x; k < 128 * (BN / 4); k += NT) {
-      const int lrow = k >> 6, ch = k & 63;
-      const int orow = (lrow >> 6) * 128 + 64 * h + (lrow & 63);
-      if (orow < rows) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(L + lrow * kEpiStride + ch * 4);
-        bf16x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(kGelu ? gelu(a[e]) : a[e]);
-        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-        // streaming store: the output is not re-read by this workgroup
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, o),
-                                    reinterpret_cast<u32x2*>(base + (uint32_t)orow * (uint32_t)ldo * 2u + (uint32_t)ch * 8u));
+        const u32x2 d0 = __builtin_bit_cast(u32x2, v0), d1 = __builtin_bit_cast(u32x2, v1);
+        // lanes 32..63 of the first operand trade places with lanes 0..31 of the second
+        const auto lo = __builtin_amdgcn_permlane32_swap(d0.x, d1.x, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(d0.y, d1.y, false, false);
+        const u32x4 v = {lo[0], hi[0], lo[1], hi[1]};
+        const int col = wn + 32 * j + 16 * p + 8 * (lane >> 5);
+        if (row < rows)
+          *reinterpret_cast<u32x4*>(base + ((uint32_t)row * ld + (uint32_t)col) * 2u) = v;
       }
-    }
-    __syncthreads();
   }
 }
 

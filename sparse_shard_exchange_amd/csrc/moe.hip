@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a) {
   mm::f32x16 acc[4][4];
   mm::tile_mma(tile, lds, acc);
   __bf16* out = (kSecond ? a.y : a.h) + row0 * N + (int64_t)c * mm::BN;
-  mm::store_tile<!kSecond>(acc, lds, out, N, rows);
+  mm::store_tile<!kSecond>(acc, out, N, rows);
   if (kSecond) {  // B[e] completes with the last tile of its segment
     __syncthreads();
     if (threadIdx.x == 0) {

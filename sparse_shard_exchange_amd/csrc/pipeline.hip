@@ -50,77 +50,153 @@ __global__ void k_pipe_reset(PipeArgs a) {
   if (threadIdx.x < a.nq) a.qctr[threadIdx.x] = 0;
 }
 
-// Persistent: one workgroup per CU loops over tiles. The plan puts all 32
+// Row block (s, m, r) of stage s is complete once all its column tiles have
+// been published (cumulative counter, target per call).
+__device__ __forceinline__ const uint32_t* gate_of(const PipeArgs& a, uint32_t s, uint32_t m, uint32_t r) {
+  return a.rb_ctr + ((uint64_t)(s - 1) * a.M + m) * a.RB + r;
+}
+
+struct PipeTile {
+  uint32_t s, m, r, c;
+};
+
+__device__ __forceinline__ PipeTile decode(const PipeArgs& a, uint32_t t) {
+  const uint32_t code = a.order[t];
+  return {code & 0xFF, (code >> 8) & 0xFF, (code >> 16) & 0xFF, code >> 24};
+}
+
+__device__ __forceinline__ mm::Tile tile_of(const PipeArgs& a, const PipeTile& p) {
+  const uint64_t item_elems = (uint64_t)a.rows * a.d;
+  const __bf16* in = p.s == 0 ? a.x + (uint64_t)p.m * item_elems : a.acts + ((uint64_t)(p.s - 1) * a.M + p.m) * item_elems;
+  mm::Tile tile;
+  tile.A = in + (uint64_t)p.r * mm::BM * a.d;
+  tile.lda = a.d;
+  tile.rows = min((int)mm::BM, (int)a.rows - (int)(p.r * mm::BM));
+  tile.Bt = a.wt + (uint64_t)p.s * a.d * a.d + (uint64_t)p.c * mm::BN * a.d;
+  tile.ldb = a.d;
+  tile.K = a.d;
+  return tile;
+}
+
+// Thread 0: count tile p as done; the last tile of a row block completes it
+// (release: the tile's stores, completed by every wave before the barrier
+// that precedes this call, become visible first), the last row block of an
+// item fires the item's future.
+__device__ __forceinline__ void publish(const PipeArgs& a, const PipeTile& p) {
+  uint32_t* ctr = a.rb_ctr + ((uint64_t)p.s * a.M + p.m) * a.RB + p.r;
+  const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (reached(old + 1, a.rb_target)) {
+    uint32_t* ic = a.item_ctr + (uint64_t)p.s * a.M + p.m;
+    const uint32_t io = __hip_atomic_fetch_add(ic, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (reached(io + 1, a.item_target)) fire(a.f, NODE_STAGE, p.s * a.M + p.m, a.epoch, false);
+  }
+}
+
+// Thread 0: is tile p's input row block complete (acquire)? With `block`,
+// wait for it, bounded by the spin limit (false once it expires).
+__device__ __forceinline__ bool input_ready(const PipeArgs& a, const PipeTile& p, bool block) {
+  if (p.s == 0) return true;
+  const uint32_t* ctr = gate_of(a, p.s, p.m, p.r);
+  if (reached(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), a.rb_target)) return true;
+  if (!block) return false;
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+    __builtin_amdgcn_s_sleep(2);
+    if (reached(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), a.rb_target)) return true;
+    if (wall_clock64() - t0 > a.f.spin_ticks) {
+      latch(a.f.status, ST_TIMEOUT);
+      return false;
+    }
+  }
+}
+
+struct Claims {
+  uint32_t next;   // the ticket after the current candidate (thread 0 writes it)
+  uint32_t ready;  // thread 0's verdict on the candidate
+};
+
+// Starting from candidate ticket t (already claimed; cl.next holds the one
+// after it), wait for a tile's input and issue its first stages. A tile whose
+// wait expires is published as done (so nothing downstream waits forever) and
+// the next ticket is taken. Returns false once the queues are empty.
+__device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl, uint32_t home, uint32_t t,
+                               PipeTile& p, mm::Tile& tile) {
+  while (t != kNone) {
+    p = decode(a, t);
+    tile = tile_of(a, p);
+    if (threadIdx.x == 0) cl.ready = input_ready(a, p, true);
+    __syncthreads();
+    if (cl.ready) {
+      mm::tile_start(tile, lds);
+      return true;
+    }
+    if (threadIdx.x == 0) publish(a, p);
+    t = cl.next;
+    __syncthreads();  // every thread has read next and ready
+    if (threadIdx.x == 0 && t != kNone) cl.next = claim(a, home);
+  }
+  return false;
+}
+
+// Persistent: one workgroup per CU loops over tiles. The plan puts all
 // tiles of an item in one XCD's queue (items dealt round-robin to the 8
 // queues in GPipe order), so the item's activation rows and weight columns
 // are shared through that XCD's L2. Each queue is in dependency order and a
 // workgroup leaves its own queue only once it is empty, so the earliest
-// unfinished tile is always held or next in line: no deadlock.
+// unfinished tile is always held or next in line.
+//
+// The epilogue of a tile overlaps the operand loads of the next: once the K
+// loop of tile t ends, the first stages of tile t+1 are issued if its input
+// row block is already complete (one non-blocking check), then tile t is
+// stored and published, and only then, if the check failed, does the
+// workgroup wait for t+1's input. Tile t+1 may depend on tile t itself, so
+// the blocking wait never comes before t is published.
 __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  __shared__ uint32_t next;
-  __shared__ uint32_t go;
+  __shared__ Claims cl;
   const uint32_t tid = threadIdx.x;
   const uint64_t item_elems = (uint64_t)a.rows * a.d;
   uint32_t home = 0;
   if (tid == 0) {
     home = xcc_id() % a.nq;
-    next = claim(a, home);
+    cl.next = claim(a, home);
   }
   __syncthreads();
-  while (true) {
-    const uint32_t t = next;
-    if (t == kNone) break;  // uniform: every thread read the same value
-    const uint32_t code = a.order[t];
-    const uint32_t s = code & 0xFF, m = (code >> 8) & 0xFF, r = (code >> 16) & 0xFF, c = code >> 24;
-    __syncthreads();  // all threads have read `next`
+  const uint32_t first = cl.next;
+  __syncthreads();
+  if (tid == 0 && first != kNone) cl.next = claim(a, home);
+  PipeTile p;
+  mm::Tile tile;
+  bool have = start_blocking(a, lds, cl, home, first, p, tile);
+  while (have) {
+    mm::f32x16 acc[4][4];
+    mm::tile_finish(tile, lds, acc);  // ends with a barrier: cl.next is visible
+    const uint32_t t2 = cl.next;
+    PipeTile p2{0, 0, 0, 0};
+    mm::Tile tile2 = tile;
+    if (t2 != kNone) {
+      p2 = decode(a, t2);
+      tile2 = tile_of(a, p2);
+    }
+    __syncthreads();  // every thread has read next
     if (tid == 0) {
-      bool ok = true;
-      if (s > 0) {  // gate on the row-block future of the previous stage
-        const uint32_t* ctr = a.rb_ctr + ((uint64_t)(s - 1) * a.M + m) * a.RB + r;
-        if (!reached(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), a.rb_target)) {
-          const uint64_t t0 = wall_clock64();
-          while (true) {
-            __builtin_amdgcn_s_sleep(2);
-            if (reached(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), a.rb_target)) break;
-            if (wall_clock64() - t0 > a.f.spin_ticks) {
-              latch(a.f.status, ST_TIMEOUT);
-              ok = false;
-              break;
-            }
-          }
-        }
-      }
-      go = ok;
-      next = claim(a, home);  // claimed now, used after this tile
+      cl.ready = t2 != kNone && input_ready(a, p2, false);
+      if (t2 != kNone) cl.next = claim(a, home);
     }
     __syncthreads();
-    if (go) {
-      const __bf16* in = s == 0 ? a.x + (uint64_t)m * item_elems : a.acts + ((uint64_t)(s - 1) * a.M + m) * item_elems;
-      __bf16* out = a.acts + ((uint64_t)s * a.M + m) * item_elems;
-      mm::Tile tile;
-      tile.A = in + (uint64_t)r * mm::BM * a.d;
-      tile.lda = a.d;
-      tile.rows = min((int)mm::BM, (int)a.rows - (int)(r * mm::BM));
-      tile.Bt = a.wt + (uint64_t)s * a.d * a.d + (uint64_t)c * mm::BN * a.d;
-      tile.ldb = a.d;
-      tile.K = a.d;
-      mm::f32x16 acc[4][4];
-      mm::tile_mma(tile, lds, acc);
-      mm::store_tile<true>(acc, lds, out + (uint64_t)r * mm::BM * a.d + (uint64_t)c * mm::BN, a.d, tile.rows);
-    }
-    // publish: every wave's stores complete, then one release per tile. A tile
-    // whose wait expired still counts, so nothing downstream waits forever.
+    const bool started = cl.ready;
+    if (started) mm::tile_start(tile2, lds);
+    __bf16* out = a.acts + ((uint64_t)p.s * a.M + p.m) * item_elems + (uint64_t)p.r * mm::BM * a.d +
+                  (uint64_t)p.c * mm::BN;
+    mm::store_tile<true>(acc, out, a.d, tile.rows);
     mm::wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t* ctr = a.rb_ctr + ((uint64_t)s * a.M + m) * a.RB + r;
-      const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      if (reached(old + 1, a.rb_target)) {  // row block complete
-        uint32_t* ic = a.item_ctr + (uint64_t)s * a.M + m;
-        const uint32_t io = __hip_atomic_fetch_add(ic, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (reached(io + 1, a.item_target)) fire(a.f, NODE_STAGE, s * a.M + m, a.epoch, false);
-      }
+    __syncthreads();  // every wave's stores complete; every thread has read ready
+    if (tid == 0) publish(a, p);
+    if (started) {
+      p = p2;
+      tile = tile2;
+    } else {
+      have = start_blocking(a, lds, cl, home, t2, p, tile);
     }
   }
   if (tid == 0) {
