@@ -244,13 +244,48 @@ __device__ __forceinline__ void tile_start(const Tile& t, unsigned char* lds) {
   issue_half(t, o, (S - 2) * BK, ring_slot(lds, S - 2), 0);
 }
 
+// Stage kHookStage of the K loop with a hook: if hook.active() (uniform),
+// every wave waits for all of its vector-memory operations (so stores issued
+// before the loop are complete), and after the barrier `hook()` runs (e.g.
+// thread 0 publishes an earlier tile with one release).
+template <int kWait, typename Hook>
+__device__ __forceinline__ void k_stage_hook(const Tile& t, const Lanes& o, const Frag& f, unsigned char* lds, int ks,
+                                             bf16x8 (&a0)[4], bf16x8 (&b0)[4], bf16x8 (&a1)[4], bf16x8 (&b1)[4],
+                                             f32x16 (&acc)[4][4], Hook& hook) {
+  read_frags(ring_slot(lds, ks), f, 1, a1, b1);
+  issue_half(t, o, (ks + kStages - 2) * BK, ring_slot(lds, ks + kStages - 2), 1);
+  mfma_step(a0, b0, acc);
+  schedule_half<true>();
+  if (hook.active())
+    wait_vmem<0>();
+  else
+    wait_vmem<kWait>();
+  ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  hook();
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(ring_slot(lds, ks + 1), f, 0, a0, b0);
+  issue_half(t, o, (ks + kStages - 1) * BK, ring_slot(lds, ks + kStages - 1), 0);
+  mfma_step(a1, b1, acc);
+  schedule_half<true>();
+}
+
+struct NoHook {
+  __device__ bool active() const { return false; }
+  __device__ void operator()() const {}
+};
+constexpr int kHookStage = 2;
+
 // The K loop of a tile whose first stages tile_start issued; K / BK must be
-// at least kStages. `lds` holds kLdsBytes. Vector-memory operations issued
-// between the two calls (epilogue stores) are allowed: loads complete in
-// order among themselves, so each wait still covers the stage it names, and
-// at worst it also waits for those stores. On return every wave has finished
-// reading LDS and every load has landed.
-__device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4]) {
+// at least kStages + kHookStage. `lds` holds kLdsBytes. Vector-memory
+// operations issued between the two calls (epilogue stores) are allowed:
+// loads complete in order among themselves, so each wait still covers the
+// stage it names, and at worst it also waits for those stores. `hook` runs
+// once, after the barrier of stage kHookStage; when hook.active(), every
+// earlier vector-memory operation of every wave is complete by then. On return every wave has
+// finished reading LDS and every load has landed.
+template <typename Hook>
+__device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4], Hook& hook) {
   constexpr int S = kStages, W = 8 * (S - 3);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -264,12 +299,19 @@ __device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   read_frags(lds, f, 0, a0, b0);
   int ks = 0;
+  for (; ks < kHookStage; ++ks) k_stage<true, true, W>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
+  k_stage_hook<W>(t, o, f, lds, ks++, a0, b0, a1, b1, acc, hook);
   for (; ks < nk - S + 1; ++ks) k_stage<true, true, W>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
   k_stage<true, false, W>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);  // issues the last half (stage nk-1)
   if (S == 5) k_stage<false, false, 8>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
   k_stage<false, false, 0>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
   k_stage<false, false, 0>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
   ring_barrier();
+}
+
+__device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4]) {
+  NoHook none;
+  tile_finish(t, lds, acc, none);
 }
 
 __device__ __forceinline__ void tile_mma(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4]) {

@@ -115,11 +115,24 @@ struct Claims {
   uint32_t ready;  // thread 0's verdict on the candidate
 };
 
-// Starting from candidate ticket t (already claimed; cl.next holds the one
-// after it), wait for a tile's input and issue its first stages. A tile whose
-// wait expires is published as done (so nothing downstream waits forever) and
-// the next ticket is taken. Returns false once the queues are empty.
-__device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl, uint32_t home, uint32_t t,
+// Thread 0's claim pipeline: `ahead` is one more ticket, claimed with an
+// atomic whose result is only needed a whole tile later, so the atomic's
+// round trip (contended by the CUs of an XCD) stays off the critical path.
+struct Claimer {
+  uint32_t ahead;
+  uint32_t home;
+  __device__ uint32_t take(const PipeArgs& a) {  // thread 0
+    const uint32_t t = ahead;
+    ahead = t == kNone ? kNone : claim(a, home);
+    return t;
+  }
+};
+
+// Starting from candidate ticket t (cl.next holds the one after it), wait for
+// a tile's input and issue its first stages. A tile whose wait expires is
+// published as done (so nothing downstream waits forever) and the next ticket
+// is taken. Returns false once the queues are empty.
+__device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl, Claimer& cr, uint32_t t,
                                PipeTile& p, mm::Tile& tile) {
   while (t != kNone) {
     p = decode(a, t);
@@ -133,46 +146,63 @@ __device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl
     if (threadIdx.x == 0) publish(a, p);
     t = cl.next;
     __syncthreads();  // every thread has read next and ready
-    if (threadIdx.x == 0 && t != kNone) cl.next = claim(a, home);
+    if (threadIdx.x == 0 && t != kNone) cl.next = cr.take(a);
   }
   return false;
 }
+
+// Publishes the previous tile from inside the next tile's K loop, once every
+// wave's stores of it are complete.
+struct PublishPrev {
+  const PipeArgs* a;
+  PipeTile p;
+  bool pending;
+  __device__ bool active() const { return pending; }
+  __device__ void operator()() {
+    if (pending && threadIdx.x == 0) publish(*a, p);
+    pending = false;
+  }
+};
 
 // Persistent: one workgroup per CU loops over tiles. The plan puts all
 // tiles of an item in one XCD's queue (items dealt round-robin to the 8
 // queues in GPipe order), so the item's activation rows and weight columns
 // are shared through that XCD's L2. Each queue is in dependency order and a
 // workgroup leaves its own queue only once it is empty, so the earliest
-// unfinished tile is always held or next in line.
+// unfinished tile is always held or next in line. (A tile, not a whole row
+// block, is the unit of work: one GPipe tick holds at most S items, and only
+// at tile granularity do they outnumber the workgroups.)
 //
-// The epilogue of a tile overlaps the operand loads of the next: once the K
-// loop of tile t ends, the first stages of tile t+1 are issued if its input
-// row block is already complete (one non-blocking check), then tile t is
-// stored and published, and only then, if the check failed, does the
-// workgroup wait for t+1's input. Tile t+1 may depend on tile t itself, so
-// the blocking wait never comes before t is published.
+// Tile t's epilogue overlaps both neighbours: once its K loop ends, the first
+// stages of tile t+1 are issued if t+1's input row block is already complete
+// (one non-blocking check), then t is stored, and t+1's K loop publishes t a
+// few stages in (its stores long complete by then). If the check failed, t is
+// published first and only then does the workgroup wait for t+1's input: t+1
+// may depend on t itself.
 __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ Claims cl;
   const uint32_t tid = threadIdx.x;
   const uint64_t item_elems = (uint64_t)a.rows * a.d;
-  uint32_t home = 0;
+  Claimer cr{kNone, 0};
   if (tid == 0) {
-    home = xcc_id() % a.nq;
-    cl.next = claim(a, home);
+    cr.home = xcc_id() % a.nq;
+    cr.ahead = claim(a, cr.home);
+    cl.next = cr.take(a);
   }
   __syncthreads();
   const uint32_t first = cl.next;
   __syncthreads();
-  if (tid == 0 && first != kNone) cl.next = claim(a, home);
+  if (tid == 0 && first != kNone) cl.next = cr.take(a);
   PipeTile p;
   mm::Tile tile;
-  bool have = start_blocking(a, lds, cl, home, first, p, tile);
+  PublishPrev prev{&a, {0, 0, 0, 0}, false};
+  bool have = start_blocking(a, lds, cl, cr, first, p, tile);
   while (have) {
     mm::f32x16 acc[4][4];
-    mm::tile_finish(tile, lds, acc);  // ends with a barrier: cl.next is visible
+    mm::tile_finish(tile, lds, acc, prev);  // may publish the previous tile; ends with a barrier
     const uint32_t t2 = cl.next;
-    PipeTile p2{0, 0, 0, 0};
+    PipeTile p2 = p;
     mm::Tile tile2 = tile;
     if (t2 != kNone) {
       p2 = decode(a, t2);
@@ -181,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
     __syncthreads();  // every thread has read next
     if (tid == 0) {
       cl.ready = t2 != kNone && input_ready(a, p2, false);
-      if (t2 != kNone) cl.next = claim(a, home);
+      if (t2 != kNone) cl.next = cr.take(a);
     }
     __syncthreads();
     const bool started = cl.ready;
@@ -189,15 +219,22 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
     __bf16* out = a.acts + ((uint64_t)p.s * a.M + p.m) * item_elems + (uint64_t)p.r * mm::BM * a.d +
                   (uint64_t)p.c * mm::BN;
     mm::store_tile<true>(acc, out, a.d, tile.rows);
-    mm::wait_stores();
-    __syncthreads();  // every wave's stores complete; every thread has read ready
-    if (tid == 0) publish(a, p);
+    prev.p = p;
+    prev.pending = true;
     if (started) {
       p = p2;
       tile = tile2;
-    } else {
-      have = start_blocking(a, lds, cl, home, t2, p, tile);
+    } else {  // publish now: the wait below may be for this very tile
+      mm::wait_stores();
+      __syncthreads();  // every wave's stores complete; every thread has read ready
+      prev();
+      have = start_blocking(a, lds, cl, cr, t2, p, tile);
     }
+  }
+  if (prev.pending) {  // uniform
+    mm::wait_stores();
+    __syncthreads();
+    prev();
   }
   if (tid == 0) {
     const uint32_t dn = __hip_atomic_fetch_add(a.done_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
