@@ -12,6 +12,12 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+# torch first: libpw.so links libamdhip64.so.7, and torch ships its own copy
+# of that runtime under the same soname. Loaded after torch, our dependency
+# resolves to torch's copy; loaded before, the process would end up with two
+# HIP runtimes, and ours would find no device once torch's had claimed it.
+import torch  # noqa: F401  (load order only)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpw.so")
 

@@ -11,12 +11,14 @@
 //
 //   hist    one workgroup per tile of `tile` consecutive tuples counts its
 //           destinations (wave64 ballot matching, LDS counters) and writes
-//           the column tile_base[d][tile];
-//   scan    one workgroup per destination scans its column over tiles
-//           (where this tile's run of d starts inside segment d); the last
-//           workgroup to finish scans the totals into segment offsets, sets
-//           the expected count of every destination and fires the futures of
-//           destinations that receive nothing;
+//           the row tile_base[tile][*];
+//   scan    one workgroup per block of scan_tiles tiles runs, per
+//           destination, down its rows (where each tile's run of d starts
+//           inside the block) and writes the block totals; the last
+//           workgroup to finish scans those over the blocks and the
+//           destination totals into segment offsets, sets the expected count
+//           of every destination and fires the futures of destinations that
+//           receive nothing;
 //   scatter one workgroup per tile re-ranks its tuples (stable: wave by wave,
 //           in source order), applies A and writes each payload row with
 //           16-byte vector stores straight into its destination segment,
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(kBlock) void k_hist(ExchangeArgs a) {
   if (bad) latch(a.f.status, ST_BAD_DEST);
   __syncthreads();
   for (uint32_t d = threadIdx.x; d < a.N; d += kBlock)
-    a.tile_base[(uint64_t)d * a.num_tiles + blockIdx.x] = cnt[d];
+    a.tile_base[(uint64_t)blockIdx.x * a.N + d] = cnt[d];
 }
 
 // ------------------------------------------------- per-source counts export
@@ -113,31 +115,49 @@ __global__ __launch_bounds__(kBlock) void k_src_counts(ExchangeArgs a) {
 }
 
 // --------------------------------------------------------------------- scan
+// Exclusive running sum, in place, of the column d of rows [r0, r1) of a
+// row-major [rows][N] table; returns the column total. The loads of 8 rows
+// are issued before any is needed.
+__device__ __forceinline__ uint32_t column_scan(uint32_t* t, uint32_t N, uint32_t d, uint32_t r0, uint32_t r1) {
+  uint32_t run = 0;
+  uint32_t r = r0;
+  for (; r + 8 <= r1; r += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (uint32_t u = 0; u < 8; ++u) v[u] = t[(uint64_t)(r + u) * N + d];
+#pragma unroll
+    for (uint32_t u = 0; u < 8; ++u) {
+      t[(uint64_t)(r + u) * N + d] = run;
+      run += v[u];
+    }
+  }
+  for (; r < r1; ++r) {
+    const uint32_t v = t[(uint64_t)r * N + d];
+    t[(uint64_t)r * N + d] = run;
+    run += v;
+  }
+  return run;
+}
+
 __global__ __launch_bounds__(kBlock) void k_scan(ExchangeArgs a) {
   __shared__ uint32_t wsum[kWaves];
   __shared__ uint32_t is_last;
   __shared__ uint32_t zero_count[kWaves];
   {
-    const uint32_t d = blockIdx.x;
-    uint32_t* col = a.tile_base + (uint64_t)d * a.num_tiles;
-    uint32_t run = 0;
-    for (uint32_t base = 0; base < a.num_tiles; base += kBlock) {
-      const uint32_t i = base + threadIdx.x;
-      const uint32_t v = i < a.num_tiles ? col[i] : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_exclusive_scan(v, wsum, tot);
-      if (i < a.num_tiles) col[i] = run + ex;
-      run += tot;
-    }
-    if (threadIdx.x == 0) a.expected[d] = run;
+    const uint32_t t0 = blockIdx.x * a.scan_tiles, t1 = min(a.num_tiles, t0 + a.scan_tiles);
+    for (uint32_t d = threadIdx.x; d < a.N; d += kBlock)
+      a.blk_base[(uint64_t)blockIdx.x * a.N + d] = column_scan(a.tile_base, a.N, d, t0, t1);
   }
-  // The last workgroup to finish turns the totals into segment offsets.
+  // The last workgroup to finish scans the block totals and turns the
+  // destination totals into segment offsets.
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) is_last = atomicAdd(&a.ctl[1], 1u) == gridDim.x - 1;
   __syncthreads();
   if (!is_last) return;
   __threadfence();
+  for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) a.expected[d] = column_scan(a.blk_base, a.N, d, 0, a.num_blk);
+  __syncthreads();
 
   const uint32_t N = a.N;
   const uint32_t per = (N + kBlock - 1) / kBlock;
@@ -276,7 +296,8 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
   // 2. first slot of each (wave, destination): segment start + this tile's
   //    start inside the segment + the counts of earlier waves
   for (uint32_t d = threadIdx.x; d < N; d += kBlock) {
-    const uint32_t base = (uint32_t)a.seg[d] + a.tile_base[(uint64_t)d * a.num_tiles + blockIdx.x];
+    const uint32_t base = (uint32_t)a.seg[d] + a.blk_base[(uint64_t)(blockIdx.x / a.scan_tiles) * N + d] +
+                          a.tile_base[(uint64_t)blockIdx.x * N + d];
     uint32_t run = base;
 #pragma unroll
     for (uint32_t ww = 0; ww < kWaves; ++ww) {
@@ -434,7 +455,7 @@ hipError_t launch_src_counts(const ExchangeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_scan, dim3(a.N), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(k_scan, dim3(a.num_blk), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

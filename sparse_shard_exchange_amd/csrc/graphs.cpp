@@ -199,6 +199,8 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done)
   a.fanout = 2;
   a.tile = L.tile;
   a.num_tiles = L.num_tiles;
+  a.scan_tiles = L.scan_tiles;
+  a.num_blk = L.num_blk;
   a.nbits = 0;
   while ((1u << a.nbits) < E) ++a.nbits;
   a.is_f32 = 0;
@@ -212,6 +214,7 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done)
   a.b_arrived = reinterpret_cast<uint32_t*>(base + L.b_arrived);
   a.ctl = m.ctl;
   a.tile_base = reinterpret_cast<uint32_t*>(base + L.tile_base);
+  a.blk_base = reinterpret_cast<uint32_t*>(base + L.blk_base);
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
 
   hipError_t e = hipSuccess;

@@ -104,6 +104,8 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
       L.G = (uint64_t)S * d.tuples_per_shard * fan;
       L.tile = pick_tile(L.G);
       L.num_tiles = (uint32_t)std::max<uint64_t>(1, (L.G + L.tile - 1) / L.tile);
+      L.scan_tiles = std::max<uint32_t>(16, (L.num_tiles + 255) / 256);  // at most 256 scan blocks
+      L.num_blk = (L.num_tiles + L.scan_tiles - 1) / L.scan_tiles;
       L.width = std::max<uint32_t>(std::max(N, S), 1);
       L.fut = c.take((size_t)kNodes * L.width * 4);
       L.fires = c.take((size_t)kNodes * L.width * 4);
@@ -113,6 +115,7 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
       L.b_arrived = c.take((size_t)N * 4);
       L.seg = c.take((size_t)(N + 1) * 8);
       L.tile_base = c.take((size_t)N * L.num_tiles * 4);
+      L.blk_base = c.take((size_t)N * L.num_blk * 4);
       if (d.kind == PW_GRAPH_MOE) {
         const uint64_t tokens = (uint64_t)S * d.tuples_per_shard;
         L.experts = c.take(tokens * d.top_k * 4);
@@ -365,6 +368,8 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   a.fanout = 1;
   a.tile = L.tile;
   a.num_tiles = L.num_tiles;
+  a.scan_tiles = L.scan_tiles;
+  a.num_blk = L.num_blk;
   a.nbits = ceil_log2(N);
   a.is_f32 = d.dtype == PW_F32;
   a.a_kind = d.a_op.kind; a.a_a = d.a_op.a; a.a_b = d.a_op.b;
@@ -377,6 +382,7 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   a.b_arrived = reinterpret_cast<uint32_t*>(base + L.b_arrived);
   a.ctl = reinterpret_cast<uint32_t*>(base + L.ctl + 64);
   a.tile_base = reinterpret_cast<uint32_t*>(base + L.tile_base);
+  a.blk_base = reinterpret_cast<uint32_t*>(base + L.blk_base);
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
 
   hipError_t e = hipSuccess;

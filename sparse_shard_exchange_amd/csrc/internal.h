@@ -43,6 +43,7 @@ struct ExchangeArgs {
   uint32_t fanout;            // payload row of tuple g is g / fanout
   uint32_t tile;              // tuples per workgroup tile (multiple of 256)
   uint32_t num_tiles;
+  uint32_t scan_tiles, num_blk;  // tiles per scan block; scan blocks
   uint32_t nbits;             // bits needed to tell destinations apart
   uint32_t is_f32;
   uint32_t a_kind; float a_a, a_b;
@@ -54,7 +55,8 @@ struct ExchangeArgs {
   uint32_t* expected;         // [N]
   uint32_t* b_arrived;        // [N]
   uint32_t* ctl;              // [0] result count, [1] scan done count
-  uint32_t* tile_base;        // [N][num_tiles]
+  uint32_t* tile_base;        // [num_tiles][N]: counts, then run starts inside the scan block
+  uint32_t* blk_base;         // [num_blk][N]: block totals, then run starts inside the segment
   int64_t* seg;               // [N+1]
 };
 

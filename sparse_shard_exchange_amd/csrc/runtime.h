@@ -22,7 +22,8 @@ struct Layout {
   size_t stamps = 0;      // [kNodes][width] u64 (PW_FLAG_TRACE)
   size_t arrived = 0, expected = 0, b_arrived = 0;  // [N] u32
   size_t seg = 0;         // [N+1] i64 segment offsets
-  size_t tile_base = 0;   // [N][num_tiles] u32
+  size_t tile_base = 0;   // [num_tiles][N] u32
+  size_t blk_base = 0;    // [num_blk][N] u32
   size_t experts = 0, gates = 0, slot_of = 0, hidden_act = 0;  // MOE
   size_t rb_start = 0, b_done = 0;                              // MOE
   size_t w1t = 0, w2t = 0, wrt = 0;  // packed (K-contiguous) weights: MOE W1^T, W2^T, W_r^T; PIPELINE W^T in w1t
@@ -32,6 +33,7 @@ struct Layout {
   size_t total = 0;
   uint64_t G = 0;         // tuples per exchange
   uint32_t tile = 0, num_tiles = 0, width = 0;
+  uint32_t scan_tiles = 0, num_blk = 0;  // tiles per scan block, scan blocks
 };
 
 struct Plan {
