@@ -10,8 +10,7 @@
 // counting sort by destination done in three launches:
 //
 //   hist    one workgroup per tile of `tile` consecutive tuples counts its
-//           destinations (wave64 ballot matching, LDS counters) and writes
-//           the row tile_base[tile][*];
+//           destinations (LDS atomics) and writes the row tile_base[tile][*];
 //   scan    one workgroup per block of scan_tiles tiles runs, per
 //           destination, down its rows (where each tile's run of d starts
 //           inside the block) and writes the block totals; the last
@@ -75,6 +74,23 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
 }
 
 // ---------------------------------------------------------------- histogram
+// A wave's destinations, loaded before any is used (up to kMaxChunks chunks
+// of 64 tuples: tile <= 4096 split over 4 waves), so that the loads of its
+// whole sub-tile are in flight together.
+constexpr uint32_t kMaxChunks = 16;
+
+struct WaveDests {
+  int d[kMaxChunks];
+};
+
+__device__ __forceinline__ WaveDests load_wave_dests(const ExchangeArgs& a, uint64_t g0, uint32_t sub, uint32_t lane,
+                                                     bool& bad) {
+  WaveDests w;
+#pragma unroll
+  for (uint32_t i = 0; i < kMaxChunks; ++i) w.d[i] = i * 64 < sub ? load_dest(a, g0 + i * 64 + lane, bad) : -1;
+  return w;
+}
+
 __global__ __launch_bounds__(kBlock) void k_hist(ExchangeArgs a) {
   extern __shared__ uint32_t lds[];
   uint32_t* cnt = lds;  // [N]
@@ -84,15 +100,15 @@ __global__ __launch_bounds__(kBlock) void k_hist(ExchangeArgs a) {
   const uint32_t sub = a.tile / kWaves;
   const uint64_t g0 = (uint64_t)blockIdx.x * a.tile + (uint64_t)w * sub;
   bool bad = false;
-  for (uint32_t c = 0; c < sub && g0 + c < a.G; c += 64) {
-    const int d = load_dest(a, g0 + c + lane, bad);
-    const uint64_t peers = match_peers(d, d >= 0, a.nbits);
-    if (d >= 0 && (peers & lanemask_lt(lane)) == 0) atomicAdd(&cnt[d], (uint32_t)__popcll(peers));
-  }
+  const WaveDests wd = load_wave_dests(a, g0, sub, lane, bad);
+  // counts need no order: one LDS atomic per tuple (the LDS serializes
+  // lanes that hit one counter, which is cheaper than matching them)
+#pragma unroll
+  for (uint32_t i = 0; i < kMaxChunks; ++i)
+    if (wd.d[i] >= 0) atomicAdd(&cnt[wd.d[i]], 1u);
   if (bad) latch(a.f.status, ST_BAD_DEST);
   __syncthreads();
-  for (uint32_t d = threadIdx.x; d < a.N; d += kBlock)
-    a.tile_base[(uint64_t)blockIdx.x * a.N + d] = cnt[d];
+  for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) a.tile_base[(uint64_t)blockIdx.x * a.N + d] = cnt[d];
 }
 
 // ------------------------------------------------- per-source counts export
@@ -116,25 +132,20 @@ __global__ __launch_bounds__(kBlock) void k_src_counts(ExchangeArgs a) {
 
 // --------------------------------------------------------------------- scan
 // Exclusive running sum, in place, of the column d of rows [r0, r1) of a
-// row-major [rows][N] table; returns the column total. The loads of 8 rows
+// row-major [rows][N] table; returns the column total. The loads of 16 rows
 // are issued before any is needed.
 __device__ __forceinline__ uint32_t column_scan(uint32_t* t, uint32_t N, uint32_t d, uint32_t r0, uint32_t r1) {
+  constexpr uint32_t kB = 16;
   uint32_t run = 0;
-  uint32_t r = r0;
-  for (; r + 8 <= r1; r += 8) {
-    uint32_t v[8];
+  for (uint32_t r = r0; r < r1; r += kB) {
+    uint32_t v[kB];
 #pragma unroll
-    for (uint32_t u = 0; u < 8; ++u) v[u] = t[(uint64_t)(r + u) * N + d];
+    for (uint32_t u = 0; u < kB; ++u) v[u] = r + u < r1 ? t[(uint64_t)(r + u) * N + d] : 0u;
 #pragma unroll
-    for (uint32_t u = 0; u < 8; ++u) {
-      t[(uint64_t)(r + u) * N + d] = run;
+    for (uint32_t u = 0; u < kB; ++u) {
+      if (r + u < r1) t[(uint64_t)(r + u) * N + d] = run;
       run += v[u];
     }
-  }
-  for (; r < r1; ++r) {
-    const uint32_t v = t[(uint64_t)r * N + d];
-    t[(uint64_t)r * N + d] = run;
-    run += v;
   }
   return run;
 }
@@ -286,10 +297,11 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
   bool bad = false;
 
   // 1. per-wave counts of this wave's contiguous sub-tile
-  for (uint32_t c = 0; c < sub && g0 + c < a.G; c += 64) {
-    const int d = load_dest(a, g0 + c + lane, bad);
-    const uint64_t peers = match_peers(d, d >= 0, a.nbits);
-    if (d >= 0 && (peers & lanemask_lt(lane)) == 0) mine[d] += (uint32_t)__popcll(peers);
+  {
+    const WaveDests wd = load_wave_dests(a, g0, sub, lane, bad);
+#pragma unroll
+    for (uint32_t i = 0; i < kMaxChunks; ++i)
+      if (wd.d[i] >= 0) atomicAdd(&mine[wd.d[i]], 1u);
   }
   __syncthreads();
 
