@@ -135,6 +135,27 @@ __device__ __forceinline__ uint32_t expert_of(const uint32_t* rb_start, uint32_t
   return lo;
 }
 
+// Workgroups -> tiles. The hardware deals consecutive workgroups to the 8
+// XCDs in turn, so workgroup b runs on XCD b % 8 and each XCD holds about 32
+// at a time (one per CU). An XCD's run of 32 workgroups covers an R x C patch
+// of tiles (R row blocks x C column tiles, R C = 32) whose R activation panels
+// and C weight panels are fetched from HBM once and shared through the XCD's
+// L2; an XCD's successive patches walk the column groups of one row group
+// before the next. (Placement only: the map is one-to-one whatever the
+// dispatch order.)
+constexpr uint32_t kXcds = 8, kPatch = 32;
+
+__device__ __forceinline__ uint32_t patch_cols(uint32_t CT) {
+  return CT % 8 == 0 ? 8 : CT % 4 == 0 ? 4 : CT % 2 == 0 ? 2 : 1;
+}
+
+__device__ __forceinline__ void tile_at(uint32_t b, uint32_t CT, uint32_t& rbg, uint32_t& c) {
+  const uint32_t C = patch_cols(CT), R = kPatch / C, groups = CT / C;
+  const uint32_t x = b % kXcds, s = b / kXcds, p = s % kPatch, k = s / kPatch;
+  rbg = ((k / groups) * kXcds + x) * R + p / C;
+  c = (k % groups) * C + p % C;
+}
+
 // One 256 x 256 tile of an expert FFN GEMM: rows of expert e's segment.
 // kSecond: input H, weights W2 [E][hidden][d], output Y (no activation);
 // otherwise input dispatched rows, W1 [E][d][hidden], output H through GELU.
@@ -143,7 +164,8 @@ __global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ uint32_t go;
   const uint32_t CT = (kSecond ? a.d : a.hidden) / mm::BN;
-  const uint32_t rbg = blockIdx.x / CT, c = blockIdx.x - rbg * CT;
+  uint32_t rbg, c;
+  tile_at(blockIdx.x, CT, rbg, c);
   const uint32_t total_rb = a.rb_start[a.E];
   if (rbg >= total_rb) return;  // grid is sized for the worst case
   const uint32_t e = expert_of(a.rb_start, a.E, rbg);
@@ -227,8 +249,11 @@ hipError_t launch_moe_prefix(const MoeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_ffn(const MoeArgs& a, bool second, hipStream_t s) {
+  // enough whole patch rounds to cover max_row_blocks row blocks (see tile_at)
   const uint32_t CT = (second ? a.d : a.hidden) / mm::BN;
-  const uint64_t blocks = (uint64_t)a.max_row_blocks * CT;
+  const uint32_t C = CT % 8 == 0 ? 8 : CT % 4 == 0 ? 4 : CT % 2 == 0 ? 2 : 1, R = kPatch / C;
+  const uint64_t row_groups = ((uint64_t)a.max_row_blocks + R - 1) / R;
+  const uint64_t blocks = (row_groups + kXcds - 1) / kXcds * kXcds * R * CT;
   if (second) {
     hipError_t e = hipFuncSetAttribute((const void*)k_ffn<true>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsTotal);
     if (e != hipSuccess) return e;
