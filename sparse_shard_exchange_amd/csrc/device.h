@@ -72,11 +72,14 @@ __device__ __forceinline__ bool await(const Futures& f, uint32_t node, uint32_t 
 
 // Wait on a future fired by an EARLIER launch on the same stream: the kernel
 // boundary already orders the producer's writes before this launch, so the
-// check is a relaxed read (an agent-scope acquire would invalidate the L2 of
-// this XCD on every call). Same bound and latch as await().
+// first check is an ordinary cacheable load (agent-scope loads of the few
+// hot future words, one or two per token in the MoE combine, would all go to
+// memory); only if that finds the epoch missing (the producer failed) does
+// the bounded spin with relaxed agent-scope loads follow. Same bound and
+// latch as await().
 __device__ __forceinline__ bool await_prior(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
   const uint32_t* p = &f.epoch[node * f.width + shard];
-  if (epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
+  if (epoch_reached(*p, epoch)) return true;
   const uint64_t t0 = wall_clock64();
   while (true) {
     __builtin_amdgcn_s_sleep(1);

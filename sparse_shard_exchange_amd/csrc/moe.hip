@@ -200,27 +200,43 @@ __global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a) {
 }
 
 // out[t] = bf16(g0 * Y[slot(2t)] + g1 * Y[slot(2t + 1)]), fp32 sum with the
-// top-1 term first; one wave per token, 16-byte chunks.
+// top-1 term first; one wave per token at a time, 16-byte chunks. The grid is
+// bounded (grid-stride over tokens): every workgroup adds once to the done
+// counter, and adds to one address serialize at the memory side (one per
+// 4-token workgroup cost ~0.3 ms at 131072 tokens).
+constexpr uint32_t kCombineBlocks = 2048;
+
 __global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  bool ok = true;
-  if (t < a.tokens) {
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < a.tokens; t += (int64_t)gridDim.x * 4) {
     const int e0 = a.experts[t * 2], e1 = a.experts[t * 2 + 1];
+    bool ok = true;
     if (lane == 0) ok = await_prior(a.f, NODE_B, e0, a.epoch) && await_prior(a.f, NODE_B, e1, a.epoch);
     ok = __shfl((int)ok, 0, 64) != 0;
-    if (ok) {
-      const float g0 = a.gates[t * 2], g1 = a.gates[t * 2 + 1];
-      const bf16x8* y0 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)a.slot_of[t * 2] * a.d);
-      const bf16x8* y1 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)a.slot_of[t * 2 + 1] * a.d);
-      bf16x8* o = reinterpret_cast<bf16x8*>(a.out + t * a.d);
-      for (uint32_t ch = lane; ch < a.d / 8; ch += 64) {
-        const bf16x8 u = y0[ch], v = y1[ch];
-        bf16x8 r;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = (__bf16)fmaf(g1, (float)v[j], g0 * (float)u[j]);
-        o[ch] = r;
+    if (!ok) continue;  // uniform per wave
+    const float g0 = a.gates[t * 2], g1 = a.gates[t * 2 + 1];
+    const bf16x8* y0 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)a.slot_of[t * 2] * a.d);
+    const bf16x8* y1 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)a.slot_of[t * 2 + 1] * a.d);
+    bf16x8* o = reinterpret_cast<bf16x8*>(a.out + t * a.d);
+    // two chunks of each row per lane per pass: all four loads in flight
+    // before the first is used (d = 1024 is exactly one pass)
+    const uint32_t nch = a.d / 8;
+    for (uint32_t ch = lane; ch < nch; ch += 128) {
+      const bool two = ch + 64 < nch;
+      const bf16x8 u0 = y0[ch], v0 = y1[ch];
+      bf16x8 u1 = {}, v1 = {};
+      if (two) {
+        u1 = y0[ch + 64];
+        v1 = y1[ch + 64];
       }
+      bf16x8 r0, r1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        r0[j] = (__bf16)fmaf(g1, (float)v0[j], g0 * (float)u0[j]);
+        r1[j] = (__bf16)fmaf(g1, (float)v1[j], g0 * (float)u1[j]);
+      }
+      o[ch] = r0;
+      if (two) o[ch + 64] = r1;
     }
   }
   __syncthreads();
@@ -267,7 +283,7 @@ hipError_t launch_ffn(const MoeArgs& a, bool second, hipStream_t s) {
 }
 
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
-  const uint64_t blocks = (a.tokens + 3) / 4;
+  const uint64_t blocks = std::min<uint64_t>((a.tokens + 3) / 4, kCombineBlocks);
   hipLaunchKernelGGL(k_combine, dim3((uint32_t)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
