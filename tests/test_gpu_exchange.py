@@ -72,6 +72,8 @@ CASES = [
     (64, 300, 64, "reversed"),
     (2048, 50, 4, "uniform"),
     (2048, 33, 4, "zipf4"),
+    (8192, 3, 4, "uniform"),      # the most shards a plan takes: the scatter's LDS is then exactly 160 KiB
+    (8192, 2, 64, "half_empty"),
 ]
 
 

@@ -55,7 +55,8 @@ def run(pw, s, m, rows, d, flags=0):
     return inp, pipe, acts, f
 
 
-@pytest.mark.parametrize("s,m,rows,d", [(1, 1, 256, 256), (3, 4, 300, 256), (2, 3, 512, 512), (4, 2, 100, 768)])
+@pytest.mark.parametrize("s,m,rows,d", [(1, 1, 256, 256), (3, 4, 300, 256), (2, 3, 512, 512), (4, 2, 100, 768),
+                                        (2, 2, 1, 256), (2, 2, 257, 1024)])
 def test_pipeline_small_all_outputs(gpu, s, m, rows, d):
     pw = gpu
     print(f"pipeline S={s} M={m} rows={rows} d={d}", flush=True)
