@@ -321,19 +321,23 @@ __device__ __forceinline__ void tile_mma(const Tile& t, unsigned char* lds, f32x
 
 // GELU(z) = z Phi(z) with Phi from erfc by Abramowitz & Stegun formula
 // 7.1.26 (erfc(x) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
-// t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7): Phi(z) = erfc(|z| / sqrt 2) / 2
-// for z < 0 and 1 - erfc(z / sqrt 2) / 2 otherwise, so negative inputs keep
-// their relative accuracy.
+// t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7), evaluated at x = |z| / sqrt 2
+// so that negative inputs keep their relative accuracy. With
+// h = erfc(|z| / sqrt 2) / 2, z Phi(z) is z (1 - h) for z >= 0 and z h for
+// z < 0, i.e. max(z, 0) - |z| h in both cases: no select. The 1/2 is folded
+// into the coefficients, 1/sqrt 2 into p, and exp(-x^2) = 2^(-z^2 log2(e) / 2).
+// About 12 VALU instructions (fmaxf adds a canonicalising max) and 2
+// transcendental ones per element.
 __device__ __forceinline__ float gelu(float z) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  const float half_erfc = 0.5f * poly * t * __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);
-  const float phi = z < 0.0f ? half_erfc : 1.0f - half_erfc;
-  return z * phi;
+  const float a = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, a, 1.0f));
+  float poly = fmaf(1.061405429f * 0.5f, t, -1.453152027f * 0.5f);
+  poly = fmaf(poly, t, 1.421413741f * 0.5f);
+  poly = fmaf(poly, t, -0.284496736f * 0.5f);
+  poly = fmaf(poly, t, 0.254829592f * 0.5f);
+  const float e = __builtin_amdgcn_exp2f(z * (z * (-0.5f * 1.4426950408889634f)));
+  const float h = poly * t * e;
+  return fmaf(-a, h, fmaxf(z, 0.0f));
 }
 
 constexpr int kLdsTotal = kLdsBytes;  // the epilogue needs no LDS
