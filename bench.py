@@ -161,6 +161,46 @@ def moe_bench(pw, torch, pw_inputs, steps=3):
             "expert_flop": flops}
 
 
+def reference_bench(torch, iters=10):
+    """Context, not the product path: the vendor BLAS (hipBLASLt through
+    torch.matmul) on the shapes of the two GEMM rows, and torch's elementwise
+    copy, on the same device. Inputs random bf16 like the workloads."""
+    def gemm(batch, m, k, n, gelu):
+        a = torch.randn(batch, m, k, device="cuda").to(torch.bfloat16)
+        b = (torch.randn(batch, k, n, device="cuda") * 0.02).to(torch.bfloat16)
+        f = (lambda: torch.nn.functional.gelu(torch.matmul(a, b))) if gelu else (lambda: torch.matmul(a, b))
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        return {"shape": f"{batch} x [{m}x{k}] @ [{k}x{n}]" + (" then GELU" if gelu else ""), "ms": ms,
+                "tflops": 2.0 * batch * m * n * k / (ms * 1e-3) / 1e12}
+    out = {"note": "vendor BLAS via torch on the same device, for context only",
+           "pipeline_stage_gemm_gelu": gemm(64, 2048, 1024, 1024, True),
+           "pipeline_stage_gemm": gemm(64, 2048, 1024, 1024, False),
+           "ffn2_like_gemm": gemm(64, 4096, 4096, 1024, False)}
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        torch.neg(x, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    out["copy_gbs"] = 2.0 * x.numel() * 4 / (ms * 1e-3) / 1e9
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +211,7 @@ def main():
     ap.add_argument("--no-pipeline", action="store_true", help="skip the pipeline measurement")
     ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts measurement")
     ap.add_argument("--chain-steps", type=int, default=10000)
+    ap.add_argument("--no-reference", action="store_true", help="skip the vendor-BLAS and copy reference timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 plain elementwise copies of 1 GiB (torch.neg) to scale HBM counters")
     args = ap.parse_args()
@@ -206,10 +247,13 @@ def main():
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     e0.record(stream)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         f = ex.step(x, dest)
+        marks[i + 1].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -217,6 +261,8 @@ def main():
     ms_events = e0.elapsed_time(e1) / args.steps
     ms_wall = (t1 - t0) * 1e3 / args.steps
     ms = max(ms_events, ms_wall)
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    pct = lambda q: per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
     kt = ex.plan.kernel_times()
     per_kernel = {k: v[1] / max(v[0], 1) for k, v in kt.items()}
     scat_ms = per_kernel["scatter"]
@@ -244,6 +290,7 @@ def main():
             "hottest_destination_share": float(counts.max() / g),
             "empty_destinations": int((counts == 0).sum()),
         },
+        "ms_per_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "step_gbs_algorithmic": BYTES_PER_TUPLE * g / (ms * 1e-3) / 1e9,
         "step_frac_hbm_peak": BYTES_PER_TUPLE * g / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernel_ms": per_kernel,
@@ -269,6 +316,10 @@ def main():
     if not args.no_chain:
         log("chain sweep")
         result["chain"] = chain_sweep(pw, torch, pw_inputs, args.chain_steps)
+
+    if not args.no_reference:
+        log("reference (vendor BLAS, copy)")
+        result["reference"] = reference_bench(torch)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
