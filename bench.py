@@ -201,6 +201,52 @@ def reference_bench(torch, iters=10):
     return out
 
 
+def cpu_other_rows(pw_inputs, pipeline=True, moe=True):
+    """The oracle on bounded samples of the other rows, scaled to the full
+    workload (reported beside the GPU numbers, never a target)."""
+    import numpy as np
+    from oracle import chain as oc
+    out = {}
+    x0 = pw_inputs.chain_state(2048, 128)
+    steps = 1000
+    t0 = time.perf_counter()
+    oc.chain(x0, steps)
+    dt = time.perf_counter() - t0
+    out["chain"] = {"value": steps / dt, "unit": "steps/s", "cores": 1,
+                    "sample": f"N=2048 shards x 128 fp32, {steps} of the 10,000 steps (oracle.chain.chain, NumPy)"}
+    if pipeline:
+        from oracle import pipeline as op
+        inp = pw_inputs.pipeline(16, 1, 2048, 1024)
+        x = inp.x[0].float().numpy()
+        w = inp.w.float().numpy()
+        t0 = time.perf_counter()
+        op.forward(x, w)
+        dt = time.perf_counter() - t0
+        out["pipeline"] = {"value": dt * 64 * 1e3, "unit": "ms per pass (estimated)", "cores": _blas_threads(),
+                           "sample": f"1 of 64 microbatches through all 16 stages (oracle.pipeline.forward, NumPy fp64 GEMMs) "
+                                     f"in {dt:.2f} s, times 64"}
+    if moe:
+        from oracle import moe as om
+        tokens = 2048
+        inp = pw_inputs.moe(tokens, 1024, 64, 4096)
+        t0 = time.perf_counter()
+        om.moe_step(inp.x.float().numpy(), inp.w_router.float().numpy(), inp.w1.float().numpy(),
+                    inp.w2.float().numpy())
+        dt = time.perf_counter() - t0
+        out["moe"] = {"value": dt * (131072 / tokens) * 1e3, "unit": "ms per step (estimated)", "cores": _blas_threads(),
+                      "sample": f"{tokens} of 131072 tokens through oracle.moe.moe_step (NumPy fp64 GEMMs) in {dt:.2f} s, "
+                                f"scaled by token count"}
+    return out
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +258,8 @@ def main():
     ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts measurement")
     ap.add_argument("--chain-steps", type=int, default=10000)
     ap.add_argument("--no-reference", action="store_true", help="skip the vendor-BLAS and copy reference timings")
+    ap.add_argument("--no-cpu-extra", action="store_true", help="skip the oracle samples of the chain and pipeline rows")
+    ap.add_argument("--cpu-moe", action="store_true", help="also time the oracle on a 2048-token MoE sample (~45 s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 plain elementwise copies of 1 GiB (torch.neg) to scale HBM counters")
     args = ap.parse_args()
@@ -346,6 +394,9 @@ def main():
                       f"median of 3 runs {dt:.2f} s, single-threaded NumPy",
             **cpu_info(),
         }
+        if not args.no_cpu_extra:
+            log("cpu baseline, other rows (oracle samples)")
+            result["cpu_baseline_other_rows"] = cpu_other_rows(pw_inputs, not args.no_pipeline, args.cpu_moe)
     print(json.dumps(result), flush=True)
 
 
