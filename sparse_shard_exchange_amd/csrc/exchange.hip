@@ -117,14 +117,11 @@ __global__ __launch_bounds__(kBlock) void k_src_counts(ExchangeArgs a) {
   uint32_t* cnt = lds;  // [N]
   for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) cnt[d] = 0;
   __syncthreads();
-  const uint32_t lane = threadIdx.x & 63;
   const uint64_t beg = (uint64_t)blockIdx.x * a.T, end = beg + a.T;
   bool bad = false;
-  for (uint64_t base = beg + (threadIdx.x & ~63u); base < end; base += kBlock) {
-    const uint64_t g = base + lane;
-    const int d = g < end ? load_dest(a, g, bad) : -1;
-    const uint64_t peers = match_peers(d, d >= 0, a.nbits);
-    if (d >= 0 && (peers & lanemask_lt(lane)) == 0) atomicAdd(&cnt[d], (uint32_t)__popcll(peers));
+  for (uint64_t g = beg + threadIdx.x; g < end; g += kBlock) {
+    const int d = load_dest(a, g, bad);
+    if (d >= 0) atomicAdd(&cnt[d], 1u);  // counts need no order
   }
   __syncthreads();
   for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) a.counts[(uint64_t)blockIdx.x * a.N + d] = cnt[d];

@@ -40,13 +40,11 @@ namespace mm {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-#ifndef PW_MM_STAGES
-#define PW_MM_STAGES 4
-#endif
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256, kStages = PW_MM_STAGES;
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
+constexpr int kStages = 4;                      // (5 stages, the whole LDS, measured slower)
 constexpr int kHalf = BM * BK * 2;              // one operand block of a stage: 16 KiB
 constexpr int kStageBytes = 2 * kHalf;          // 32 KiB
-constexpr int kLdsBytes = kStages * kStageBytes;
+constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
 
 // Byte offsets inside a tile (rows x K of A, 256 x K of B^T, the output tile)
 // must stay below 4 GiB: they are 32-bit.
@@ -68,8 +66,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // slower, no permutation ~2.3x slower).
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-// Wait until at most n vector-memory operations of this wave are outstanding
-// (n in {0, 8, 16}); encodes vmcnt with expcnt and lgkmcnt left at their maxima.
+// Wait until at most n (< 64) vector-memory operations of this wave are
+// outstanding; encodes vmcnt with expcnt and lgkmcnt left at their maxima.
 template <int n>
 __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
@@ -204,11 +202,11 @@ __device__ __forceinline__ unsigned char* ring_slot(unsigned char* lds, int stag
 // One stage ks of the K loop. On entry a0/b0 hold its first k-step's
 // fragments; on exit they hold the first k-step's fragments of stage ks + 1.
 // Stage j is loaded in two halves: the first during the second half of stage
-// j - S + 1 (into the slot the barrier there freed), the second during the
-// first half of stage j - S + 2 (S = kStages). kLoadB / kLoadA: issue the
-// second half of stage ks + S - 2 / the first half of stage ks + S - 1.
-// kWait: vector-memory operations allowed in flight once stage ks + 1 has
-// landed (those issued after it).
+// j - 3 (into the slot the barrier there freed), the second during the first
+// half of stage j - 2. kLoadB / kLoadA: issue the second half of stage
+// ks + 2 / the first half of stage ks + 3. kWait: vector-memory operations
+// allowed in flight once stage ks + 1 has landed (those issued after it: the
+// two halves of stage ks + 2, 8 operations, while there is one).
 template <bool kLoadB, bool kLoadA, int kWait>
 __device__ __forceinline__ void k_stage(const Tile& t, const Lanes& o, const Frag& f, unsigned char* lds, int ks,
                                         bf16x8 (&a0)[4], bf16x8 (&b0)[4], bf16x8 (&a1)[4], bf16x8 (&b1)[4],
@@ -230,18 +228,18 @@ __device__ __forceinline__ void k_stage(const Tile& t, const Lanes& o, const Fra
   schedule_half<kLoadA>();
 }
 
-// The loads of the first stages of a tile (stage S - 2 only half): issued
-// ahead, e.g. while the previous tile's epilogue runs, once every wave has
-// finished reading the ring. tile_finish must follow with the same tile.
+// The loads of the first stages of a tile (stages 0 and 1, the first half of
+// stage 2): issued ahead, e.g. while the previous tile's epilogue runs, once
+// every wave has finished reading the ring. tile_finish must follow with the
+// same tile.
 __device__ __forceinline__ void tile_start(const Tile& t, unsigned char* lds) {
-  constexpr int S = kStages;
   const Lanes o = lane_offsets(t);
 #pragma unroll
-  for (int s = 0; s < S - 2; ++s) {
+  for (int s = 0; s < 2; ++s) {
     issue_half(t, o, s * BK, ring_slot(lds, s), 0);
     issue_half(t, o, s * BK, ring_slot(lds, s), 1);
   }
-  issue_half(t, o, (S - 2) * BK, ring_slot(lds, S - 2), 0);
+  issue_half(t, o, 2 * BK, ring_slot(lds, 2), 0);
 }
 
 // Stage kHookStage of the K loop with a hook: if hook.active() (uniform),
@@ -277,16 +275,17 @@ struct NoHook {
 constexpr int kHookStage = 2;
 
 // The K loop of a tile whose first stages tile_start issued; K / BK must be
-// at least kStages + kHookStage. `lds` holds kLdsBytes. Vector-memory
-// operations issued between the two calls (epilogue stores) are allowed:
-// loads complete in order among themselves, so each wait still covers the
-// stage it names, and at worst it also waits for those stores. `hook` runs
-// once, after the barrier of stage kHookStage; when hook.active(), every
-// earlier vector-memory operation of every wave is complete by then. On return every wave has
-// finished reading LDS and every load has landed.
+// at least kStages + kHookStage (every caller has K >= 256, i.e. 8 stages).
+// `lds` holds kLdsBytes. Vector-memory operations issued between the two
+// calls (epilogue stores) are allowed: loads complete in order among
+// themselves, so each wait still covers the stage it names, and at worst it
+// also waits for those stores. `hook` runs once, after the barrier of stage
+// kHookStage; when hook.active(), every earlier vector-memory operation of
+// every wave is complete by then. On return every wave has finished reading
+// LDS and every load has landed.
 template <typename Hook>
 __device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4], Hook& hook) {
-  constexpr int S = kStages, W = 8 * (S - 3);
+  constexpr int S = kStages, W = 8;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -294,7 +293,7 @@ __device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f
   const Frag f = frag_offsets();
   const Lanes o = lane_offsets(t);
   const int nk = t.K / BK;
-  wait_vmem<8 * (S - 3) + 4>();  // stage 0 landed (a half stage is 4 operations)
+  wait_vmem<12>();  // stage 0 landed: stage 1 and half of stage 2 (4 operations per half) may be in flight
   ring_barrier();
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   read_frags(lds, f, 0, a0, b0);
@@ -303,7 +302,6 @@ __device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f
   k_stage_hook<W>(t, o, f, lds, ks++, a0, b0, a1, b1, acc, hook);
   for (; ks < nk - S + 1; ++ks) k_stage<true, true, W>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
   k_stage<true, false, W>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);  // issues the last half (stage nk-1)
-  if (S == 5) k_stage<false, false, 8>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
   k_stage<false, false, 0>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
   k_stage<false, false, 0>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
   ring_barrier();

@@ -315,7 +315,6 @@ int run_pipeline(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipS
   if (st) return st;
   auto* ks = static_cast<KindState*>(p->kind_state);
   const uint32_t RB = (R + 255) / 256, CT = D / 256;
-  const uint32_t total = S * M * RB * CT;
   const uint64_t call = ks->calls + 1;
 
   PipeArgs a{};
@@ -334,7 +333,7 @@ int run_pipeline(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipS
   a.rb_target = (uint32_t)(call * CT);
   a.item_target = (uint32_t)(call * RB);
   a.done_target = (uint32_t)(call * ks->grid);
-  a.S = S; a.M = M; a.rows = R; a.d = D; a.RB = RB; a.CT = CT; a.total_tiles = total;
+  a.S = S; a.M = M; a.rows = R; a.d = D; a.RB = RB; a.CT = CT;
   a.epoch = (uint32_t)(p->epoch + 1);
   a.f = p->futures();
   p->launch_begin("pipeline", s);

@@ -80,7 +80,7 @@ struct PipeArgs {
   const __bf16* x;        // [M][rows][d] microbatch inputs
   __bf16* acts;           // [S][M][rows][d] stage outputs
   const __bf16* wt;       // [S][d][d] packed W_s^T ([out][in], K-contiguous)
-  const uint32_t* order;  // [total_tiles] tiles by queue, s | m << 8 | r << 16 | c << 24
+  const uint32_t* order;  // [S M RB CT] tiles by queue, s | m << 8 | r << 16 | c << 24
   const uint32_t* qstart; // [nq] first order index of each queue
   const uint32_t* qlen;   // [nq] tiles in each queue
   uint32_t* qctr;         // [nq] claim counters (cleared before each pass)
@@ -89,7 +89,7 @@ struct PipeArgs {
   uint32_t* item_ctr;     // [S][M] row blocks finished (cumulative)
   uint32_t* done_ctr;     // workgroups finished (cumulative)
   uint32_t rb_target, item_target, done_target;
-  uint32_t S, M, rows, d, RB, CT, total_tiles;
+  uint32_t S, M, rows, d, RB, CT;
   uint32_t epoch;
   Futures f;
 };
