@@ -99,6 +99,46 @@ def chain_sweep(pw, torch, pw_inputs, steps):
     return out
 
 
+def dispatch_study(pw, torch, pw_inputs, total=4096):
+    """Per-node cost of the chained A -> B program against program length D
+    (steps per call) for four ways of dispatching it: the persistent executor
+    (one launch per call, device-side futures gate every node), parallel
+    asynchronous dispatch (one launch per node, all enqueued without waiting),
+    a fused kernel loop (no futures), and sequential dispatch (one step per
+    call, the host waiting for it before the next)."""
+    modes = {"chained": pw.PW_CHAIN_CHAINED, "opbyop": pw.PW_CHAIN_OPBYOP, "fused": pw.PW_CHAIN_FUSED}
+    depths = (1, 4, 16, 64, 256, 1024, 4096)
+    out = {"total_steps_per_point": total, "elems_per_shard": 128, "unit": "ns per gated node (2 nodes per step)",
+           "by_n": {}}
+    for n in (256, 2048):
+        row = {}
+        st0 = torch.from_numpy(pw_inputs.chain_state(n, 128)).cuda()
+        for name, mode in modes.items():
+            ch = pw.Chain(n, 128, mode=mode)
+            row[name] = {}
+            for depth in depths:
+                st = st0.clone()
+                pw.future_wait(ch.run(st, depth), 60_000_000_000)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(total // depth):
+                    f = ch.run(st, depth)
+                pw.future_wait(f, 60_000_000_000)
+                torch.cuda.synchronize()
+                row[name][depth] = (time.perf_counter() - t0) / (2 * total) * 1e9
+            ch.plan.destroy()
+        ch = pw.Chain(n, 128, mode=pw.PW_CHAIN_OPBYOP)
+        st = st0.clone()
+        steps = 512
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            pw.future_wait(ch.run(st, 1), 60_000_000_000)
+        row["sequential"] = {1: (time.perf_counter() - t0) / (2 * steps) * 1e9}
+        ch.plan.destroy()
+        out["by_n"][n] = row
+    return out
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -260,6 +300,8 @@ def main():
     ap.add_argument("--no-reference", action="store_true", help="skip the vendor-BLAS and copy reference timings")
     ap.add_argument("--no-cpu-extra", action="store_true", help="skip the oracle samples of the chain and pipeline rows")
     ap.add_argument("--cpu-moe", action="store_true", help="also time the oracle on a 2048-token MoE sample (~45 s)")
+    ap.add_argument("--dispatch-study", action="store_true",
+                    help="also measure per-node cost against program length for the four dispatch modes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 plain elementwise copies of 1 GiB (torch.neg) to scale HBM counters")
     args = ap.parse_args()
@@ -364,6 +406,10 @@ def main():
     if not args.no_chain:
         log("chain sweep")
         result["chain"] = chain_sweep(pw, torch, pw_inputs, args.chain_steps)
+
+    if args.dispatch_study:
+        log("dispatch study")
+        result["dispatch_study"] = dispatch_study(pw, torch, pw_inputs)
 
     if not args.no_reference:
         log("reference (vendor BLAS, copy)")

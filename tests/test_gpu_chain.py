@@ -79,6 +79,28 @@ def test_chain_aux_receives_last_a(gpu):
     assert np.array_equal(aux.cpu().numpy().view(np.uint32), last_a.view(np.uint32))
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("depth", [1, 3, 20])
+def test_chain_split_into_calls_matches_one_program(gpu, mode, depth):
+    """20 steps run as calls of `depth` steps each (each call's Result is the
+    next call's Arg, the epochs continue) equal the oracle's 20 steps bit for
+    bit: the program length per call changes dispatch, not values."""
+    pw = gpu
+    n, e, k = 64, 128, 20
+    x0 = pw_inputs.chain_state(n, e)
+    ref = oc.chain(x0, k)
+    ch = pw.Chain(n, e, mode=_mode(pw, mode))
+    st = torch.from_numpy(x0).cuda()
+    done = 0
+    while done < k:
+        d = min(depth, k - done)
+        f = ch.run(st, d)
+        done += d
+    pw.future_wait(f, 10_000_000_000)
+    assert np.array_equal(st.cpu().numpy().view(np.uint32), ref.state.view(np.uint32))
+    assert not np.all(ref.state == np.float32(1.0))  # still short of the fp32 fixed point
+
+
 def test_chain_rejects_bad_state(gpu):
     pw = gpu
     ch = pw.Chain(8, 128)
