@@ -321,6 +321,32 @@ int Plan::read_epoch(uint32_t node, uint32_t shard, uint32_t* v) {
   return PW_OK;
 }
 
+// The status word and one future's epoch with a single round trip: two small
+// copies into pinned host memory on the read-back stream, one synchronize.
+int Plan::read_status_and_epoch(uint32_t node, uint32_t shard, uint32_t* status, uint32_t* epoch) {
+  if (node >= kNodes || shard >= L.width) return fail(PW_ERR_INVALID, "future (%u, %u) outside the table", node, shard);
+  if (!aux) {
+    hipError_t e = hipStreamCreateWithFlags(&aux, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreate");
+  }
+  if (!host_words) {
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&host_words), 2 * sizeof(uint32_t), hipHostMallocDefault);
+    if (e != hipSuccess) {
+      host_words = nullptr;
+      return hip_fail(e, "hipHostMalloc");
+    }
+  }
+  auto* base = static_cast<unsigned char*>(ws);
+  const uint32_t* fut = reinterpret_cast<const uint32_t*>(base + L.fut) + node * L.width + shard;
+  hipError_t e = hipMemcpyAsync(host_words, base + L.ctl, 4, hipMemcpyDeviceToHost, aux);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_words + 1, fut, 4, hipMemcpyDeviceToHost, aux);
+  if (e == hipSuccess) e = hipStreamSynchronize(aux);
+  if (e != hipSuccess) return hip_fail(e, "reading the status word and the future table");
+  *status = host_words[0];
+  *epoch = host_words[1];
+  return PW_OK;
+}
+
 static int status_to_code(uint32_t st) {
   switch (st) {
     case ST_OK: return PW_OK;
@@ -504,6 +530,7 @@ int pw_plan_destroy(pw_plan_t plan) {
   for (auto e : p->done_pool) (void)hipEventDestroy(e);
   for (auto e : p->event_pool) (void)hipEventDestroy(e);
   if (p->aux) (void)hipStreamDestroy(p->aux);
+  if (p->host_words) (void)hipHostFree(p->host_words);
   plan_release_kind(p);
   delete p;
   return PW_OK;
@@ -540,13 +567,15 @@ static int future_common(pw_future_t f, Plan** out) {
 }
 
 static int check_fired(Plan* p, pw_future_t f) {
-  uint32_t st = 0;
-  int rc = p->read_status(&st, true);
-  if (rc) return rc;
-  if (st) return status_to_code(st);
+  uint32_t st = 0, v = 0;
   const uint32_t shard = f.shard < 0 ? 0u : (uint32_t)f.shard;
-  uint32_t v = 0;
-  if ((rc = p->read_epoch(f.node, shard, &v))) return rc;
+  int rc = p->read_status_and_epoch(f.node, shard, &st, &v);
+  if (rc) return rc;
+  if (st) {  // latched device error: report it and clear it for the next call
+    uint32_t again = 0;
+    if ((rc = p->read_status(&again, true))) return rc;
+    return status_to_code(st);
+  }
   if ((int32_t)(v - (uint32_t)f.epoch) < 0)
     return fail(PW_ERR_STATE, "future (%u, %d) holds epoch %u < %llu after its call completed", f.node, f.shard, v,
                 (unsigned long long)f.epoch);
@@ -565,6 +594,8 @@ int pw_future_wait(pw_future_t f, int64_t timeout_ns) {
     hipError_t err = hipEventSynchronize(e);
     if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
   } else {
+    // spin for the first 100 us (short device work completes with no sleep
+    // latency), then poll every 20 us
     const auto t0 = std::chrono::steady_clock::now();
     while (true) {
       hipError_t err = hipEventQuery(e);
@@ -572,7 +603,7 @@ int pw_future_wait(pw_future_t f, int64_t timeout_ns) {
       if (err != hipErrorNotReady) return hip_fail(err, "hipEventQuery");
       const auto el = std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count();
       if (el >= timeout_ns) return fail(PW_ERR_TIMEOUT, "future not fired within %lld ns", (long long)timeout_ns);
-      std::this_thread::sleep_for(std::chrono::microseconds(20));
+      if (el > 100000) std::this_thread::sleep_for(std::chrono::microseconds(20));
     }
   }
   return check_fired(p, f);

@@ -53,6 +53,7 @@ struct Plan {
   std::deque<Done> done;  // completion events of the latest calls
   std::vector<hipEvent_t> done_pool;
   hipStream_t aux = nullptr;  // non-blocking stream for small read-backs
+  uint32_t* host_words = nullptr;  // pinned: status word and one future epoch, read back together
 
   struct Pending {
     const char* name;
@@ -77,6 +78,7 @@ struct Plan {
   hipEvent_t event_for(uint64_t epoch) const;
   Futures futures() const;
   int read_status(uint32_t* status, bool clear);
+  int read_status_and_epoch(uint32_t node, uint32_t shard, uint32_t* status, uint32_t* epoch);
   int read_epoch(uint32_t node, uint32_t shard, uint32_t* v);
   unsigned char* base() const { return static_cast<unsigned char*>(ws); }
 };
