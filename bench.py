@@ -139,6 +139,116 @@ def dispatch_study(pw, torch, pw_inputs, total=4096):
     return out
 
 
+def multi_tenant(pw, torch, pw_inputs, point_s=1.5, target_ms=0.33):
+    """Programs of concurrent clients through the multi-tenant scheduler
+    (PATHWAYS page, section 5.2, Figures 8 and 9; Appendix D, Figure 11).
+    A program is a chained run of D steps over 256 shards x 128 fp32, D sized
+    to ~0.33 ms of device time. Throughput: each client a host thread in a
+    closed loop (submit, wait), per client count, against one client calling
+    the plan directly (no scheduler); busy = summed device time of the
+    programs over the span from the first start to the last end. Shares: four
+    clients with every program queued up front, device time per client over
+    the dispatches before the first client runs dry."""
+    import threading
+    n, e = 256, 128
+    x0 = torch.from_numpy(pw_inputs.chain_state(n, e)).cuda()
+    cal = pw.Chain(n, e)
+    st = x0.clone()
+    pw.future_wait(cal.run(st, 256), 60_000_000_000)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pw.future_wait(cal.run(st, 4096), 60_000_000_000)
+    step_s = (time.perf_counter() - t0) / 4096
+    d = max(1, int(round(target_ms * 1e-3 / step_s)))
+    cal.plan.destroy()
+    out = {"program": f"chained run of {d} steps, {n} shards x {e} fp32", "steps_per_program": d}
+
+    # one client calling the plan directly, no scheduler
+    ch = pw.Chain(n, e)
+    st = x0.clone()
+    pw.future_wait(ch.run(st, d), 60_000_000_000)
+    k = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < point_s:
+        pw.future_wait(ch.run(st, d), 60_000_000_000)
+        k += 1
+    wall = time.perf_counter() - t0
+    out["direct_one_client"] = {"programs_per_s": k / wall, "program_ms_wall": wall / k * 1e3}
+    ch.plan.destroy()
+
+    def closed_loop(clients, weights=None):
+        sch = pw.Sched(2)
+        chains = [pw.Chain(n, e) for _ in range(clients)]
+        states = [x0.clone() for _ in range(clients)]
+        for c in range(clients):
+            sch.add_client(weights[c] if weights else 1)
+        for c in range(clients):  # warm the plans
+            sch.wait(sch.submit_chain(c, chains[c], states[c], d), 60_000_000_000)
+        sch.records()
+        stop = [False]
+        done = [0] * clients
+
+        def client(c):
+            while not stop[0]:
+                sch.wait(sch.submit_chain(c, chains[c], states[c], d), 60_000_000_000)
+                done[c] += 1
+
+        ths = [threading.Thread(target=client, args=(c,)) for c in range(clients)]
+        t0 = time.perf_counter()
+        for th in ths:
+            th.start()
+        time.sleep(point_s)
+        stop[0] = True
+        for th in ths:
+            th.join()
+        wall = time.perf_counter() - t0
+        recs = sch.records()
+        sch.destroy()
+        for ch in chains:
+            ch.plan.destroy()
+        busy = sum(r[5] - r[4] for r in recs)
+        span = max(r[5] for r in recs) - min(r[4] for r in recs)
+        return {"programs_per_s": sum(done) / wall, "device_busy": busy / span,
+                "program_ms_device": busy / len(recs), "programs": sum(done)}
+
+    out["scheduler_clients"] = {}
+    for c in (1, 2, 4, 8, 16):
+        out["scheduler_clients"][c] = closed_loop(c)
+
+    def shares(weights, per_client=240):
+        sch = pw.Sched(2)
+        chains = [pw.Chain(n, e) for _ in weights]
+        states = [x0.clone() for _ in weights]
+        for w in weights:
+            sch.add_client(w)
+        sch.hold(True)
+        tickets = [sch.submit_chain(c, chains[c], states[c], d) for c in range(len(weights)) for _ in range(per_client)]
+        sch.hold(False)
+        for t in tickets:
+            sch.wait(t, 60_000_000_000)
+        recs = sch.records()
+        sch.destroy()
+        for ch in chains:
+            ch.plan.destroy()
+        # the window where every client still had queued programs
+        seen = [0] * len(weights)
+        end = len(recs)
+        for i, r in enumerate(recs):
+            seen[r[1]] += 1
+            if seen[r[1]] == per_client:
+                end = i + 1
+                break
+        dev = [0.0] * len(weights)
+        for r in recs[:end]:
+            dev[r[1]] += r[5] - r[4]
+        tot = sum(dev)
+        return {"weights": list(weights), "device_time_share": [x / tot for x in dev],
+                "target_share": [w / sum(weights) for w in weights], "window_programs": end}
+
+    out["shares"] = [shares((1, 1, 1, 1)), shares((1, 2, 4, 8))]
+    return out
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -302,6 +412,8 @@ def main():
     ap.add_argument("--cpu-moe", action="store_true", help="also time the oracle on a 2048-token MoE sample (~45 s)")
     ap.add_argument("--dispatch-study", action="store_true",
                     help="also measure per-node cost against program length for the four dispatch modes")
+    ap.add_argument("--multi-tenant", action="store_true",
+                    help="throughput of concurrent clients and proportional shares through the scheduler")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 plain elementwise copies of 1 GiB (torch.neg) to scale HBM counters")
     args = ap.parse_args()
@@ -410,6 +522,10 @@ def main():
     if args.dispatch_study:
         log("dispatch study")
         result["dispatch_study"] = dispatch_study(pw, torch, pw_inputs)
+
+    if args.multi_tenant:
+        log("multi-tenant scheduler")
+        result["multi_tenant"] = multi_tenant(pw, torch, pw_inputs)
 
     if not args.no_reference:
         log("reference (vendor BLAS, copy)")

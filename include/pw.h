@@ -280,6 +280,82 @@ int pw_plan_kernel_times(pw_plan_t plan, pw_kernel_time* out, int max, int* n);
 /* Clear the accumulated kernel times. */
 int pw_plan_reset_times(pw_plan_t plan);
 
+/* ======================================================================== *
+ * Multi-tenant scheduler (PATHWAYS page, section 5.2 "Multi-tenancy",
+ * Figures 8 and 9; Appendix D, Figure 11): programs of several clients are
+ * gang-scheduled onto the whole GPU one after another, interleaved at the
+ * granularity of one program, and each client receives accelerator time in
+ * proportion to its weight (e.g. 1:1:1:1 or 1:2:4:8).
+ *
+ * Policy (the pages name none): stride scheduling in integers. Client c has
+ * weight w_c and stride floor(2^32 / w_c); among clients with queued
+ * programs the smallest pass dispatches its oldest program (ties: lowest
+ * client number) and advances by cost * stride; a client whose queue was
+ * empty resumes at max(its pass, the pass of the last dispatch).
+ *
+ * One dispatch thread per scheduler issues the programs, in that order, on
+ * one stream the scheduler owns (default priority), keeping at most
+ * max_inflight of them queued on the device so that the order decided on
+ * the host is close to the order the device runs. A plan submitted here
+ * must not be used by other callers while it has programs pending; its
+ * buffers stay the caller's, alive until pw_sched_wait returned for the
+ * program. Thread safety: every pw_sched_* call may come from any thread.
+ * ======================================================================== */
+typedef struct pw_sched_s* pw_sched_t;
+
+typedef enum { PW_PROG_CHAIN = 0, PW_PROG_EXCHANGE = 1 } pw_prog_kind;
+
+typedef struct {
+  uint32_t kind;          /* pw_prog_kind                                                    */
+  uint32_t cost;          /* accelerator time charged to the client, caller's units, 1..2^20  */
+  pw_plan_t plan;         /* CHAIN or PIPELINE plan for PW_PROG_CHAIN; EXCHANGE or MOE plan   */
+  uint64_t steps;         /* PW_PROG_CHAIN: pw_chain_run's steps                              */
+  pw_sharded_buf state;   /* PW_PROG_CHAIN: pw_chain_run's state (copied at submission)        */
+  void* aux;              /* PW_PROG_CHAIN: pw_chain_run's aux                                */
+  pw_exchange_io io;      /* PW_PROG_EXCHANGE: pw_exchange's arguments (copied at submission) */
+} pw_program;
+
+typedef struct {
+  uint64_t ticket;        /* as returned by pw_sched_submit                                   */
+  uint32_t client;
+  int32_t status;         /* the launch call's status                                         */
+  uint64_t dispatch;      /* position in the dispatch order, from 0                           */
+  double start_ms;        /* device time the program started / ended, in ms after the         */
+  double end_ms;          /* scheduler's first dispatch (HIP events on its stream)            */
+} pw_sched_record;
+
+/* Create a scheduler on the current HIP device. max_inflight in [1, 64].
+ * Creates its stream and its dispatch thread. */
+int pw_sched_create(uint32_t max_inflight, pw_sched_t* out);
+
+/* Add a client with weight in [1, 65536]; *client receives its number
+ * (0, 1, ... in call order). */
+int pw_sched_add_client(pw_sched_t s, uint32_t weight, uint32_t* client);
+
+/* Queue a program for `client`. Validates the kind, cost and plan handle
+ * (argument errors of the launch itself surface at pw_sched_wait); copies
+ * *prog. *ticket receives the program's ticket (1, 2, ...). */
+int pw_sched_submit(pw_sched_t s, uint32_t client, const pw_program* prog, uint64_t* ticket);
+
+/* Block until the program of `ticket` has finished on the device or
+ * timeout_ns passed (< 0: no limit). Returns the launch status, else the
+ * plan's latched device status (as pw_future_wait), else PW_OK. A ticket is
+ * waited at most once: afterwards it is unknown (PW_ERR_STATE). */
+int pw_sched_wait(pw_sched_t s, uint64_t ticket, int64_t timeout_ns);
+
+/* hold != 0: dispatch nothing until called again with 0 (programs keep
+ * queuing; what is already on the device runs on). */
+int pw_sched_hold(pw_sched_t s, int hold);
+
+/* Copy the records of finished programs, in dispatch order, from the
+ * oldest not yet read: up to `capacity` into out; *n receives the count.
+ * Records are dropped once read. */
+int pw_sched_records(pw_sched_t s, pw_sched_record* out, size_t capacity, size_t* n);
+
+/* Wait for every queued and running program, stop the thread, destroy the
+ * stream. Tickets not yet waited are dropped. */
+int pw_sched_destroy(pw_sched_t s);
+
 #ifdef __cplusplus
 }
 #endif

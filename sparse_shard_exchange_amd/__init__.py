@@ -75,6 +75,23 @@ class pw_kernel_time(C.Structure):
     _fields_ = [("name", C.c_char * 32), ("launches", C.c_uint64), ("total_ms", C.c_double)]
 
 
+PW_PROG_CHAIN, PW_PROG_EXCHANGE = 0, 1
+
+
+class pw_program(C.Structure):
+    _fields_ = [
+        ("kind", C.c_uint32), ("cost", C.c_uint32), ("plan", C.c_void_p), ("steps", C.c_uint64),
+        ("state", pw_sharded_buf), ("aux", C.c_void_p), ("io", pw_exchange_io),
+    ]
+
+
+class pw_sched_record(C.Structure):
+    _fields_ = [
+        ("ticket", C.c_uint64), ("client", C.c_uint32), ("status", C.c_int32), ("dispatch", C.c_uint64),
+        ("start_ms", C.c_double), ("end_ms", C.c_double),
+    ]
+
+
 # Every function the header declares, with its C signature.
 _SIGNATURES = {
     "pw_abi_version": (C.c_uint32, []),
@@ -91,6 +108,13 @@ _SIGNATURES = {
                                        C.POINTER(C.c_uint32), C.POINTER(C.c_uint32)]),
     "pw_plan_kernel_times": (C.c_int, [C.c_void_p, C.POINTER(pw_kernel_time), C.c_int, C.POINTER(C.c_int)]),
     "pw_plan_reset_times": (C.c_int, [C.c_void_p]),
+    "pw_sched_create": (C.c_int, [C.c_uint32, C.POINTER(C.c_void_p)]),
+    "pw_sched_add_client": (C.c_int, [C.c_void_p, C.c_uint32, C.POINTER(C.c_uint32)]),
+    "pw_sched_submit": (C.c_int, [C.c_void_p, C.c_uint32, C.POINTER(pw_program), C.POINTER(C.c_uint64)]),
+    "pw_sched_wait": (C.c_int, [C.c_void_p, C.c_uint64, C.c_int64]),
+    "pw_sched_hold": (C.c_int, [C.c_void_p, C.c_int]),
+    "pw_sched_records": (C.c_int, [C.c_void_p, C.POINTER(pw_sched_record), C.c_size_t, C.POINTER(C.c_size_t)]),
+    "pw_sched_destroy": (C.c_int, [C.c_void_p]),
 }
 
 
@@ -385,3 +409,82 @@ class MoE:
         io.experts = _ptr(self.experts)
         io.gates = _ptr(self.gates)
         return self.plan.exchange(io, stream)
+
+
+class Sched:
+    """Multi-tenant scheduler: clients with weights submit programs (chain
+    runs, exchange steps) that run one after another on the scheduler's own
+    stream in proportional shares. Tensors handed to a program are kept
+    referenced here until its ticket is waited."""
+
+    def __init__(self, max_inflight=2):
+        h = C.c_void_p()
+        check(lib.pw_sched_create(max_inflight, C.byref(h)))
+        self.handle = h
+        self._keep = {}
+
+    def add_client(self, weight=1) -> int:
+        c = C.c_uint32(0)
+        check(lib.pw_sched_add_client(self.handle, weight, C.byref(c)))
+        return c.value
+
+    def _submit(self, client, prog, keep) -> int:
+        t = C.c_uint64(0)
+        check(lib.pw_sched_submit(self.handle, client, C.byref(prog), C.byref(t)))
+        self._keep[t.value] = keep
+        return t.value
+
+    def submit_chain(self, client, chain, state, steps, cost=None, aux=None) -> int:
+        """A chain run of `steps` steps of `chain` (a Chain) over `state`;
+        cost defaults to the step count."""
+        prog = pw_program()
+        prog.kind = PW_PROG_CHAIN
+        prog.cost = steps if cost is None else cost
+        prog.plan = chain.plan.handle.value
+        prog.steps = steps
+        prog.state = sharded(state, chain.N, chain.E, PW_F32)
+        prog.aux = _ptr(aux)
+        return self._submit(client, prog, (chain, state, aux))
+
+    def submit_exchange(self, client, ex, x, dest, cost=1) -> int:
+        """One step of `ex` (an Exchange) on x, dest."""
+        prog = pw_program()
+        prog.kind = PW_PROG_EXCHANGE
+        prog.cost = cost
+        prog.plan = ex.plan.handle.value
+        prog.io = ex.io(x, dest)
+        return self._submit(client, prog, (ex, x, dest))
+
+    def wait(self, ticket, timeout_ns=-1) -> None:
+        rc = lib.pw_sched_wait(self.handle, ticket, timeout_ns)
+        if rc != PW_ERR_TIMEOUT:  # the ticket is consumed; on a timeout it stays waitable
+            self._keep.pop(ticket, None)
+        check(rc)
+
+    def hold(self, on=True) -> None:
+        check(lib.pw_sched_hold(self.handle, 1 if on else 0))
+
+    def records(self, capacity=1 << 16) -> list:
+        """Records of finished programs in dispatch order (each read once):
+        (ticket, client, status, dispatch, start_ms, end_ms) tuples."""
+        out = []
+        buf = (pw_sched_record * capacity)()
+        while True:
+            n = C.c_size_t(0)
+            check(lib.pw_sched_records(self.handle, buf, capacity, C.byref(n)))
+            out += [(r.ticket, r.client, r.status, r.dispatch, r.start_ms, r.end_ms) for r in buf[:n.value]]
+            if n.value < capacity:
+                return out
+
+    def destroy(self) -> None:
+        if self.handle:
+            check(lib.pw_sched_destroy(self.handle))
+            self.handle = None
+            self._keep.clear()
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                lib.pw_sched_destroy(self.handle)
+        except Exception:
+            pass

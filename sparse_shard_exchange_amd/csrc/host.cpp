@@ -42,6 +42,8 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+void clear_error() { g_last_error.clear(); }
+
 int hip_fail(hipError_t e, const char* what) {
   return fail(PW_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
@@ -689,3 +691,13 @@ int pw_plan_reset_times(pw_plan_t plan) {
 }
 
 }  // extern "C"
+
+// The status of a call known to have finished (its completion event
+// passed): the plan's latched device status, then the future's epoch.
+int pw::future_check(pw_future_t f) {
+  Plan* p = nullptr;
+  int rc = future_common(f, &p);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(p->mu);
+  return check_fired(p, f);
+}

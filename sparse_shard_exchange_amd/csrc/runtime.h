@@ -85,6 +85,9 @@ struct Plan {
 
 int fail(int code, const char* fmt, ...);
 int hip_fail(hipError_t e, const char* what);
+void clear_error();                 // empty this thread's pw_last_error()
+bool is_live(const Plan* p);        // the registry holds p
+int future_check(pw_future_t f);    // latched device status of a call known to have finished
 
 // graphs.cpp: the CHAIN, MOE and PIPELINE programs.
 int validate_desc_more(const pw_plan_desc* d);

@@ -41,6 +41,26 @@ def test_struct_sizes_match_the_header_layout():
     assert C.sizeof(pw.pw_future_t) == 24
     assert C.sizeof(pw.pw_sharded_buf) == 40
     assert C.sizeof(pw.pw_plan_desc) == 112
+    assert C.sizeof(pw.pw_exchange_io) == 144
+    assert C.sizeof(pw.pw_program) == 216
+    assert C.sizeof(pw.pw_sched_record) == 40
+
+
+def test_scheduler_argument_errors_need_no_device():
+    h = C.c_void_p(0)
+    assert pw.lib.pw_sched_create(0, C.byref(h)) == pw.PW_ERR_INVALID
+    assert pw.lib.pw_sched_create(65, C.byref(h)) == pw.PW_ERR_INVALID
+    assert pw.lib.pw_sched_create(1, None) == pw.PW_ERR_INVALID
+    c = C.c_uint32(0)
+    assert pw.lib.pw_sched_add_client(None, 1, C.byref(c)) == pw.PW_ERR_INVALID
+    t = C.c_uint64(0)
+    prog = pw.pw_program()
+    assert pw.lib.pw_sched_submit(None, 0, C.byref(prog), C.byref(t)) == pw.PW_ERR_INVALID
+    assert pw.lib.pw_sched_wait(None, 1, 0) == pw.PW_ERR_INVALID
+    assert pw.lib.pw_sched_hold(None, 1) == pw.PW_ERR_INVALID
+    n = C.c_size_t(0)
+    assert pw.lib.pw_sched_records(None, None, 0, C.byref(n)) == pw.PW_ERR_INVALID
+    assert pw.lib.pw_sched_destroy(None) == pw.PW_ERR_INVALID
 
 
 def _ex(**kw):
