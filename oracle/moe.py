@@ -18,8 +18,15 @@ Readings where the pages are silent:
   * expert FFN with no biases: H = bf16(GELU(fp32(X_e . W1_e))),
     Y_e = bf16(fp32(H . W2_e)), weights stored [in][out], GELU exact (erf);
   * combine: out[t] = bf16(g_0 * Y[slot of (t,0)] + g_1 * Y[slot of (t,1)]),
-    summed in fp64 and rounded to fp32 then bf16; no capacity limit, no
-    dropped tokens.
+    summed in fp64 and rounded to fp32 then bf16; without a capacity limit
+    no tuple is dropped.
+  * with a capacity C per expert (section 4.5: a node whose resource needs
+    depend on its predecessor's results; the usual way to give expert
+    buffers a static bound): an expert keeps the first C of its tuples in
+    tuple order g and drops the rest; the kept tuples are placed as without
+    a limit (segments of min(n_e, C) rows, source order inside); a dropped
+    tuple contributes nothing to its token's combine (its gate is not
+    renormalised), so a token with both tuples dropped combines to zero.
 
 Arrays are numpy float32 holding bf16-exact values where the workload is
 bf16 (callers convert bf16 tensors with ``.float()``).
@@ -82,25 +89,45 @@ class MoEResult:
     out: np.ndarray | None # [T, d] combined output
 
 
-def route(logits: np.ndarray, num_experts: int, num_src: int):
-    """Top-2, gates and the dispatch exchange from fp32 logits."""
+def capacity_keep(dest: np.ndarray, num_experts: int, capacity: int) -> np.ndarray:
+    """keep[g]: tuple g is among the first `capacity` tuples of its expert in
+    tuple order (capacity 0: no limit, every tuple kept)."""
+    keep = np.ones(dest.size, dtype=bool)
+    if capacity <= 0:
+        return keep
+    seen = np.zeros(num_experts, dtype=np.int64)
+    for g in range(dest.size):
+        e = dest[g]
+        keep[g] = seen[e] < capacity
+        seen[e] += 1
+    return keep
+
+
+def route(logits: np.ndarray, num_experts: int, num_src: int, capacity: int = 0):
+    """Top-2, gates and the dispatch exchange from fp32 logits. counts are
+    the routed tuples per (source, expert) before any capacity limit;
+    offsets and src_index describe the kept tuples only."""
     experts, kept = top2(logits)
     g = gates(kept)
     dest = experts.reshape(-1)
     t = logits.shape[0]
     counts = histogram(dest, num_experts, num_src, (2 * t) // num_src)
-    offsets = exclusive_scan(counts.sum(axis=0))
-    src_index = stable_place(dest, offsets)
+    keep = capacity_keep(dest, num_experts, capacity)
+    idx = np.flatnonzero(keep)
+    offsets = exclusive_scan(np.bincount(dest[idx], minlength=num_experts)[:num_experts])
+    src_index = idx[stable_place(dest[idx], offsets)]
     return experts, g, dest, counts, offsets, src_index
 
 
-def moe_step(x, w_router, w1, w2, num_src: int = 1, logits=None, with_ffn: bool = True) -> MoEResult:
+def moe_step(x, w_router, w1, w2, num_src: int = 1, logits=None, with_ffn: bool = True,
+             capacity: int = 0) -> MoEResult:
     """The whole step on every token. ``logits`` may be given to recompute the
-    routing from another implementation's fp32 logits."""
+    routing from another implementation's fp32 logits. ``capacity``: tuples
+    kept per expert (0: no limit)."""
     if logits is None:
         logits = router_logits(x, w_router)
     num_experts = w_router.shape[1]
-    experts, g, dest, counts, offsets, src_index = route(logits, num_experts, num_src)
+    experts, g, dest, counts, offsets, src_index = route(logits, num_experts, num_src, capacity)
     y = out = None
     if with_ffn:
         t = x.shape[0]
@@ -110,9 +137,11 @@ def moe_step(x, w_router, w1, w2, num_src: int = 1, logits=None, with_ffn: bool 
             lo, hi = offsets[e], offsets[e + 1]
             if hi > lo:
                 y[lo:hi] = expert_ffn(rows[lo:hi], w1[e], w2[e])
-        pos = np.empty(2 * t, dtype=np.int64)          # slot of tuple g
-        pos[src_index] = np.arange(2 * t)
-        out = combine_rows(g, y[pos[0::2]], y[pos[1::2]])
+        pos = np.full(2 * t, -1, dtype=np.int64)       # slot of tuple g, -1 if dropped
+        pos[src_index] = np.arange(src_index.size)
+        zero = np.zeros((1, x.shape[1]), dtype=np.float32)
+        yz = np.concatenate([y, zero])                 # row -1: a dropped tuple's zero contribution
+        out = combine_rows(g, yz[pos[0::2]], yz[pos[1::2]])
     return MoEResult(logits, experts, g, dest, counts, offsets, src_index, y, out)
 
 

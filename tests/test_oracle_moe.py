@@ -137,6 +137,59 @@ def test_planted_swap_of_gates_is_caught(monkeypatch):
     assert not np.array_equal(good.out, bad.out)
 
 
+def test_capacity_drops_by_hand():
+    """Four tokens, two experts, capacity 2 (logits chosen so the routing is
+    [[0, 1], [0, 1], [1, 0], [0, 1]]): tuples g = 2t + slot go to experts
+    0 1 | 0 1 | 1 0 | 0 1. Expert 0 receives g = 0, 2, 5, 6 and keeps 0, 2;
+    expert 1 receives g = 1, 3, 4, 7 and keeps 1, 3. Tokens 2 and 3 lose
+    both tuples and combine to zero; tokens 0 and 1 are as without a limit."""
+    x, wr, w1, w2 = _tiny(tokens=4, e=2)
+    logits = np.array([[2.0, 1.0], [3.0, -1.0], [0.0, 0.5], [1.0, 0.25]], np.float32)
+    r = moe.moe_step(x, wr, w1, w2, num_src=1, logits=logits, capacity=2)
+    assert r.experts.tolist() == [[0, 1], [0, 1], [1, 0], [0, 1]]
+    assert r.offsets.tolist() == [0, 2, 4]
+    assert r.src_index.tolist() == [0, 2, 1, 3]
+    assert r.counts.tolist() == [[4, 4]]                  # routed, before the limit
+    assert np.all(r.out[2:] == 0)
+    free = moe.moe_step(x, wr, w1, w2, num_src=1, logits=logits)
+    assert np.array_equal(r.out[:2], free.out[:2])
+    # capacity 3: expert 0 keeps g = 0, 2, 5 (token 2's slot 1), expert 1
+    # keeps g = 1, 3, 4 (token 2's slot 0): token 2 is whole again, token 3
+    # has no tuple left
+    r3 = moe.moe_step(x, wr, w1, w2, num_src=1, logits=logits, capacity=3)
+    assert r3.offsets.tolist() == [0, 3, 6]
+    assert r3.src_index.tolist() == [0, 2, 5, 1, 3, 4]
+    assert np.array_equal(r3.out[:3], free.out[:3]) and np.all(r3.out[3] == 0)
+
+
+def test_capacity_one_tuple_dropped_keeps_the_other_term():
+    """Three tokens, three experts, capacity 2, routing [[0, 1], [0, 2],
+    [0, 1]]: expert 0 receives g = 0, 2, 4 and drops g = 4 (token 2's top-1
+    tuple); experts 1 (g = 1, 5) and 2 (g = 3) keep everything. Token 2's
+    output is its top-2 term alone, bf16(g_1 * y), not renormalised."""
+    x, wr, w1, w2 = _tiny(tokens=3, e=3)
+    logits = np.array([[2.0, 1.0, 0.0], [2.0, 0.0, 1.0], [2.0, 1.0, 0.0]], np.float32)
+    r = moe.moe_step(x, wr, w1, w2, num_src=1, logits=logits, capacity=2)
+    assert r.experts.tolist() == [[0, 1], [0, 2], [0, 1]]
+    assert r.offsets.tolist() == [0, 2, 4, 5]
+    assert r.src_index.tolist() == [0, 2, 1, 5, 3]
+    y1 = moe.expert_ffn(x[2:3], w1[1], w2[1])[0]
+    assert np.array_equal(r.out[2], nm.to_bf16(nm.to_f32(float(r.gates[2, 1]) * y1.astype(np.float64))))
+    free = moe.moe_step(x, wr, w1, w2, num_src=1, logits=logits)
+    assert np.array_equal(r.out[:2], free.out[:2]) and not np.array_equal(r.out[2], free.out[2])
+
+
+def test_capacity_at_or_above_the_largest_count_changes_nothing():
+    x, wr, w1, w2 = _tiny()
+    free = moe.moe_step(x, wr, w1, w2, num_src=4)
+    top = int(free.counts.sum(axis=0).max())
+    for c in (top, top + 5):
+        r = moe.moe_step(x, wr, w1, w2, num_src=4, capacity=c)
+        assert np.array_equal(r.src_index, free.src_index) and np.array_equal(r.out, free.out)
+    r = moe.moe_step(x, wr, w1, w2, num_src=4, capacity=top - 1)
+    assert r.offsets[-1] == 80 - int((free.counts.sum(axis=0) > top - 1).sum())
+
+
 def test_moe_inputs_shapes():
     inp = pw_inputs.moe(tokens=64, d=32, experts=8, hidden=16)
     assert inp.x.dtype == torch.bfloat16 and tuple(inp.w1.shape) == (8, 32, 16) and tuple(inp.w2.shape) == (8, 16, 32)
