@@ -311,6 +311,47 @@ def moe_bench(pw, torch, pw_inputs, steps=3):
             "expert_flop": flops}
 
 
+def moe_capacity_bench(pw, torch, pw_inputs, steps=5):
+    """Data-dependent output sizes (PATHWAYS page, section 4.5: a node whose
+    resource needs depend on its predecessor falls back to sequential
+    scheduling). MoE steps with an expert capacity C (kept: the first C tuples
+    of each expert): the static path (one call, buffers of the bound
+    min(2T, E C)) against the sequential one (route, the host waits for the
+    segment offsets, allocates exactly, then the rest), wall clock per step
+    including the wait, at the full workload and at a 16x smaller one where
+    the host round trip weighs more."""
+    out = []
+    for tokens, factor in ((131072, 1.0), (131072, 1.25), (8192, 1.0)):
+        d, experts, hidden = 1024, 64, 4096
+        cap = int(factor * 2 * tokens / experts)
+        inp = pw_inputs.moe(tokens, d, experts, hidden)
+        wr, w1, w2 = inp.w_router.cuda(), inp.w1.cuda(), inp.w2.cuda()
+        x = inp.x.cuda()
+        ms = {}
+        rows = None
+        for mode in ("static", "sequential"):
+            m = pw.MoE(wr, w1, w2, tokens, num_src_shards=64, capacity=cap, want_logits=False,
+                       static_buffers=(mode == "static"))
+            run = m.step if mode == "static" else m.split_step
+            pw.future_wait(run(x), 60_000_000_000)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                f = run(x)
+            pw.future_wait(f, 60_000_000_000)
+            torch.cuda.synchronize()
+            ms[mode] = (time.perf_counter() - t0) / steps * 1e3
+            if mode == "sequential":
+                rows = int(m.xd.shape[0])
+            m.plan.destroy()
+        bound = min(2 * tokens, experts * cap)
+        out.append({"tokens": tokens, "capacity_factor": factor, "capacity": cap,
+                    "ms_per_step_static": ms["static"], "ms_per_step_sequential": ms["sequential"],
+                    "rows_static_bound": bound, "rows_routed": rows,
+                    "dropped_tuple_share": 1.0 - rows / (2 * tokens)})
+    return out
+
+
 def reference_bench(torch, iters=10):
     """Context, not the product path: the vendor BLAS (hipBLASLt through
     torch.matmul) on the shapes of the two GEMM rows, and torch's elementwise
@@ -412,6 +453,8 @@ def main():
     ap.add_argument("--cpu-moe", action="store_true", help="also time the oracle on a 2048-token MoE sample (~45 s)")
     ap.add_argument("--dispatch-study", action="store_true",
                     help="also measure per-node cost against program length for the four dispatch modes")
+    ap.add_argument("--moe-capacity", action="store_true",
+                    help="MoE with an expert capacity: one static call vs route, host wait, exact allocation, rest")
     ap.add_argument("--multi-tenant", action="store_true",
                     help="throughput of concurrent clients and proportional shares through the scheduler")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -514,6 +557,10 @@ def main():
     if not args.no_moe:
         log("moe")
         result["moe"] = moe_bench(pw, torch, pw_inputs)
+
+    if args.moe_capacity:
+        log("moe capacity: static vs sequential")
+        result["moe_capacity"] = moe_capacity_bench(pw, torch, pw_inputs)
 
     if not args.no_chain:
         log("chain sweep")

@@ -112,7 +112,9 @@ typedef struct {
   uint32_t microbatches;     /* PIPELINE: M                                                    */
   uint32_t chain_mode;       /* CHAIN: pw_chain_mode                                           */
   uint32_t flags;            /* PW_FLAG_*                                                      */
-  uint32_t reserved0;
+  uint32_t capacity;         /* MOE: tuples each expert keeps, the first in tuple order
+                                g = 2 * token + slot (0 = no limit); the rest are dropped and
+                                add nothing to their token's combine. Other kinds: 0         */
   uint64_t spin_limit_ns;    /* bound of every device-side wait (0 = 2 s); an expired wait
                                 latches PW_ERR_TIMEOUT and the waiting work is skipped        */
   /* Weights are stored [in][out], row-major. They are read once, when the plan is built
@@ -230,6 +232,33 @@ int pw_plan_destroy(pw_plan_t plan);
  * PW_ERR_INVALID before anything is enqueued.
  */
 int pw_exchange(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done);
+
+/*
+ * pw_exchange_begin / pw_exchange_end -- the same step in two calls, split
+ * where its output sizes become known (PATHWAYS page, section 4.5: a node
+ * whose resource needs depend on its predecessor's results falls back to
+ * sequential scheduling; here, the rows an MOE step dispatches under an
+ * expert capacity).
+ *
+ * begin enqueues Compute(A) (MOE: router and top-k gate), the histogram and
+ * the scan on `stream`, then BLOCKS until they finish and copies the
+ * destination segment offsets to offsets_host[0..N] (caller's host memory,
+ * N + 1 int64; for MOE with a capacity, of the kept tuples). It reads src,
+ * dest (EXCHANGE) and logits / experts / gates / counts (MOE, nullable) of
+ * io; the output fields are not read.
+ * end enqueues the scatter, B and the Result and returns at once; *done
+ * receives the Result future. Its io must name the src, dest, logits,
+ * experts, gates and counts begin was given (else PW_ERR_INVALID); dst and
+ * b_out need only hold offsets_host[N] rows.
+ * While a step is open (begin returned, end not yet called) pw_exchange and
+ * pw_exchange_begin on the plan return PW_ERR_STATE; pw_exchange_end
+ * without begin returns PW_ERR_STATE.
+ *
+ * pw_exchange needs dst and b_out of the static bound instead: G rows for
+ * EXCHANGE, 2 * tokens for MOE, or min(2 * tokens, E * capacity).
+ */
+int pw_exchange_begin(pw_plan_t plan, const pw_exchange_io* io, void* stream, int64_t* offsets_host);
+int pw_exchange_end(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done);
 
 /*
  * pw_chain_run -- run a chained program in one call (PATHWAYS page, section

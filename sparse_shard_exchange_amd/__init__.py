@@ -43,7 +43,7 @@ class pw_plan_desc(C.Structure):
         ("num_src_shards", C.c_uint32), ("tuples_per_shard", C.c_uint64), ("payload_elems", C.c_uint32),
         ("dtype", C.c_uint32), ("a_op", pw_op), ("b_op", pw_op), ("top_k", C.c_uint32),
         ("hidden", C.c_uint32), ("microbatches", C.c_uint32), ("chain_mode", C.c_uint32),
-        ("flags", C.c_uint32), ("reserved0", C.c_uint32), ("spin_limit_ns", C.c_uint64),
+        ("flags", C.c_uint32), ("capacity", C.c_uint32), ("spin_limit_ns", C.c_uint64),
         ("w_router", C.c_void_p), ("w1", C.c_void_p), ("w2", C.c_void_p),
     ]
 
@@ -100,6 +100,8 @@ _SIGNATURES = {
     "pw_plan": (C.c_int, [C.POINTER(pw_plan_desc), C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t), C.POINTER(C.c_void_p)]),
     "pw_plan_destroy": (C.c_int, [C.c_void_p]),
     "pw_exchange": (C.c_int, [C.c_void_p, C.POINTER(pw_exchange_io), C.c_void_p, C.POINTER(pw_future_t)]),
+    "pw_exchange_begin": (C.c_int, [C.c_void_p, C.POINTER(pw_exchange_io), C.c_void_p, C.c_void_p]),
+    "pw_exchange_end": (C.c_int, [C.c_void_p, C.POINTER(pw_exchange_io), C.c_void_p, C.POINTER(pw_future_t)]),
     "pw_chain_run": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(pw_sharded_buf), C.c_void_p, C.c_void_p,
                                C.POINTER(pw_future_t)]),
     "pw_future_wait": (C.c_int, [pw_future_t, C.c_int64]),
@@ -153,7 +155,7 @@ def op(kind=PW_OP_IDENTITY, a=0.0, b=0.0) -> pw_op:
 
 def desc(kind, num_shards, tuples_per_shard, payload_elems=0, dtype=PW_F32, num_src_shards=0,
          a_op=None, b_op=None, top_k=0, hidden=0, microbatches=0, chain_mode=PW_CHAIN_CHAINED,
-         flags=0, spin_limit_ns=0, w_router=None, w1=None, w2=None) -> pw_plan_desc:
+         flags=0, spin_limit_ns=0, w_router=None, w1=None, w2=None, capacity=0) -> pw_plan_desc:
     d = pw_plan_desc()
     d.abi_version = PW_ABI_VERSION
     d.kind = kind
@@ -169,6 +171,7 @@ def desc(kind, num_shards, tuples_per_shard, payload_elems=0, dtype=PW_F32, num_
     d.microbatches = microbatches
     d.chain_mode = chain_mode
     d.flags = flags
+    d.capacity = capacity
     d.spin_limit_ns = spin_limit_ns
     d.w_router = _ptr(w_router)
     d.w1 = _ptr(w1)
@@ -236,6 +239,19 @@ class Plan:
     def exchange(self, io: pw_exchange_io, stream=None) -> pw_future_t:
         f = pw_future_t()
         check(lib.pw_exchange(self.handle, C.byref(io), _stream(stream), C.byref(f)))
+        return f
+
+    def exchange_begin(self, io: pw_exchange_io, num_dest: int, stream=None):
+        """First half of a split step; blocks, returns the segment offsets
+        (numpy int64 [num_dest + 1])."""
+        import numpy as np
+        offs = np.zeros(num_dest + 1, dtype=np.int64)
+        check(lib.pw_exchange_begin(self.handle, C.byref(io), _stream(stream), C.c_void_p(offs.ctypes.data)))
+        return offs
+
+    def exchange_end(self, io: pw_exchange_io, stream=None) -> pw_future_t:
+        f = pw_future_t()
+        check(lib.pw_exchange_end(self.handle, C.byref(io), _stream(stream), C.byref(f)))
         return f
 
     def chain_run(self, steps: int, state: pw_sharded_buf, aux=None, stream=None) -> pw_future_t:
@@ -374,20 +390,25 @@ class MoE:
     Weights (bf16, stored [in][out]) are borrowed: keep them alive."""
 
     def __init__(self, w_router, w1, w2, tokens, num_src_shards=64, flags=0, spin_limit_ns=0,
-                 want_logits=True, want_counts=False, device="cuda"):
+                 want_logits=True, want_counts=False, capacity=0, static_buffers=True, device="cuda"):
         import torch
         self.d, self.E = w_router.shape
         self.hidden = w1.shape[2]
         assert tokens % num_src_shards == 0
         self.T, self.S = tokens, num_src_shards
         self.w = (w_router, w1, w2)
+        self.capacity = capacity
+        self.device = device
         self.desc = desc(PW_GRAPH_MOE, self.E, tokens // num_src_shards, self.d, PW_BF16,
                          num_src_shards=num_src_shards, top_k=2, hidden=self.hidden, flags=flags,
-                         spin_limit_ns=spin_limit_ns, w_router=w_router, w1=w1, w2=w2)
+                         spin_limit_ns=spin_limit_ns, w_router=w_router, w1=w1, w2=w2, capacity=capacity)
         self.plan = Plan(self.desc, device)
         bf = torch.bfloat16
-        self.xd = torch.empty((2 * tokens, self.d), dtype=bf, device=device)
-        self.y = torch.empty((2 * tokens, self.d), dtype=bf, device=device)
+        # dispatched rows at most: every tuple, or E * capacity if fewer
+        self.static_rows = min(2 * tokens, self.E * capacity) if capacity else 2 * tokens
+        rows = self.static_rows if static_buffers else 0  # split_step allocates them per step
+        self.xd = torch.empty((rows, self.d), dtype=bf, device=device)
+        self.y = torch.empty((rows, self.d), dtype=bf, device=device)
         self.out = torch.empty((tokens, self.d), dtype=bf, device=device)
         self.offsets = torch.empty(self.E + 1, dtype=torch.int64, device=device)
         self.src_index = torch.empty(2 * tokens, dtype=torch.int32, device=device)
@@ -396,7 +417,7 @@ class MoE:
         self.logits = torch.empty((tokens, self.E), dtype=torch.float32, device=device) if want_logits else None
         self.counts = torch.empty((num_src_shards, self.E), dtype=torch.int32, device=device) if want_counts else None
 
-    def step(self, x, stream=None) -> pw_future_t:
+    def _io(self, x) -> pw_exchange_io:
         io = pw_exchange_io()
         io.src = sharded(x, self.S, self.d, PW_BF16)
         io.dest = None
@@ -408,7 +429,26 @@ class MoE:
         io.logits = _ptr(self.logits)
         io.experts = _ptr(self.experts)
         io.gates = _ptr(self.gates)
-        return self.plan.exchange(io, stream)
+        return io
+
+    def step(self, x, stream=None) -> pw_future_t:
+        """One step with buffers of the static bound (one call)."""
+        return self.plan.exchange(self._io(x), stream)
+
+    def split_step(self, x, stream=None) -> pw_future_t:
+        """One step in two calls: route (the host waits for the segment
+        offsets), allocate the dispatched rows and expert outputs at exactly
+        the routed size, then run the rest."""
+        import torch
+        io = self._io(x)
+        offs = self.plan.exchange_begin(io, self.E, stream)
+        rows = int(offs[-1])
+        self.xd = torch.empty((rows, self.d), dtype=torch.bfloat16, device=self.device)
+        self.y = torch.empty((rows, self.d), dtype=torch.bfloat16, device=self.device)
+        io.dst = sharded(self.xd, self.E, self.d, PW_BF16, self.offsets)
+        io.dst.num_tuples = rows
+        io.b_out = _ptr(self.y)
+        return self.plan.exchange_end(io, stream)
 
 
 class Sched:

@@ -164,7 +164,10 @@ __global__ __launch_bounds__(kBlock) void k_scan(ExchangeArgs a) {
   __syncthreads();
   if (!is_last) return;
   __threadfence();
-  for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) a.expected[d] = column_scan(a.blk_base, a.N, d, 0, a.num_blk);
+  for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) {
+    const uint32_t total = column_scan(a.blk_base, a.N, d, 0, a.num_blk);
+    a.expected[d] = a.capacity ? min(total, a.capacity) : total;  // the tuples d keeps
+  }
   __syncthreads();
 
   const uint32_t N = a.N;
@@ -281,12 +284,17 @@ __device__ __forceinline__ void copy_chunk(const ExchangeArgs& a, uint32_t lane,
   }
 }
 
-template <bool kAffine>
+// kCap: each destination keeps its first `capacity` tuples in tuple order.
+// Then wrun holds ranks inside the destination (not slots), a tuple is kept
+// if its rank is below the capacity, and its slot is the segment start
+// (segl) plus the rank; a dropped tuple moves nothing and its slot_of is -1.
+template <bool kAffine, bool kCap>
 __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
   extern __shared__ uint32_t lds[];
   const uint32_t N = a.N;
-  uint32_t* wrun = lds;            // [kWaves][N]: next slot of each destination, per wave
-  uint32_t* tcnt = lds + kWaves * N;  // [N]: tuples of this tile per destination
+  uint32_t* wrun = lds;            // [kWaves][N]: next slot (kCap: rank) of each destination, per wave
+  uint32_t* tcnt = lds + kWaves * N;  // [N]: tuples of this tile per destination that are kept
+  uint32_t* segl = tcnt + N;          // [N] kCap: segment starts
   for (uint32_t i = threadIdx.x; i < kWaves * N; i += kBlock) wrun[i] = 0;
   __syncthreads();
 
@@ -308,8 +316,9 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
   // 2. first slot of each (wave, destination): segment start + this tile's
   //    start inside the segment + the counts of earlier waves
   for (uint32_t d = threadIdx.x; d < N; d += kBlock) {
-    const uint32_t base = (uint32_t)a.seg[d] + a.blk_base[(uint64_t)(blockIdx.x / a.scan_tiles) * N + d] +
-                          a.tile_base[(uint64_t)blockIdx.x * N + d];
+    const uint32_t rank0 = a.blk_base[(uint64_t)(blockIdx.x / a.scan_tiles) * N + d] +
+                           a.tile_base[(uint64_t)blockIdx.x * N + d];
+    const uint32_t base = kCap ? rank0 : (uint32_t)a.seg[d] + rank0;
     uint32_t run = base;
 #pragma unroll
     for (uint32_t ww = 0; ww < kWaves; ++ww) {
@@ -317,7 +326,12 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
       wrun[ww * N + d] = run;
       run += c;
     }
-    tcnt[d] = run - base;
+    if (kCap) {
+      tcnt[d] = min(run, a.capacity) - min(base, a.capacity);
+      segl[d] = (uint32_t)a.seg[d];
+    } else {
+      tcnt[d] = run - base;
+    }
   }
   __syncthreads();
 
@@ -333,17 +347,24 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
     const uint64_t peers = match_peers(d, valid_d, a.nbits);
     const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt(lane));
     int slot = 0;
-    if (valid_d) slot = (int)(mine[d] + rank);
-    // every lane has read mine[] before the group's leader advances it
-    if (valid_d && rank == 0) mine[d] = (uint32_t)slot + (uint32_t)__popcll(peers);
+    bool keep = valid_d;
+    if (valid_d) {
+      const uint32_t r = mine[d] + rank;  // kCap: rank inside d; else the slot
+      // every lane has read mine[] before the group's leader advances it
+      if (rank == 0) mine[d] = r + (uint32_t)__popcll(peers);
+      if (kCap) {
+        keep = r < a.capacity;
+        slot = (int)(segl[d] + r);
+      } else {
+        slot = (int)r;
+      }
+    }
     // a slot past the end can only come from dest changing between the
     // histogram and this pass; never write outside the output
-    const bool valid = valid_d && (uint64_t)slot < a.G;
-    if (valid_d && !valid) bad = true;
-    if (valid) {
-      if (a.src_index) a.src_index[slot] = (int32_t)g;
-      if (a.slot_of) a.slot_of[g] = slot;
-    }
+    const bool valid = keep && (uint64_t)slot < a.dst_rows;
+    if (keep && !valid) bad = true;
+    if (valid && a.src_index) a.src_index[slot] = (int32_t)g;
+    if (valid_d && a.slot_of) a.slot_of[g] = valid ? slot : -1;
     const uint32_t srow = valid ? (uint32_t)(g / a.fanout) : 0u;
     if (unit_bytes == 16u)
       copy_chunk<u32x4, kAffine>(a, lane, slot, srow, valid, v_units, v_shift, v_pow2);
@@ -454,7 +475,8 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
 
 }  // namespace
 
-size_t scatter_lds_bytes(uint32_t N) { return (size_t)(kWaves + 1) * N * sizeof(uint32_t); }
+// wrun and tcnt, plus segl with a capacity (MOE plans only: N <= 64)
+size_t scatter_lds_bytes(uint32_t N, bool cap) { return (size_t)(kWaves + (cap ? 2 : 1)) * N * sizeof(uint32_t); }
 
 hipError_t launch_hist(const ExchangeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_hist, dim3(a.num_tiles), dim3(kBlock), a.N * sizeof(uint32_t), s, a);
@@ -472,11 +494,16 @@ hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s) {
-  const size_t lds = scatter_lds_bytes(a.N);
-  if (a.a_kind == OP_AFFINE)
-    hipLaunchKernelGGL((k_scatter<true>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
+  const bool cap = a.capacity != 0;
+  const size_t lds = scatter_lds_bytes(a.N, cap);
+  if (cap && a.a_kind == OP_AFFINE)
+    hipLaunchKernelGGL((k_scatter<true, true>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
+  else if (cap)
+    hipLaunchKernelGGL((k_scatter<false, true>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
+  else if (a.a_kind == OP_AFFINE)
+    hipLaunchKernelGGL((k_scatter<true, false>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
   else
-    hipLaunchKernelGGL((k_scatter<false>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
+    hipLaunchKernelGGL((k_scatter<false, false>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
 

@@ -61,6 +61,7 @@ int validate_desc_more(const pw_plan_desc* d) {
       if (!d->w_router || !d->w1 || !d->w2) return fail(PW_ERR_INVALID, "MOE: w_router, w1 and w2 are required");
       if ((uint64_t)d->payload_elems * d->hidden * 2 > 0xffffffffull)
         return fail(PW_ERR_INVALID, "MOE: one expert weight must stay below 4 GiB");
+      if (d->capacity > 2 * tokens) return fail(PW_ERR_INVALID, "MOE: capacity above the tuple count");
       return PW_OK;
     }
     default:
@@ -138,23 +139,36 @@ void plan_release_kind(Plan* p) {
 }
 
 // -------------------------------------------------------------------- MOE
-int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done) {
+// Rows the dispatch can write at most: every tuple, or with a capacity C
+// per expert, E C if that is fewer.
+uint64_t moe_static_rows(const pw_plan_desc& d) {
+  const uint64_t S = d.num_src_shards ? d.num_src_shards : d.num_shards;
+  const uint64_t tuples = 2 * S * d.tuples_per_shard;
+  return d.capacity ? std::min<uint64_t>(tuples, (uint64_t)d.num_shards * d.capacity) : tuples;
+}
+
+int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host) {
   const pw_plan_desc& d = p->desc;
   const Layout& L = p->L;
   const uint32_t E = d.num_shards;
   const uint32_t S = d.num_src_shards ? d.num_src_shards : E;
   const uint64_t tokens = (uint64_t)S * d.tuples_per_shard;
   const uint32_t D = d.payload_elems;
+  const bool outs = ph != Phase::kBegin;  // the second half writes dst, b_out and result
+  const uint64_t rows = ph == Phase::kEnd ? p->open.rows : moe_static_rows(d);
   if (!io->src.base || io->src.num_tuples != tokens || io->src.elems_per_tuple != D || io->src.dtype != PW_BF16)
     return fail(PW_ERR_INVALID, "src must be %llu tokens x %u bf16", (unsigned long long)tokens, D);
-  if (!io->dst.base || io->dst.num_tuples < 2 * tokens || io->dst.elems_per_tuple != D || io->dst.dtype != PW_BF16)
-    return fail(PW_ERR_INVALID, "dst must hold 2 x %llu dispatched rows of %u bf16", (unsigned long long)tokens, D);
-  if (!io->b_out || !io->result) return fail(PW_ERR_INVALID, "b_out (expert outputs) and result are required");
+  if (outs && (!io->dst.base || io->dst.num_tuples < rows || io->dst.elems_per_tuple != D || io->dst.dtype != PW_BF16))
+    return fail(PW_ERR_INVALID, "dst must hold %llu dispatched rows of %u bf16", (unsigned long long)rows, D);
+  if (outs && (!io->b_out || !io->result)) return fail(PW_ERR_INVALID, "b_out (expert outputs) and result are required");
   if (io->dest) return fail(PW_ERR_INVALID, "MOE routes with its router: dest must be NULL");
-  const uintptr_t al = (uintptr_t)io->src.base | (uintptr_t)io->dst.base | (uintptr_t)io->b_out | (uintptr_t)io->result;
+  const uintptr_t al = outs ? ((uintptr_t)io->src.base | (uintptr_t)io->dst.base | (uintptr_t)io->b_out |
+                               (uintptr_t)io->result)
+                            : (uintptr_t)io->src.base;
   if (al & 15u) return fail(PW_ERR_INVALID, "buffers must be 16-byte aligned");
-  int st = p->begin_call(s);
+  int st = ph == Phase::kEnd ? check_end(p, io) : PW_OK;
   if (st) return st;
+  if ((st = p->begin_call(s))) return st;
   unsigned char* base = p->base();
 
   MoeArgs m{};
@@ -174,7 +188,7 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done)
   m.d = D;
   m.hidden = d.hidden;
   m.E = E;
-  m.max_row_blocks = (uint32_t)((2 * tokens + 255) / 256 + E);
+  m.max_row_blocks = (uint32_t)((moe_static_rows(d) + 255) / 256 + E);
   m.seg = reinterpret_cast<const int64_t*>(base + L.seg);
   m.rb_start = reinterpret_cast<uint32_t*>(base + L.rb_start);
   m.b_done = reinterpret_cast<uint32_t*>(base + L.b_done);
@@ -192,6 +206,8 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done)
   a.offsets_out = io->dst.shard_offsets;
   a.b_out = nullptr;
   a.G = L.G;
+  a.dst_rows = outs ? std::min<uint64_t>(io->dst.num_tuples, L.G) : 0;  // also bounds src_index (G entries)
+  a.capacity = d.capacity;
   a.T = 2 * d.tuples_per_shard;
   a.N = E;
   a.num_src = S;
@@ -225,10 +241,14 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done)
     p->launch_end(s);                  \
     if (e != hipSuccess) return hip_fail(e, "launch " label); \
   } while (0)
-  PW_STEP("router", launch_router(m, s));
-  if (io->counts) PW_STEP("src_counts", launch_src_counts(a, s));
-  PW_STEP("hist", launch_hist(a, s));
-  PW_STEP("scan", launch_scan(a, s));
+  if (ph != Phase::kEnd) {
+    PW_STEP("router", launch_router(m, s));
+    if (io->counts) PW_STEP("src_counts", launch_src_counts(a, s));
+    PW_STEP("hist", launch_hist(a, s));
+    PW_STEP("scan", launch_scan(a, s));
+    if (ph == Phase::kBegin) return finish_begin(p, io, s, offsets_host);
+  }
+  p->open.active = false;
   PW_STEP("scatter", launch_scatter(a, s));
   PW_STEP("moe_prefix", launch_moe_prefix(m, s));
   PW_STEP("ffn1", launch_ffn(m, false, s));

@@ -125,7 +125,7 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
         L.experts = c.take(tokens * d.top_k * 4);
         L.gates = c.take(tokens * d.top_k * 4);
         L.slot_of = c.take(L.G * 4);
-        L.hidden_act = c.take(L.G * (uint64_t)d.hidden * 2);
+        L.hidden_act = c.take(moe_static_rows(d) * (uint64_t)d.hidden * 2);
         L.rb_start = c.take((size_t)(N + 1) * 4);
         L.b_done = c.take((size_t)N * 4);
         L.w1t = c.take((size_t)N * d.hidden * d.payload_elems * 2);
@@ -174,6 +174,7 @@ int validate_desc(const pw_plan_desc* d) {
   if (d->abi_version != PW_ABI_VERSION)
     return fail(PW_ERR_INVALID, "abi_version %u != %u", d->abi_version, PW_ABI_VERSION);
   if (d->flags & ~(PW_FLAG_TRACE | PW_FLAG_TIMING)) return fail(PW_ERR_INVALID, "unknown flags 0x%x", d->flags);
+  if (d->capacity && d->kind != PW_GRAPH_MOE) return fail(PW_ERR_INVALID, "capacity is for MOE plans only");
   switch (d->kind) {
     case PW_GRAPH_EXCHANGE: {
       // the scatter keeps 5 words per destination in LDS (160 KiB per CU)
@@ -361,24 +362,62 @@ static int status_to_code(uint32_t st) {
 // ------------------------------------------------------------ exchange call
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done) {
+// After the first half of a split step: wait for it, hand the segment
+// offsets to the host and remember the inputs the second half must match.
+int finish_begin(Plan* p, const pw_exchange_io* io, hipStream_t s, int64_t* offsets_host) {
+  const uint32_t N = p->desc.num_shards;
+  const int64_t* seg = reinterpret_cast<const int64_t*>(p->base() + p->L.seg);
+  hipError_t e = hipMemcpyAsync(offsets_host, seg, (N + 1) * sizeof(int64_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the segment offsets");
+  Plan::Open& o = p->open;
+  o.active = true;
+  o.rows = (uint64_t)offsets_host[N];
+  o.src = io->src.base;
+  o.dest = io->dest;
+  o.logits = io->logits;
+  o.experts = io->experts;
+  o.gates = io->gates;
+  o.counts = io->counts;
+  return PW_OK;
+}
+
+// The second half of a split step must name the inputs of the first.
+int check_end(Plan* p, const pw_exchange_io* io) {
+  const Plan::Open& o = p->open;
+  if (!o.active) return fail(PW_ERR_STATE, "pw_exchange_end without pw_exchange_begin");
+  if (io->src.base != o.src || io->dest != o.dest || io->logits != o.logits || io->experts != o.experts ||
+      io->gates != o.gates || io->counts != o.counts)
+    return fail(PW_ERR_INVALID, "pw_exchange_end must name the src, dest, logits, experts, gates and counts of begin");
+  if (io->dst.num_tuples < o.rows) return fail(PW_ERR_INVALID, "dst holds %llu rows, the step writes %llu",
+                                               (unsigned long long)io->dst.num_tuples, (unsigned long long)o.rows);
+  return PW_OK;
+}
+
+int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host) {
   const pw_plan_desc& d = p->desc;
   const Layout& L = p->L;
   const uint32_t N = d.num_shards;
   const uint32_t S = d.num_src_shards ? d.num_src_shards : N;
   const uint32_t esz = d.dtype == PW_F32 ? 4 : 2;
   const uint32_t row = esz * d.payload_elems;
-  if (L.G && (!io->src.base || !io->dest || !io->dst.base)) return fail(PW_ERR_INVALID, "src, dest and dst are required");
+  const bool need_dst = ph != Phase::kBegin;
+  if (L.G && (!io->src.base || !io->dest || (need_dst && !io->dst.base)))
+    return fail(PW_ERR_INVALID, "src, dest and dst are required");
   if (io->src.num_tuples != L.G || io->src.elems_per_tuple != d.payload_elems || io->src.dtype != d.dtype)
     return fail(PW_ERR_INVALID, "src does not match the plan (tuples %llu, elems %u, dtype %u)",
                 (unsigned long long)io->src.num_tuples, io->src.elems_per_tuple, io->src.dtype);
   if (io->src.shard_offsets) return fail(PW_ERR_UNSUPPORTED, "non-uniform source shards");
-  if (io->dst.num_tuples < L.G || io->dst.elems_per_tuple != d.payload_elems || io->dst.dtype != d.dtype)
+  if (need_dst && (io->dst.num_tuples < (ph == Phase::kEnd ? p->open.rows : L.G) ||
+                   io->dst.elems_per_tuple != d.payload_elems || io->dst.dtype != d.dtype))
     return fail(PW_ERR_INVALID, "dst does not match the plan");
-  if (!aligned16(io->src.base) || !aligned16(io->dst.base)) return fail(PW_ERR_INVALID, "src/dst must be 16-byte aligned");
-  if (d.b_op.kind != PW_OP_IDENTITY && !io->b_out) return fail(PW_ERR_INVALID, "b_out is required when B is not IDENTITY");
-  int st = p->begin_call(s);
+  if (!aligned16(io->src.base) || (need_dst && !aligned16(io->dst.base)))
+    return fail(PW_ERR_INVALID, "src/dst must be 16-byte aligned");
+  if (need_dst && d.b_op.kind != PW_OP_IDENTITY && !io->b_out)
+    return fail(PW_ERR_INVALID, "b_out is required when B is not IDENTITY");
+  int st = ph == Phase::kEnd ? check_end(p, io) : PW_OK;
   if (st) return st;
+  if ((st = p->begin_call(s))) return st;
 
   ExchangeArgs a{};
   auto* base = static_cast<unsigned char*>(p->ws);
@@ -391,6 +430,8 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   a.offsets_out = io->dst.shard_offsets;
   a.b_out = io->b_out;
   a.G = L.G;
+  a.dst_rows = std::min<uint64_t>(io->dst.num_tuples, L.G);  // also bounds src_index (G entries)
+  a.capacity = 0;
   a.T = d.tuples_per_shard;
   a.N = N;
   a.num_src = S;
@@ -416,20 +457,24 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
 
   hipError_t e = hipSuccess;
-  if (io->counts) {
-    p->launch_begin("src_counts", s);
-    e = launch_src_counts(a, s);
+  if (ph != Phase::kEnd) {
+    if (io->counts) {
+      p->launch_begin("src_counts", s);
+      e = launch_src_counts(a, s);
+      p->launch_end(s);
+      if (e != hipSuccess) return hip_fail(e, "launch src_counts");
+    }
+    p->launch_begin("hist", s);
+    e = launch_hist(a, s);
     p->launch_end(s);
-    if (e != hipSuccess) return hip_fail(e, "launch src_counts");
+    if (e != hipSuccess) return hip_fail(e, "launch hist");
+    p->launch_begin("scan", s);
+    e = launch_scan(a, s);
+    p->launch_end(s);
+    if (e != hipSuccess) return hip_fail(e, "launch scan");
+    if (ph == Phase::kBegin) return finish_begin(p, io, s, offsets_host);
   }
-  p->launch_begin("hist", s);
-  e = launch_hist(a, s);
-  p->launch_end(s);
-  if (e != hipSuccess) return hip_fail(e, "launch hist");
-  p->launch_begin("scan", s);
-  e = launch_scan(a, s);
-  p->launch_end(s);
-  if (e != hipSuccess) return hip_fail(e, "launch scan");
+  p->open.active = false;
   p->launch_begin("scatter", s);
   e = launch_scatter(a, s);
   p->launch_end(s);
@@ -538,15 +583,32 @@ int pw_plan_destroy(pw_plan_t plan) {
   return PW_OK;
 }
 
-int pw_exchange(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done) {
+static int exchange_phase(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done, Phase ph,
+                          int64_t* offsets_host) {
   g_last_error.clear();
   Plan* p = reinterpret_cast<Plan*>(plan);
   if (!is_live(p)) return fail(PW_ERR_STATE, "not a live plan");
   if (!io) return fail(PW_ERR_INVALID, "io is NULL");
+  if (ph == Phase::kBegin && !offsets_host) return fail(PW_ERR_INVALID, "offsets_host is NULL");
   std::lock_guard<std::mutex> lk(p->mu);
-  if (p->desc.kind == PW_GRAPH_EXCHANGE) return run_exchange(p, io, static_cast<hipStream_t>(stream), done);
-  if (p->desc.kind == PW_GRAPH_MOE) return run_moe(p, io, static_cast<hipStream_t>(stream), done);
-  return fail(PW_ERR_INVALID, "pw_exchange needs an EXCHANGE or MOE plan");
+  if (ph != Phase::kEnd && p->open.active) return fail(PW_ERR_STATE, "a split step is open: call pw_exchange_end first");
+  if (ph == Phase::kEnd && !p->open.active) return fail(PW_ERR_STATE, "pw_exchange_end without pw_exchange_begin");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->desc.kind == PW_GRAPH_EXCHANGE) return run_exchange(p, io, s, done, ph, offsets_host);
+  if (p->desc.kind == PW_GRAPH_MOE) return run_moe(p, io, s, done, ph, offsets_host);
+  return fail(PW_ERR_INVALID, "an EXCHANGE or MOE plan is needed");
+}
+
+int pw_exchange(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done) {
+  return exchange_phase(plan, io, stream, done, Phase::kAll, nullptr);
+}
+
+int pw_exchange_begin(pw_plan_t plan, const pw_exchange_io* io, void* stream, int64_t* offsets_host) {
+  return exchange_phase(plan, io, stream, nullptr, Phase::kBegin, offsets_host);
+}
+
+int pw_exchange_end(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done) {
+  return exchange_phase(plan, io, stream, done, Phase::kEnd, nullptr);
 }
 
 int pw_chain_run(pw_plan_t plan, uint64_t steps, pw_sharded_buf* state, void* aux, void* stream, pw_future_t* done) {

@@ -31,11 +31,13 @@ struct ExchangeArgs {
   const int32_t* dest;        // [G]
   unsigned char* dst;         // [G] rows, exchange order
   int32_t* src_index;         // [G] or null
-  int32_t* slot_of;           // [G] inverse of src_index or null
+  int32_t* slot_of;           // [G] inverse of src_index (-1: dropped by the capacity) or null
   int32_t* counts;            // [num_src][N] or null
   int64_t* offsets_out;       // [N+1] or null
   void* b_out;                // B output or null
   uint64_t G;                 // tuples
+  uint64_t dst_rows;          // rows dst can hold, at most G (slots past it are never written)
+  uint32_t capacity;          // tuples kept per destination, first in tuple order (0 = all)
   uint64_t T;                 // tuples per source shard
   uint32_t N;                 // destinations
   uint32_t num_src;
@@ -107,7 +109,7 @@ struct MoeArgs {
   float* logits;           // [tokens][E] or null
   int32_t* experts;        // [tokens][2]
   float* gates;            // [tokens][2]
-  int32_t* slot_of;        // [2 tokens] dispatched slot of tuple g
+  int32_t* slot_of;        // [2 tokens] dispatched slot of tuple g, -1 if dropped
   uint64_t tokens;
   uint32_t d, hidden, E;
   uint32_t max_row_blocks;  // upper bound of the expert row blocks (grid sizing)
@@ -125,7 +127,7 @@ hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_src_counts(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_b(const ExchangeArgs& a, hipStream_t s);
-size_t scatter_lds_bytes(uint32_t N);
+size_t scatter_lds_bytes(uint32_t N, bool cap);
 // mode: 0 chained (one launch, all steps), 1 one node (OpByOp), 2 fused.
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);
 hipError_t launch_pipeline(const PipeArgs& a, uint32_t grid, hipStream_t s);

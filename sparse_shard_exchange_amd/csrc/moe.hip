@@ -200,7 +200,9 @@ __global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a) {
 }
 
 // out[t] = bf16(g0 * Y[slot(2t)] + g1 * Y[slot(2t + 1)]), fp32 sum with the
-// top-1 term first; one wave per token at a time, 16-byte chunks. The grid is
+// top-1 term first; a tuple dropped by the expert capacity (slot -1) adds
+// nothing (its row is not read); one wave per token at a time, 16-byte
+// chunks. The grid is
 // bounded (grid-stride over tokens): every workgroup adds once to the done
 // counter, and adds to one address serialize at the memory side (one per
 // 4-token workgroup cost ~0.3 ms at 131072 tokens).
@@ -215,19 +217,21 @@ __global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
     ok = __shfl((int)ok, 0, 64) != 0;
     if (!ok) continue;  // uniform per wave
     const float g0 = a.gates[t * 2], g1 = a.gates[t * 2 + 1];
-    const bf16x8* y0 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)a.slot_of[t * 2] * a.d);
-    const bf16x8* y1 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)a.slot_of[t * 2 + 1] * a.d);
+    const int s0 = a.slot_of[t * 2], s1 = a.slot_of[t * 2 + 1];  // wave-uniform
+    const bf16x8* y0 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)max(s0, 0) * a.d);
+    const bf16x8* y1 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)max(s1, 0) * a.d);
     bf16x8* o = reinterpret_cast<bf16x8*>(a.out + t * a.d);
     // two chunks of each row per lane per pass: all four loads in flight
     // before the first is used (d = 1024 is exactly one pass)
     const uint32_t nch = a.d / 8;
     for (uint32_t ch = lane; ch < nch; ch += 128) {
       const bool two = ch + 64 < nch;
-      const bf16x8 u0 = y0[ch], v0 = y1[ch];
-      bf16x8 u1 = {}, v1 = {};
+      bf16x8 u0 = {}, v0 = {}, u1 = {}, v1 = {};
+      if (s0 >= 0) u0 = y0[ch];
+      if (s1 >= 0) v0 = y1[ch];
       if (two) {
-        u1 = y0[ch + 64];
-        v1 = y1[ch + 64];
+        if (s0 >= 0) u1 = y0[ch + 64];
+        if (s1 >= 0) v1 = y1[ch + 64];
       }
       bf16x8 r0, r1;
 #pragma unroll

@@ -69,6 +69,19 @@ struct Plan {
 
   void* kind_state = nullptr;  // per-kind host state
 
+  // Between pw_exchange_begin and pw_exchange_end: the inputs begin was
+  // given and the output rows it reported.
+  struct Open {
+    bool active = false;
+    uint64_t rows = 0;
+    const void* src = nullptr;
+    const int32_t* dest = nullptr;
+    float* logits = nullptr;
+    int32_t* experts = nullptr;
+    float* gates = nullptr;
+    int32_t* counts = nullptr;
+  } open;
+
   void launch_begin(const char* name, hipStream_t s);
   void launch_end(hipStream_t s);
   hipEvent_t get_event();
@@ -93,7 +106,15 @@ int future_check(pw_future_t f);    // latched device status of a call known to 
 int validate_desc_more(const pw_plan_desc* d);
 int plan_init_kind(Plan* p);
 void plan_release_kind(Plan* p);
-int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done);
+// A step whole (kAll), or split where its output sizes become known: kBegin
+// runs A, the histogram and the scan and returns the segment offsets to the
+// host; kEnd runs the rest.
+enum class Phase { kAll, kBegin, kEnd };
+int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host);
+int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host);
+int finish_begin(Plan* p, const pw_exchange_io* io, hipStream_t s, int64_t* offsets_host);
+uint64_t moe_static_rows(const pw_plan_desc& d);  // dispatched rows at most (graphs.cpp)
+int check_end(Plan* p, const pw_exchange_io* io);
 int run_chain(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStream_t s, pw_future_t* done);
 int run_pipeline(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStream_t s, pw_future_t* done);
 
