@@ -352,6 +352,59 @@ def moe_capacity_bench(pw, torch, pw_inputs, steps=5):
     return out
 
 
+def store_bench(pw, torch, pw_inputs, point_s=1.0, clients=8):
+    """Backpressure of the HBM object store (PATHWAYS page, section 4.6).
+    Each client thread loops: take its program's state buffer from the store
+    (waiting if the store is full), copy its input in, run a chained program
+    of ~0.3 ms on it, free the buffer stream-ordered right after the launch,
+    wait for the result. The store holds `slots` such buffers; with fewer
+    slots than clients, allocations stall instead of failing. Programs/s and
+    the store's stall counters per slot count."""
+    import threading
+    n, e, d = 256, 128, 503
+    nbytes = n * e * 4
+    x0 = torch.from_numpy(pw_inputs.chain_state(n, e)).cuda()
+    out = {"program": f"chained run of {d} steps on {n} shards x {e} fp32; state ({nbytes} B) from the store",
+           "clients": clients, "by_slots": {}}
+    chains = [pw.Chain(n, e) for _ in range(clients)]
+    for slots in (1, 2, 4, 8):
+        st = pw.Store(slots * nbytes)
+        stop = [False]
+        done = [0] * clients
+        errors = []
+
+        def client(c):
+            try:
+                while not stop[0]:
+                    obj, ptr = st.alloc(nbytes, owner=c, timeout_ns=10_000_000_000)
+                    state = st.tensor(ptr, (n, e))
+                    state.copy_(x0)
+                    f = chains[c].run(state, d)
+                    st.free(obj)
+                    pw.future_wait(f, 10_000_000_000)
+                    done[c] += 1
+            except Exception as ex:  # reported in the result
+                errors.append(repr(ex))
+
+        ths = [threading.Thread(target=client, args=(c,)) for c in range(clients)]
+        t0 = time.perf_counter()
+        for th in ths:
+            th.start()
+        time.sleep(point_s)
+        stop[0] = True
+        for th in ths:
+            th.join()
+        wall = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        s = st.stats()
+        out["by_slots"][slots] = {"programs_per_s": sum(done) / wall, "programs": sum(done), "stalls": s["stalls"],
+                                  "stalled_ms_total": s["stalled_ms"], "errors": errors[:3]}
+        st.destroy()
+    for ch in chains:
+        ch.plan.destroy()
+    return out
+
+
 def reference_bench(torch, iters=10):
     """Context, not the product path: the vendor BLAS (hipBLASLt through
     torch.matmul) on the shapes of the two GEMM rows, and torch's elementwise
@@ -455,6 +508,7 @@ def main():
                     help="also measure per-node cost against program length for the four dispatch modes")
     ap.add_argument("--moe-capacity", action="store_true",
                     help="MoE with an expert capacity: one static call vs route, host wait, exact allocation, rest")
+    ap.add_argument("--store", action="store_true", help="object-store backpressure: client programs vs store slots")
     ap.add_argument("--multi-tenant", action="store_true",
                     help="throughput of concurrent clients and proportional shares through the scheduler")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -569,6 +623,10 @@ def main():
     if args.dispatch_study:
         log("dispatch study")
         result["dispatch_study"] = dispatch_study(pw, torch, pw_inputs)
+
+    if args.store:
+        log("object store backpressure")
+        result["store"] = store_bench(pw, torch, pw_inputs)
 
     if args.multi_tenant:
         log("multi-tenant scheduler")

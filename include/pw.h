@@ -19,8 +19,9 @@
  * Conventions for every entry point:
  *   - Every pointer named "device" is device memory the CALLER owns and keeps
  *     alive until the future returned by the call has fired; the library
- *     never allocates, frees or retains device memory of its own. Host
- *     structs passed in are read during the call only.
+ *     never allocates, frees or retains device memory of its own, except
+ *     the one extent an object store (pw_store_*) takes when the caller
+ *     creates it. Host structs passed in are read during the call only.
  *   - A stream argument is a hipStream_t passed as void* (NULL = the null
  *     stream). Calls are stream ordered and return before the device work
  *     finishes.
@@ -384,6 +385,62 @@ int pw_sched_records(pw_sched_t s, pw_sched_record* out, size_t capacity, size_t
 /* Wait for every queued and running program, stop the thread, destroy the
  * stream. Tickets not yet waited are dropped. */
 int pw_sched_destroy(pw_sched_t s);
+
+/* ======================================================================== *
+ * HBM object store (PATHWAYS page, section 4.6 "Data management"): buffers
+ * in device memory named by handle and labelled with an owner, so that all
+ * buffers of a failed client or program can be released at once; an
+ * allocation that does not fit because other programs' buffers occupy the
+ * memory stalls (backpressure) instead of failing.
+ *
+ * One extent of device memory, taken by pw_store_create. Sizes round up to
+ * 256 bytes; placement is first fit by address and freed extents merge with
+ * free neighbours; waiting requests are served in arrival order (a later
+ * request never overtakes a waiting one). Frees are stream ordered: the
+ * extent is reused only after the work enqueued on the given stream before
+ * the free has finished. Every call may come from any thread.
+ * ======================================================================== */
+typedef struct pw_store_s* pw_store_t;
+
+typedef struct {
+  uint64_t base;          /* device address of the extent                    */
+  uint64_t capacity;      /* bytes                                            */
+  uint64_t in_use;        /* bytes held by live objects                       */
+  uint64_t pending_free;  /* bytes freed whose stream work is still running   */
+  uint64_t largest_free;  /* longest free extent now                          */
+  uint64_t objects;       /* live objects                                     */
+  uint64_t waiting;       /* allocations waiting now                          */
+  uint64_t stalls;        /* allocations that had to wait, so far             */
+  double stalled_ms;      /* host time they spent waiting, so far             */
+} pw_store_stats;
+
+/* Take `bytes` (rounded down to 256) of device memory on the current device.
+ * PW_ERR_NOMEM if the device cannot provide it. */
+int pw_store_create(size_t bytes, pw_store_t* out);
+
+/* Allocate `bytes` for `owner`. If they do not fit now, wait until frees
+ * make room (backpressure) for up to timeout_ns (< 0: no limit, 0: no wait);
+ * PW_ERR_NOMEM on expiry, and at once if bytes exceed the whole store.
+ * *object receives the handle (never 0), *device_ptr the address (256-byte
+ * aligned; contents undefined). */
+int pw_store_alloc(pw_store_t s, size_t bytes, uint32_t owner, int64_t timeout_ns, uint64_t* object,
+                   void** device_ptr);
+
+/* Free an object; its memory is reused once the work enqueued on `stream`
+ * (hipStream_t as void*, NULL = null stream) before this call has finished.
+ * PW_ERR_STATE if the handle is not live. */
+int pw_store_free(pw_store_t s, uint64_t object, void* stream);
+
+/* Free every live object of `owner` (e.g. after that client failed), stream
+ * ordered as pw_store_free; *released (nullable) receives how many. */
+int pw_store_release_owner(pw_store_t s, uint32_t owner, void* stream, uint64_t* released);
+
+/* Occupancy and backpressure counters. */
+int pw_store_get_stats(pw_store_t s, pw_store_stats* out);
+
+/* Release the extent (waits for frees in flight). Live objects become
+ * invalid. PW_ERR_STATE while an allocation is waiting. */
+int pw_store_destroy(pw_store_t s);
 
 #ifdef __cplusplus
 }

@@ -78,6 +78,14 @@ class pw_kernel_time(C.Structure):
 PW_PROG_CHAIN, PW_PROG_EXCHANGE = 0, 1
 
 
+class pw_store_stats(C.Structure):
+    _fields_ = [
+        ("base", C.c_uint64), ("capacity", C.c_uint64), ("in_use", C.c_uint64), ("pending_free", C.c_uint64),
+        ("largest_free", C.c_uint64), ("objects", C.c_uint64), ("waiting", C.c_uint64), ("stalls", C.c_uint64),
+        ("stalled_ms", C.c_double),
+    ]
+
+
 class pw_program(C.Structure):
     _fields_ = [
         ("kind", C.c_uint32), ("cost", C.c_uint32), ("plan", C.c_void_p), ("steps", C.c_uint64),
@@ -117,6 +125,13 @@ _SIGNATURES = {
     "pw_sched_hold": (C.c_int, [C.c_void_p, C.c_int]),
     "pw_sched_records": (C.c_int, [C.c_void_p, C.POINTER(pw_sched_record), C.c_size_t, C.POINTER(C.c_size_t)]),
     "pw_sched_destroy": (C.c_int, [C.c_void_p]),
+    "pw_store_create": (C.c_int, [C.c_size_t, C.POINTER(C.c_void_p)]),
+    "pw_store_alloc": (C.c_int, [C.c_void_p, C.c_size_t, C.c_uint32, C.c_int64, C.POINTER(C.c_uint64),
+                                 C.POINTER(C.c_void_p)]),
+    "pw_store_free": (C.c_int, [C.c_void_p, C.c_uint64, C.c_void_p]),
+    "pw_store_release_owner": (C.c_int, [C.c_void_p, C.c_uint32, C.c_void_p, C.POINTER(C.c_uint64)]),
+    "pw_store_get_stats": (C.c_int, [C.c_void_p, C.POINTER(pw_store_stats)]),
+    "pw_store_destroy": (C.c_int, [C.c_void_p]),
 }
 
 
@@ -526,5 +541,61 @@ class Sched:
         try:
             if getattr(self, "handle", None):
                 lib.pw_sched_destroy(self.handle)
+        except Exception:
+            pass
+
+
+class _DeviceArray:
+    """A borrowed view of device memory for torch.as_tensor (array interface
+    of version 2); the memory stays the store's."""
+
+    def __init__(self, ptr, shape, typestr):
+        self.__cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr, "data": (ptr, False),
+                                         "version": 2, "strides": None}
+
+
+class Store:
+    """HBM object store: owner-labelled device buffers with backpressure."""
+
+    _TYPESTR = {"float32": "<f4", "int32": "<i4", "int64": "<i8", "uint8": "|u1"}
+
+    def __init__(self, nbytes):
+        h = C.c_void_p()
+        check(lib.pw_store_create(nbytes, C.byref(h)))
+        self.handle = h
+
+    def alloc(self, nbytes, owner=0, timeout_ns=-1):
+        """(object handle, device address)."""
+        obj, ptr = C.c_uint64(0), C.c_void_p()
+        check(lib.pw_store_alloc(self.handle, nbytes, owner, timeout_ns, C.byref(obj), C.byref(ptr)))
+        return obj.value, ptr.value
+
+    def tensor(self, ptr, shape, dtype="float32"):
+        """A torch tensor over store memory (borrowed: valid until freed)."""
+        import torch
+        return torch.as_tensor(_DeviceArray(ptr, shape, self._TYPESTR[dtype]), device="cuda")
+
+    def free(self, obj, stream=None):
+        check(lib.pw_store_free(self.handle, obj, _stream(stream)))
+
+    def release_owner(self, owner, stream=None) -> int:
+        n = C.c_uint64(0)
+        check(lib.pw_store_release_owner(self.handle, owner, _stream(stream), C.byref(n)))
+        return n.value
+
+    def stats(self) -> dict:
+        st = pw_store_stats()
+        check(lib.pw_store_get_stats(self.handle, C.byref(st)))
+        return {name: getattr(st, name) for name, _ in st._fields_}
+
+    def destroy(self):
+        if self.handle:
+            check(lib.pw_store_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                lib.pw_store_destroy(self.handle)
         except Exception:
             pass

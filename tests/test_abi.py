@@ -44,6 +44,20 @@ def test_struct_sizes_match_the_header_layout():
     assert C.sizeof(pw.pw_exchange_io) == 144
     assert C.sizeof(pw.pw_program) == 216
     assert C.sizeof(pw.pw_sched_record) == 40
+    assert C.sizeof(pw.pw_store_stats) == 72
+
+
+def test_store_argument_errors_need_no_device():
+    h = C.c_void_p(0)
+    assert pw.lib.pw_store_create(100, C.byref(h)) == pw.PW_ERR_INVALID   # below 256 bytes
+    assert pw.lib.pw_store_create(1 << 20, None) == pw.PW_ERR_INVALID
+    obj, ptr = C.c_uint64(0), C.c_void_p()
+    assert pw.lib.pw_store_alloc(None, 256, 0, 0, C.byref(obj), C.byref(ptr)) == pw.PW_ERR_INVALID
+    assert pw.lib.pw_store_free(None, 1, None) == pw.PW_ERR_INVALID
+    assert pw.lib.pw_store_release_owner(None, 1, None, None) == pw.PW_ERR_INVALID
+    st = pw.pw_store_stats()
+    assert pw.lib.pw_store_get_stats(None, C.byref(st)) == pw.PW_ERR_INVALID
+    assert pw.lib.pw_store_destroy(None) == pw.PW_ERR_INVALID
 
 
 def test_scheduler_argument_errors_need_no_device():
