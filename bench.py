@@ -254,32 +254,41 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 def pipeline_bench(pw, torch, pw_inputs, passes=3):
     """16-stage GPipe pipeline, 64 microbatches of 2048 x 1024 bf16, each stage a
-    1024 x 1024 GEMM + GELU: 4.398 TFLOP per pass, one launch per pass."""
+    1024 x 1024 GEMM + GELU: 4.398 TFLOP per pass, one launch per pass. Timed in
+    both claim orders: GPipe lock-step ticks, and stage by stage within windows
+    of 16 microbatches (PW_FLAG_STAGE_WINDOWS; same dependencies and results)."""
     s, m, rows, d = 16, 64, 2048, 1024
     inp = pw_inputs.pipeline(s, m, rows, d)
     w = inp.w.cuda()
     x = inp.x.cuda()
     acts = torch.empty((s, m, rows, d), dtype=torch.bfloat16, device="cuda")
-    pipe = pw.Pipeline(w, m, rows, flags=pw.PW_FLAG_TIMING)
-    pw.future_wait(pipe.run(x, acts), 60_000_000_000)
-    pipe.plan.reset_times()
-    torch.cuda.synchronize()
-    st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(passes):
-        f = pipe.run(x, acts)
-    e1.record(st)
-    torch.cuda.synchronize()
-    pw.future_wait(f, 60_000_000_000)
-    ms = e0.elapsed_time(e1) / passes
-    kt = pipe.plan.kernel_times()
-    kms = kt["pipeline"][1] / kt["pipeline"][0]
     flops = 2.0 * s * m * rows * d * d
-    tf = flops / (kms * 1e-3) / 1e12
-    return {"workload": "GPipe 16 stages x 64 microbatches of 2048x1024 bf16, stage = 1024x1024 GEMM + GELU",
-            "ms_per_pass": ms, "kernel_ms": kms, "tflops": tf, "frac_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS,
-            "flop_per_pass": flops, "gpipe_bubble_lockstep": (s - 1) / (m + s - 1)}
+
+    def timed(extra_flags):
+        pipe = pw.Pipeline(w, m, rows, flags=pw.PW_FLAG_TIMING | extra_flags)
+        pw.future_wait(pipe.run(x, acts), 60_000_000_000)
+        pipe.plan.reset_times()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(passes):
+            f = pipe.run(x, acts)
+        e1.record(st)
+        torch.cuda.synchronize()
+        pw.future_wait(f, 60_000_000_000)
+        ms = e0.elapsed_time(e1) / passes
+        kt = pipe.plan.kernel_times()
+        kms = kt["pipeline"][1] / kt["pipeline"][0]
+        tf = flops / (kms * 1e-3) / 1e12
+        return {"ms_per_pass": ms, "kernel_ms": kms, "tflops": tf, "frac_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+
+    out = {"workload": "GPipe 16 stages x 64 microbatches of 2048x1024 bf16, stage = 1024x1024 GEMM + GELU",
+           "order": "lock-step ticks"}
+    out.update(timed(0))
+    out["stage_windows"] = timed(pw.PW_FLAG_STAGE_WINDOWS)
+    out.update({"flop_per_pass": flops, "gpipe_bubble_lockstep": (s - 1) / (m + s - 1)})
+    return out
 
 
 def moe_bench(pw, torch, pw_inputs, steps=3):

@@ -94,6 +94,9 @@ typedef enum {
 /* ---- plan flags ----------------------------------------------------------- */
 #define PW_FLAG_TRACE   0x1u /* record a device timestamp for every future fire          */
 #define PW_FLAG_TIMING  0x2u /* record HIP events around every kernel (pw_plan_kernel_times) */
+#define PW_FLAG_STAGE_WINDOWS 0x4u /* PIPELINE: claim tiles stage by stage within windows of 16
+                                      microbatches instead of in GPipe lock-step ticks; the same
+                                      dependencies and per-stage microbatch order, fewer waits  */
 
 /* ---- plan descriptor ------------------------------------------------------ */
 typedef struct {

@@ -73,22 +73,34 @@ int plan_init_kind(Plan* p) {
   auto* ks = new KindState();
   p->kind_state = ks;
   if (p->desc.kind == PW_GRAPH_PIPELINE) {
-    // Items in GPipe lock-step order (tick t = s + m ascending, then stage)
-    // are dealt round-robin to one queue per XCD; an item's tiles (row block,
-    // then column block) stay together in its queue. Uploaded once.
+    // Items in GPipe lock-step order (tick t = s + m ascending, then stage),
+    // or with PW_FLAG_STAGE_WINDOWS stage by stage within windows of
+    // kWindow microbatches (item (s, m) then comes a whole window of items
+    // after (s - 1, m), so its input is long complete, and a window's
+    // activations stay in the last-level cache), are dealt round-robin to
+    // one queue per XCD; an item's tiles (row block, then column block) stay
+    // together in its queue. Both orders keep each stage's microbatches in
+    // ascending order and every item after its predecessor stage. Uploaded once.
     const pw_plan_desc& d = p->desc;
     const uint32_t S = d.num_shards, M = d.microbatches;
     const uint32_t RB = (uint32_t)((d.tuples_per_shard + 255) / 256), CT = d.payload_elems / 256;
     std::vector<std::vector<uint32_t>> queues(kQueues);
     uint32_t item = 0;
-    for (uint32_t t = 0; t + 1 < S + M; ++t)
-      for (uint32_t s = 0; s < S; ++s) {
-        if (t < s || t - s >= M) continue;
-        const uint32_t m = t - s;
-        auto& q = queues[item++ % kQueues];
-        for (uint32_t r = 0; r < RB; ++r)
-          for (uint32_t c = 0; c < CT; ++c) q.push_back(s | m << 8 | r << 16 | c << 24);
-      }
+    auto deal = [&](uint32_t s, uint32_t m) {
+      auto& q = queues[item++ % kQueues];
+      for (uint32_t r = 0; r < RB; ++r)
+        for (uint32_t c = 0; c < CT; ++c) q.push_back(s | m << 8 | r << 16 | c << 24);
+    };
+    if (d.flags & PW_FLAG_STAGE_WINDOWS) {
+      constexpr uint32_t kWindow = 16;
+      for (uint32_t w0 = 0; w0 < M; w0 += kWindow)
+        for (uint32_t s = 0; s < S; ++s)
+          for (uint32_t m = w0; m < std::min(M, w0 + kWindow); ++m) deal(s, m);
+    } else {
+      for (uint32_t t = 0; t + 1 < S + M; ++t)
+        for (uint32_t s = 0; s < S; ++s)
+          if (t >= s && t - s < M) deal(s, t - s);
+    }
     std::vector<uint32_t> order, head(kQueues), len(kQueues);
     order.reserve((size_t)S * M * RB * CT);
     for (uint32_t q = 0; q < kQueues; ++q) {

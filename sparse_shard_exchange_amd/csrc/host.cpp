@@ -173,7 +173,10 @@ int validate_desc(const pw_plan_desc* d) {
   if (!d) return fail(PW_ERR_INVALID, "descriptor is NULL");
   if (d->abi_version != PW_ABI_VERSION)
     return fail(PW_ERR_INVALID, "abi_version %u != %u", d->abi_version, PW_ABI_VERSION);
-  if (d->flags & ~(PW_FLAG_TRACE | PW_FLAG_TIMING)) return fail(PW_ERR_INVALID, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(PW_FLAG_TRACE | PW_FLAG_TIMING | PW_FLAG_STAGE_WINDOWS))
+    return fail(PW_ERR_INVALID, "unknown flags 0x%x", d->flags);
+  if ((d->flags & PW_FLAG_STAGE_WINDOWS) && d->kind != PW_GRAPH_PIPELINE)
+    return fail(PW_ERR_INVALID, "PW_FLAG_STAGE_WINDOWS is for PIPELINE plans");
   if (d->capacity && d->kind != PW_GRAPH_MOE) return fail(PW_ERR_INVALID, "capacity is for MOE plans only");
   switch (d->kind) {
     case PW_GRAPH_EXCHANGE: {

@@ -60,10 +60,16 @@ struct PipeTile {
   uint32_t s, m, r, c;
 };
 
-__device__ __forceinline__ PipeTile decode(const PipeArgs& a, uint32_t t) {
-  const uint32_t code = a.order[t];
+// Tickets and tile codes are wave-uniform; readfirstlane says so. The loop
+// over tiles carries only the 32-bit code of a tile and recomputes its
+// pointers where they are used, so that little state lives across the K loop.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ PipeTile unpack(uint32_t code) {
   return {code & 0xFF, (code >> 8) & 0xFF, (code >> 16) & 0xFF, code >> 24};
 }
+
+__device__ __forceinline__ uint32_t code_at(const PipeArgs& a, uint32_t t) { return uniform(a.order[t]); }
 
 __device__ __forceinline__ mm::Tile tile_of(const PipeArgs& a, const PipeTile& p) {
   const uint64_t item_elems = (uint64_t)a.rows * a.d;
@@ -133,18 +139,18 @@ struct Claimer {
 // published as done (so nothing downstream waits forever) and the next ticket
 // is taken. Returns false once the queues are empty.
 __device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl, Claimer& cr, uint32_t t,
-                               PipeTile& p, mm::Tile& tile) {
+                               uint32_t& code) {
   while (t != kNone) {
-    p = decode(a, t);
-    tile = tile_of(a, p);
+    code = code_at(a, t);
+    const PipeTile p = unpack(code);
     if (threadIdx.x == 0) cl.ready = input_ready(a, p, true);
     __syncthreads();
-    if (cl.ready) {
-      mm::tile_start(tile, lds);
+    if (uniform(cl.ready)) {
+      mm::tile_start(tile_of(a, p), lds);
       return true;
     }
     if (threadIdx.x == 0) publish(a, p);
-    t = cl.next;
+    t = uniform(cl.next);
     __syncthreads();  // every thread has read next and ready
     if (threadIdx.x == 0 && t != kNone) cl.next = cr.take(a);
   }
@@ -155,11 +161,11 @@ __device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl
 // wave's stores of it are complete.
 struct PublishPrev {
   const PipeArgs* a;
-  PipeTile p;
+  uint32_t code;
   bool pending;
   __device__ bool active() const { return pending; }
   __device__ void operator()() {
-    if (pending && threadIdx.x == 0) publish(*a, p);
+    if (pending && threadIdx.x == 0) publish(*a, unpack(code));
     pending = false;
   }
 };
@@ -191,44 +197,49 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
     cl.next = cr.take(a);
   }
   __syncthreads();
-  const uint32_t first = cl.next;
+  const uint32_t first = uniform(cl.next);
   __syncthreads();
   if (tid == 0 && first != kNone) cl.next = cr.take(a);
-  PipeTile p;
-  mm::Tile tile;
-  PublishPrev prev{&a, {0, 0, 0, 0}, false};
-  bool have = start_blocking(a, lds, cl, cr, first, p, tile);
+  uint32_t cur = 0;  // code of the tile in hand
+  PublishPrev prev{&a, 0, false};
+  bool have = start_blocking(a, lds, cl, cr, first, cur);
+  // The candidate after the tile in hand and its code, loaded a tile ahead so
+  // that the check below does not wait for the order table.
+  uint32_t nxt = uniform(cl.next);
+  uint32_t nxt_code = nxt != kNone ? code_at(a, nxt) : 0;
   while (have) {
     mm::f32x16 acc[4][4];
-    mm::tile_finish(tile, lds, acc, prev);  // may publish the previous tile; ends with a barrier
-    const uint32_t t2 = cl.next;
-    PipeTile p2 = p;
-    mm::Tile tile2 = tile;
-    if (t2 != kNone) {
-      p2 = decode(a, t2);
-      tile2 = tile_of(a, p2);
-    }
-    __syncthreads();  // every thread has read next
+    mm::tile_finish(tile_of(a, unpack(cur)), lds, acc, prev);  // may publish the previous tile; ends with a barrier
+    const uint32_t t2 = nxt, code2 = nxt_code;
+    // every thread read cl.next and cl.ready before the barriers of the K loop
     if (tid == 0) {
-      cl.ready = t2 != kNone && input_ready(a, p2, false);
+      cl.ready = t2 != kNone && input_ready(a, unpack(code2), false);
       if (t2 != kNone) cl.next = cr.take(a);
     }
     __syncthreads();
-    const bool started = cl.ready;
-    if (started) mm::tile_start(tile2, lds);
+    const bool started = uniform(cl.ready) != 0;
+    uint32_t nxt_raw = 0;  // the load is issued here, its value taken after the epilogue
+    if (started) {
+      nxt = uniform(cl.next);
+      if (nxt != kNone) nxt_raw = a.order[nxt];
+      mm::tile_start(tile_of(a, unpack(code2)), lds);
+    }
+    const PipeTile p = unpack(cur);
     __bf16* out = a.acts + ((uint64_t)p.s * a.M + p.m) * item_elems + (uint64_t)p.r * mm::BM * a.d +
                   (uint64_t)p.c * mm::BN;
-    mm::store_tile<true>(acc, out, a.d, tile.rows);
-    prev.p = p;
+    mm::store_tile<true>(acc, out, a.d, min((int)mm::BM, (int)a.rows - (int)(p.r * mm::BM)));
+    nxt_code = uniform(nxt_raw);
+    prev.code = cur;
     prev.pending = true;
     if (started) {
-      p = p2;
-      tile = tile2;
+      cur = code2;
     } else {  // publish now: the wait below may be for this very tile
       mm::wait_stores();
       __syncthreads();  // every wave's stores complete; every thread has read ready
       prev();
-      have = start_blocking(a, lds, cl, cr, t2, p, tile);
+      have = start_blocking(a, lds, cl, cr, t2, cur);
+      nxt = uniform(cl.next);
+      nxt_code = nxt != kNone ? code_at(a, nxt) : 0;
     }
   }
   if (prev.pending) {  // uniform

@@ -101,6 +101,7 @@ def test_sizing_is_host_only_and_scales_with_tiles():
     (dict(dtype=pw.PW_BF16, a_op=pw.op(pw.PW_OP_AFFINE, 2, 1)), pw.PW_ERR_INVALID),
     (dict(tuples_per_shard=1 << 24), pw.PW_ERR_INVALID),
     (dict(flags=0x80), pw.PW_ERR_INVALID),
+    (dict(flags=pw.PW_FLAG_STAGE_WINDOWS), pw.PW_ERR_INVALID),   # a pipeline claim order on an exchange
 ])
 def test_validation_errors(bad, code):
     d = _ex(**bad)

@@ -77,6 +77,32 @@ def test_pipeline_small_all_outputs(gpu, s, m, rows, d):
     assert np.all(st[1:] > st[:-1])            # stage s of microbatch m completes after stage s-1
 
 
+@pytest.mark.parametrize("s,m,rows", [(3, 20, 300), (2, 33, 257), (16, 4, 256)])
+def test_pipeline_stage_windows_order(gpu, s, m, rows):
+    """PW_FLAG_STAGE_WINDOWS claims the same tiles in another order (stage by
+    stage within windows of 16 microbatches, a ragged last window here): every
+    tile is the same MFMA arithmetic, so the outputs equal the lock-step order's
+    bit for bit; each item still completes after its predecessor stage."""
+    pw = gpu
+    d = 256
+    print(f"pipeline stage windows S={s} M={m} rows={rows}", flush=True)
+    inp, pipe, acts, f = run(pw, s, m, rows, d, flags=pw.PW_FLAG_TRACE | pw.PW_FLAG_STAGE_WINDOWS)
+    _, _, base, _ = run(pw, s, m, rows, d)
+    assert torch.equal(acts, base)
+    x = inp.x.float().numpy()
+    w = inp.w.float().numpy()
+    got = acts.float().cpu().numpy()
+    for mb in (0, m - 1):
+        ref = op.forward(x[mb], w, keep_all=True)
+        for st in range(s):
+            check_stage(got[st, mb], ref[st], (st, mb))
+    ep, fi, stamps = pipe.plan.read_futures(trace=True)
+    n = s * m
+    assert np.all(fi[pw.PW_NODE_STAGE, :n] == 1) and fi[pw.PW_NODE_RESULT, 0] == 1
+    st = stamps[pw.PW_NODE_STAGE, :n].reshape(s, m)
+    assert np.all(st[1:] > st[:-1])
+
+
 def test_pipeline_repeat_is_deterministic(gpu):
     pw = gpu
     inp, pipe, acts, f = run(pw, 2, 3, 300, 256)
@@ -90,12 +116,16 @@ def test_pipeline_repeat_is_deterministic(gpu):
     assert np.all(fi[pw.PW_NODE_STAGE, :6] == 2) and fi[pw.PW_NODE_RESULT, 0] == 2
 
 
-def test_pipeline_full_size_sampled(gpu):
+@pytest.mark.parametrize("order", ["lockstep", "stage_windows"])
+def test_pipeline_full_size_sampled(gpu, order):
     """16 stages x 64 microbatches x 2048 x 1024: every stage output of sampled
-    rows of sampled microbatches against the oracle; GPipe dependency order."""
+    rows of sampled microbatches against the oracle; GPipe dependency order.
+    Both claim orders the bench times."""
     pw = gpu
     s, m, rows, d = 16, 64, 2048, 1024
-    inp, pipe, acts, f = run(pw, s, m, rows, d, flags=pw.PW_FLAG_TRACE)
+    flags = pw.PW_FLAG_TRACE | (pw.PW_FLAG_STAGE_WINDOWS if order == "stage_windows" else 0)
+    print(f"pipeline full size, {order}", flush=True)
+    inp, pipe, acts, f = run(pw, s, m, rows, d, flags=flags)
     x = inp.x
     w = inp.w.float().numpy()
     rng = np.random.default_rng(5)
