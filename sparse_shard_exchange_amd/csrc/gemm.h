@@ -59,6 +59,10 @@ struct Tile {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no
+// swizzle, no index stride; with stride 0 the size field is in bytes.
+constexpr int kBufWord3 = 0x00020000;
+
 // Chunk permutation of 64-byte LDS rows. gfx950 serves a 16-byte-per-lane
 // LDS read 16 lanes (256 bytes) at a time; lanes reading 16 consecutive rows
 // at one logical chunk land in 16 distinct 16-byte bank groups with this
@@ -240,6 +244,31 @@ __device__ __forceinline__ void tile_start(const Tile& t, unsigned char* lds) {
     issue_half(t, o, s * BK, ring_slot(lds, s), 1);
   }
   issue_half(t, o, 2 * BK, ring_slot(lds, 2), 0);
+}
+
+// tile_start predicated on `live` without a branch: the same loads through
+// buffer resources whose size is zero when !live, so that every one is out of
+// range and returns without touching memory (the ring then holds junk, which
+// the caller discards after waiting for it). Used where the next tile is
+// started speculatively right before an epilogue: a conditional tile_start
+// there makes the compiler move the accumulators out before the branch.
+__device__ __forceinline__ void tile_start_if(const Tile& t, unsigned char* lds, bool live) {
+  const Lanes o = lane_offsets(t);
+  const int w = threadIdx.x >> 6;
+  const int n = live ? 0x7FFFFFFF : 0;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)t.A, (short)0, n, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)t.Bt, (short)0, n, kBufWord3);
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int h = 0; h < (s < 2 ? 2 : 1); ++h)
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * h + ii, group = w * 4 + i;
+        unsigned char* stage = ring_slot(lds, s);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(stage + group * 1024), 16, o.a[i] + s * BK * 2, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(stage + kHalf + group * 1024), 16, o.b[i] + s * BK * 2, 0, 0, 0);
+      }
 }
 
 // Stage kHookStage of the K loop with a hook: if hook.active() (uniform),

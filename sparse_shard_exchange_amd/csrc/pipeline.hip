@@ -35,13 +35,13 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return v;
 }
 
-// Claim the next tile: this XCD's queue first; only once it is empty, the
-// other queues in turn. Returns an index into the order table or kNone.
-__device__ __forceinline__ uint32_t claim(const PipeArgs& a, uint32_t home) {
-  for (uint32_t q = 0; q < a.nq; ++q) {
-    const uint32_t qi = (home + q) % a.nq;
-    const uint32_t k = __hip_atomic_fetch_add(&a.qctr[qi], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (k < a.qlen[qi]) return a.qstart[qi] + k;
+// Claim the next tile, blocking: queue q first, then the others in turn.
+// Returns an index into the order table (and the queue it came from in q) or
+// kNone.
+__device__ __forceinline__ uint32_t claim_from(const PipeArgs& a, uint32_t& q) {
+  for (uint32_t n = 0; n < a.nq; ++n, q = (q + 1) % a.nq) {
+    const uint32_t k = __hip_atomic_fetch_add(&a.qctr[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (k < a.qlen[q]) return a.qstart[q] + k;
   }
   return kNone;
 }
@@ -121,15 +121,35 @@ struct Claims {
   uint32_t ready;  // thread 0's verdict on the candidate
 };
 
-// Thread 0's claim pipeline: `ahead` is one more ticket, claimed with an
-// atomic whose result is only needed a whole tile later, so the atomic's
-// round trip (contended by the CUs of an XCD) stays off the critical path.
+// Thread 0's claim pipeline. A claim is an atomic add on a queue counter
+// shared by the CUs of an XCD, a round trip of several microseconds; its
+// result is needed only a whole tile later. So take() hands out the ticket
+// claimed on the previous call and issues the next claim without waiting for
+// it (`raw` holds the counter value in flight, for queue q); the next take()
+// turns it into a ticket, falling back to the other queues (blocking) once
+// queue q is exhausted.
 struct Claimer {
-  uint32_t ahead;
-  uint32_t home;
+  uint32_t raw;   // value returned by the add in flight on queue q
+  uint32_t q;     // the queue being drained
+  bool live;      // an add is in flight
+  __device__ void issue(const PipeArgs& a) {
+    raw = __hip_atomic_fetch_add(&a.qctr[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    live = true;
+  }
   __device__ uint32_t take(const PipeArgs& a) {  // thread 0
-    const uint32_t t = ahead;
-    ahead = t == kNone ? kNone : claim(a, home);
+    if (!live) return kNone;
+    uint32_t t;
+    if (raw < a.qlen[q]) {
+      t = a.qstart[q] + raw;
+    } else {
+      q = (q + 1) % a.nq;
+      t = claim_from(a, q);  // blocking; leaves q at the queue that had work
+    }
+    if (t == kNone) {
+      live = false;
+    } else {
+      issue(a);
+    }
     return t;
   }
 };
@@ -180,20 +200,20 @@ struct PublishPrev {
 // at tile granularity do they outnumber the workgroups.)
 //
 // Tile t's epilogue overlaps both neighbours: once its K loop ends, the first
-// stages of tile t+1 are issued if t+1's input row block is already complete
-// (one non-blocking check), then t is stored, and t+1's K loop publishes t a
-// few stages in (its stores long complete by then). If the check failed, t is
-// published first and only then does the workgroup wait for t+1's input: t+1
-// may depend on t itself.
+// stages of tile t+1 are issued (and kept if t+1's input row block is already
+// complete, by one non-blocking check), then t is stored, and t+1's K loop
+// publishes t a few stages in (its stores long complete by then). If the
+// check failed, t is published first and only then does the workgroup wait
+// for t+1's input: t+1 may depend on t itself.
 __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ Claims cl;
   const uint32_t tid = threadIdx.x;
   const uint64_t item_elems = (uint64_t)a.rows * a.d;
-  Claimer cr{kNone, 0};
+  Claimer cr{0, 0, false};
   if (tid == 0) {
-    cr.home = xcc_id() % a.nq;
-    cr.ahead = claim(a, cr.home);
+    cr.q = xcc_id() % a.nq;
+    cr.issue(a);
     cl.next = cr.take(a);
   }
   __syncthreads();
@@ -222,8 +242,14 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
     if (started) {
       nxt = uniform(cl.next);
       if (nxt != kNone) nxt_raw = a.order[nxt];
-      mm::tile_start(tile_of(a, unpack(code2)), lds);
     }
+    // Issued without a branch (a conditional start here makes the compiler
+    // read the accumulators out before the branch, which doubles the register
+    // demand of the epilogue and spills); when not started the loads are out
+    // of range and touch no memory, and the ring contents are discarded below
+    // once every wave has waited for them. (code2 is a valid tile even when
+    // there is no candidate.)
+    mm::tile_start_if(tile_of(a, unpack(code2)), lds, started);
     const PipeTile p = unpack(cur);
     __bf16* out = a.acts + ((uint64_t)p.s * a.M + p.m) * item_elems + (uint64_t)p.r * mm::BM * a.d +
                   (uint64_t)p.c * mm::BN;
@@ -235,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
       cur = code2;
     } else {  // publish now: the wait below may be for this very tile
       mm::wait_stores();
-      __syncthreads();  // every wave's stores complete; every thread has read ready
+      __syncthreads();  // every wave's stores and ring loads complete; every thread has read ready
       prev();
       have = start_blocking(a, lds, cl, cr, t2, cur);
       nxt = uniform(cl.next);
