@@ -14,7 +14,7 @@ constexpr uint32_t kQueues = 8;  // one claim queue per XCD
 
 struct KindState {
   uint64_t calls = 0;  // calls launched so far (targets of the cumulative device counters)
-  uint32_t grid = 0;   // PIPELINE: persistent workgroups (one per CU)
+  uint32_t grid = 0;   // PIPELINE, MOE: persistent workgroups (one per CU)
 };
 
 }  // namespace
@@ -129,7 +129,11 @@ int plan_init_kind(Plan* p) {
     // expert and router weights -> packed K-contiguous copies, once
     const pw_plan_desc& d = p->desc;
     const uint32_t E = d.num_shards, D = d.payload_elems, H = d.hidden;
-    hipError_t e = hipDeviceSynchronize();
+    int cus = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    ks->grid = (uint32_t)std::max(1, cus);
+    e = hipDeviceSynchronize();
     if (e == hipSuccess)
       e = launch_pack_t(static_cast<const __bf16*>(d.w1), reinterpret_cast<__bf16*>(p->base() + p->L.w1t), E, D, H, H,
                         nullptr);
@@ -263,8 +267,9 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done,
   p->open.active = false;
   PW_STEP("scatter", launch_scatter(a, s));
   PW_STEP("moe_prefix", launch_moe_prefix(m, s));
-  PW_STEP("ffn1", launch_ffn(m, false, s));
-  PW_STEP("ffn2", launch_ffn(m, true, s));
+  const uint32_t cus = static_cast<KindState*>(p->kind_state)->grid;
+  PW_STEP("ffn1", launch_ffn(m, false, cus, s));
+  PW_STEP("ffn2", launch_ffn(m, true, cus, s));
   PW_STEP("combine", launch_combine(m, s));
 #undef PW_STEP
   p->epoch += 1;

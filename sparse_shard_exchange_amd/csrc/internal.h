@@ -133,7 +133,7 @@ hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);
 hipError_t launch_pipeline(const PipeArgs& a, uint32_t grid, hipStream_t s);
 hipError_t launch_router(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_prefix(const MoeArgs& a, hipStream_t s);
-hipError_t launch_ffn(const MoeArgs& a, bool second, hipStream_t s);
+hipError_t launch_ffn(const MoeArgs& a, bool second, uint32_t cus, hipStream_t s);
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s);
 hipError_t launch_pack_t(const __bf16* in, __bf16* out, uint32_t batch, uint32_t K, uint32_t N_in, uint32_t N_out,
                          hipStream_t s);

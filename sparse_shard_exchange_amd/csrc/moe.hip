@@ -14,6 +14,8 @@
 // Token t emits tuples 2t (top-1 expert) and 2t + 1 (top-2 expert); the
 // exchange (exchange.hip) moves token rows into expert segments and records
 // slot_of[g], the inverse of the permutation, which the combine reads.
+#include <algorithm>
+
 #include "device.h"
 #include "gemm.h"
 
@@ -156,47 +158,146 @@ __device__ __forceinline__ void tile_at(uint32_t b, uint32_t CT, uint32_t& rbg, 
   c = (k % groups) * C + p % C;
 }
 
-// One 256 x 256 tile of an expert FFN GEMM: rows of expert e's segment.
-// kSecond: input H, weights W2 [E][hidden][d], output Y (no activation);
-// otherwise input dispatched rows, W1 [E][d][hidden], output H through GELU.
+// Per-workgroup copies of the segment tables and the set of experts whose
+// exchange future has fired (their input rows are complete).
+struct FfnShared {
+  uint32_t rb_start[kMaxExperts + 1];
+  int64_t seg[kMaxExperts + 1];
+  uint32_t ok[2];  // bit e: expert e may be read
+};
+
+// One 256 x 256 output tile of an expert FFN GEMM (wave-uniform).
+struct FfnTile {
+  uint32_t e, c;
+  int64_t row0;  // first row of the tile in the expert-sorted activations
+  int rows;      // valid rows (1..256)
+};
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  return (int64_t)((uint64_t)uniform((uint32_t)(u >> 32)) << 32 | uniform((uint32_t)u));
+}
+
+__device__ __forceinline__ FfnTile ffn_tile(const FfnShared& sh, uint32_t E, uint32_t rbg, uint32_t c) {
+  FfnTile t;
+  t.e = uniform(expert_of(sh.rb_start, E, rbg));
+  const uint32_t rb = rbg - uniform(sh.rb_start[t.e]);
+  const int64_t seg0 = uniform64(sh.seg[t.e]), n_e = uniform64(sh.seg[t.e + 1]) - seg0;
+  t.row0 = seg0 + (int64_t)rb * mm::BM;
+  t.rows = (int)uniform((uint32_t)min<int64_t>(mm::BM, n_e - (int64_t)rb * mm::BM));
+  t.c = c;
+  return t;
+}
+
+// The first tile index at or after b (stride: the grid) whose row block
+// exists for this call's expert segments and whose expert's input is
+// complete; ~0u if none.
+__device__ __forceinline__ uint32_t next_tile(const FfnShared& sh, uint32_t E, uint32_t CT, uint32_t total_rb,
+                                              uint32_t b, uint32_t nb, FfnTile& t) {
+  for (; b < nb; b += gridDim.x) {
+    uint32_t rbg, c;
+    tile_at(b, CT, rbg, c);
+    if (rbg >= total_rb) continue;
+    t = ffn_tile(sh, E, rbg, c);
+    if ((uniform(sh.ok[t.e >> 5]) >> (t.e & 31)) & 1u) return b;
+  }
+  return ~0u;
+}
+
 template <bool kSecond>
-__global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  __shared__ uint32_t go;
-  const uint32_t CT = (kSecond ? a.d : a.hidden) / mm::BN;
-  uint32_t rbg, c;
-  tile_at(blockIdx.x, CT, rbg, c);
-  const uint32_t total_rb = a.rb_start[a.E];
-  if (rbg >= total_rb) return;  // grid is sized for the worst case
-  const uint32_t e = expert_of(a.rb_start, a.E, rbg);
-  const uint32_t rb = rbg - a.rb_start[e];
-  const int64_t seg0 = a.seg[e], n_e = a.seg[e + 1] - seg0;
-  const int64_t row0 = seg0 + (int64_t)rb * mm::BM;
-  const int rows = (int)min<int64_t>(mm::BM, n_e - (int64_t)rb * mm::BM);
-  if (threadIdx.x == 0) go = await_prior(a.f, NODE_EXCH, e, a.epoch);  // the expert's input is complete
-  __syncthreads();
-  if (!go) return;
-  mm::Tile tile;
+__device__ __forceinline__ mm::Tile ffn_operands(const MoeArgs& a, const FfnTile& t) {
   const uint32_t K = kSecond ? a.hidden : a.d, N = kSecond ? a.d : a.hidden;
-  const __bf16* in = kSecond ? a.h : a.xd;
-  tile.A = in + row0 * K;
+  mm::Tile tile;
+  tile.A = (kSecond ? a.h : a.xd) + t.row0 * K;
   tile.lda = K;
-  tile.rows = rows;
-  tile.Bt = (kSecond ? a.w2t : a.w1t) + (int64_t)e * K * N + (int64_t)c * mm::BN * K;
+  tile.rows = t.rows;
+  tile.Bt = (kSecond ? a.w2t : a.w1t) + (int64_t)t.e * K * N + (int64_t)t.c * mm::BN * K;
   tile.ldb = K;
   tile.K = (int)K;
-  mm::f32x16 acc[4][4];
-  mm::tile_mma(tile, lds, acc);
-  __bf16* out = (kSecond ? a.y : a.h) + row0 * N + (int64_t)c * mm::BN;
-  mm::store_tile<!kSecond>(acc, out, N, rows);
-  if (kSecond) {  // B[e] completes with the last tile of its segment
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t tiles_e = (uint32_t)((n_e + mm::BM - 1) / mm::BM) * CT;
-      const uint32_t old = __hip_atomic_fetch_add(&a.b_done[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old + 1 == tiles_e) fire(a.f, NODE_B, e, a.epoch, false);
+  return tile;
+}
+
+// FFN2: a finished tile counts towards its expert; the expert's last tile
+// fires B[e]. Called once every wave's stores of the tile have completed (after
+// the next tile's K loop); the consumer (the combine) is a later launch on the
+// same stream, so the kernel boundary makes the rows visible to it.
+struct CountTile {
+  const MoeArgs* a;
+  uint32_t e, tiles_e;
+  bool pending;
+  __device__ void operator()() {
+    if (pending && threadIdx.x == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(&a->b_done[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + 1 == tiles_e) fire(a->f, NODE_B, e, a->epoch, false);
     }
+    pending = false;
   }
+};
+
+// Expert FFN GEMM, persistent: one workgroup per CU walks the tiles
+// b = blockIdx.x + k * gridDim.x (grid a multiple of 8, so all of a
+// workgroup's tiles map to the XCD it runs on; see tile_at). kSecond: input
+// H, weights W2 [E][hidden][d], output Y (no activation); otherwise input the
+// dispatched rows, W1 [E][d][hidden], output H through GELU.
+//
+// B is gated on the exchange: before touching any rows, lane e of wave 0
+// waits for expert e's exchange future (all experts at once); tiles of an
+// expert whose wait expired are skipped (its B future then never fires and
+// the combine reports the timeout). Each tile's epilogue overlaps the next
+// tile's first loads, issued through size-predicated buffer loads (a branch
+// there would make the compiler move the accumulators out early).
+template <bool kSecond>
+__global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a, uint32_t nb) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  __shared__ FfnShared sh;
+  const uint32_t tid = threadIdx.x, E = a.E;
+  const uint32_t CT = (kSecond ? a.d : a.hidden) / mm::BN;
+  const uint32_t N = kSecond ? a.d : a.hidden;
+  if (tid <= E) {
+    sh.rb_start[tid] = a.rb_start[tid];
+    sh.seg[tid] = a.seg[tid];
+  }
+  if (tid < 2) sh.ok[tid] = 0;
+  __syncthreads();
+  if (tid < E) {
+    const bool go = await_prior(a.f, NODE_EXCH, tid, a.epoch);  // the expert's input is complete
+    if (go) atomicOr(&sh.ok[tid >> 5], 1u << (tid & 31));
+  }
+  __syncthreads();
+  const uint32_t total_rb = uniform(sh.rb_start[E]);
+  FfnTile cur;
+  uint32_t b = next_tile(sh, E, CT, total_rb, blockIdx.x, nb, cur);
+  if (b == ~0u) return;  // uniform
+  mm::tile_start(ffn_operands<kSecond>(a, cur), lds);
+  CountTile count{&a, 0, 0, false};
+  while (true) {
+    // the next tile is looked up before the K loop: control flow between the
+    // K loop and the epilogue would also make the accumulators move early
+    FfnTile nxt = cur;
+    const uint32_t b2 = next_tile(sh, E, CT, total_rb, b + gridDim.x, nb, nxt);
+    mm::f32x16 acc[4][4];
+    mm::NoHook none;
+    mm::tile_finish(ffn_operands<kSecond>(a, cur), lds, acc, none);
+    mm::tile_start_if(ffn_operands<kSecond>(a, nxt), lds, b2 != ~0u);
+    mm::store_tile<!kSecond>(acc, (kSecond ? a.y : a.h) + cur.row0 * N + (int64_t)cur.c * mm::BN, N, cur.rows);
+    if (kSecond) {
+      // every wave waited for all its memory operations inside the K loop
+      // above, then met at its final barrier: the previous tile's stores are
+      // complete (counted only here, after the epilogue, because a branch
+      // between the K loop and the epilogue makes the accumulators move early)
+      count();
+      count.e = cur.e;
+      count.tiles_e = uniform((uint32_t)((sh.seg[cur.e + 1] - sh.seg[cur.e] + mm::BM - 1) / mm::BM)) * CT;
+      count.pending = true;
+    }
+    if (b2 == ~0u) break;
+    b = b2;
+    cur = nxt;
+  }
+  mm::wait_stores();  // also the out-of-range loads of the start above
+  __syncthreads();
+  if (kSecond) count();
 }
 
 // out[t] = bf16(g0 * Y[slot(2t)] + g1 * Y[slot(2t + 1)]), fp32 sum with the
@@ -268,21 +369,21 @@ hipError_t launch_moe_prefix(const MoeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_ffn(const MoeArgs& a, bool second, hipStream_t s) {
-  // enough whole patch rounds to cover max_row_blocks row blocks (see tile_at)
+hipError_t launch_ffn(const MoeArgs& a, bool second, uint32_t cus, hipStream_t s) {
+  // tile indices: enough whole patch rounds to cover max_row_blocks row
+  // blocks (see tile_at); persistent grid: one workgroup per CU, a multiple of 8
   const uint32_t CT = (second ? a.d : a.hidden) / mm::BN;
   const uint32_t C = CT % 8 == 0 ? 8 : CT % 4 == 0 ? 4 : CT % 2 == 0 ? 2 : 1, R = kPatch / C;
   const uint64_t row_groups = ((uint64_t)a.max_row_blocks + R - 1) / R;
-  const uint64_t blocks = (row_groups + kXcds - 1) / kXcds * kXcds * R * CT;
-  if (second) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_ffn<true>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsTotal);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ffn<true>, dim3((uint32_t)blocks), dim3(mm::NT), mm::kLdsTotal, s, a);
-  } else {
-    hipError_t e = hipFuncSetAttribute((const void*)k_ffn<false>, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsTotal);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ffn<false>, dim3((uint32_t)blocks), dim3(mm::NT), mm::kLdsTotal, s, a);
-  }
+  const uint64_t nb = (row_groups + kXcds - 1) / kXcds * kXcds * R * CT;
+  const uint32_t grid = (uint32_t)std::min<uint64_t>(nb, std::max<uint32_t>(kXcds, cus / kXcds * kXcds));
+  const void* fn = second ? (const void*)k_ffn<true> : (const void*)k_ffn<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, mm::kLdsTotal);
+  if (e != hipSuccess) return e;
+  if (second)
+    hipLaunchKernelGGL(k_ffn<true>, dim3(grid), dim3(mm::NT), mm::kLdsTotal, s, a, (uint32_t)nb);
+  else
+    hipLaunchKernelGGL(k_ffn<false>, dim3(grid), dim3(mm::NT), mm::kLdsTotal, s, a, (uint32_t)nb);
   return hipGetLastError();
 }
 
