@@ -9,8 +9,11 @@
 // buffers. On one GPU the "interconnect" is HBM, and the exchange is a stable
 // counting sort by destination done in three launches:
 //
-//   hist    one workgroup per tile of `tile` consecutive tuples counts its
-//           destinations (LDS atomics) and writes the row tile_base[tile][*];
+//   rank    one workgroup per tile of `tile` consecutive tuples counts its
+//           destinations (LDS atomics), writes the row tile_base[tile][*]
+//           (and a copy, tile_cnt), and ranks each tuple among the tuples of
+//           the tile with the same destination, in tuple order (wave by wave;
+//           inside a wave by ballot matching), into rank[g] (16 bits);
 //   scan    one workgroup per block of scan_tiles tiles runs, per
 //           destination, down its rows (where each tile's run of d starts
 //           inside the block) and writes the block totals; the last
@@ -18,11 +21,17 @@
 //           destination totals into segment offsets, sets the expected count
 //           of every destination and fires the futures of destinations that
 //           receive nothing;
-//   scatter one workgroup per tile re-ranks its tuples (stable: wave by wave,
-//           in source order), applies A and writes each payload row with
-//           16-byte vector stores straight into its destination segment,
-//           then adds its per-destination counts to the arrival counters;
-//           the workgroup whose add completes a destination fires that
+//   scatter one short-lived workgroup per chunk of ~16 KiB of payload (64
+//           rows of 256 bytes) finds each tuple's slot (segment start + the
+//           tile's run start + its rank), applies A and writes each payload
+//           row with 16-byte vector stores straight into its destination
+//           segment. Chunks are dispatched in tuple order, so the workgroups
+//           in flight read one compact window of the input and append to a
+//           few destination runs: measured on this part, a copy split into
+//           16 KiB pieces per workgroup runs at ~6.3 TB/s, one whose
+//           workgroups each own 64 KiB or more at ~5.5. The last chunk of a
+//           tile to finish adds the tile's per-destination counts to the
+//           arrival counters; the add that completes a destination fires that
 //           destination's future.
 //
 // B (exchange.hip: k_b) runs per block of output slots and starts only after
@@ -73,7 +82,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return pre + x - v;
 }
 
-// ---------------------------------------------------------------- histogram
+// --------------------------------------------------------------------- rank
 // A wave's destinations, loaded before any is used (up to kMaxChunks chunks
 // of 64 tuples: tile <= 4096 split over 4 waves), so that the loads of its
 // whole sub-tile are in flight together.
@@ -91,24 +100,54 @@ __device__ __forceinline__ WaveDests load_wave_dests(const ExchangeArgs& a, uint
   return w;
 }
 
-__global__ __launch_bounds__(kBlock) void k_hist(ExchangeArgs a) {
+__global__ __launch_bounds__(kBlock) void k_rank(ExchangeArgs a) {
   extern __shared__ uint32_t lds[];
-  uint32_t* cnt = lds;  // [N]
-  for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) cnt[d] = 0;
+  const uint32_t N = a.N;
+  uint32_t* wrun = lds;  // [kWaves][N]: counts of each wave's sub-tile, then its next rank per destination
+  for (uint32_t i = threadIdx.x; i < kWaves * N; i += kBlock) wrun[i] = 0;
   __syncthreads();
   const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t sub = a.tile / kWaves;
   const uint64_t g0 = (uint64_t)blockIdx.x * a.tile + (uint64_t)w * sub;
+  uint32_t* mine = wrun + w * N;
   bool bad = false;
+  // 1. per-wave counts of its contiguous sub-tile (order-free: LDS atomics)
   const WaveDests wd = load_wave_dests(a, g0, sub, lane, bad);
-  // counts need no order: one LDS atomic per tuple (the LDS serializes
-  // lanes that hit one counter, which is cheaper than matching them)
 #pragma unroll
   for (uint32_t i = 0; i < kMaxChunks; ++i)
-    if (wd.d[i] >= 0) atomicAdd(&cnt[wd.d[i]], 1u);
-  if (bad) latch(a.f.status, ST_BAD_DEST);
+    if (wd.d[i] >= 0) atomicAdd(&mine[wd.d[i]], 1u);
   __syncthreads();
-  for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) a.tile_base[(uint64_t)blockIdx.x * a.N + d] = cnt[d];
+  // 2. the tile's counts (for the scan, and kept for the arrival counts) and
+  //    the first rank of each (wave, destination): the counts of earlier waves
+  for (uint32_t d = threadIdx.x; d < N; d += kBlock) {
+    uint32_t run = 0;
+#pragma unroll
+    for (uint32_t ww = 0; ww < kWaves; ++ww) {
+      const uint32_t c = wrun[ww * N + d];
+      wrun[ww * N + d] = run;
+      run += c;
+    }
+    a.tile_base[(uint64_t)blockIdx.x * N + d] = run;
+    a.tile_cnt[(uint64_t)blockIdx.x * N + d] = run;
+  }
+  if (threadIdx.x == 0) a.tile_done[blockIdx.x] = 0;
+  __syncthreads();
+  // 3. stable rank inside each 64-tuple chunk of the sub-tile, in order
+#pragma unroll
+  for (uint32_t i = 0; i < kMaxChunks; ++i) {
+    if (i * 64 >= sub) break;  // uniform
+    const int d = wd.d[i];
+    const bool valid = d >= 0;
+    const uint64_t peers = match_peers(d, valid, a.nbits);
+    if (valid) {
+      const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt(lane));
+      const uint32_t r = mine[d] + rank;
+      // every lane has read mine[] before the group's leader advances it
+      if (rank == 0) mine[d] = r + (uint32_t)__popcll(peers);
+      a.rank[g0 + i * 64 + lane] = (uint16_t)r;
+    }
+  }
+  if (bad) latch(a.f.status, ST_BAD_DEST);
 }
 
 // ------------------------------------------------- per-source counts export
@@ -230,153 +269,129 @@ __device__ __forceinline__ uint32_t apply_a<uint32_t>(uint32_t v, const Exchange
   return __float_as_uint(f);
 }
 
-// Copy the payload rows of one 64-tuple chunk: tuple t of the chunk (lane t
-// holds its slot and source row) goes to slot __shfl(slot, t). Unit U is 16
-// bytes when rows are a multiple of 16 bytes, else 4 bytes;
-// v_units = row_bytes / sizeof(U). kCopyBatch units per lane are loaded
-// before any is stored, so each wave keeps 16 KiB of reads in flight (a
-// whole chunk of 256-byte rows; measured 2% faster than 8 KiB).
-constexpr uint32_t kCopyBatch = 16;
+// Tuples per scatter workgroup: about 16 KiB of payload, a power of two
+// that divides the tile (tiles are powers of two >= 256), at most kMaxChunk.
+constexpr uint32_t kMaxChunk = 1024;
+constexpr uint32_t kCopyBatch = 4;  // units per thread loaded before any is stored (16 KiB per workgroup)
 
-template <typename U, bool kAffine>
-__device__ __forceinline__ void copy_chunk(const ExchangeArgs& a, uint32_t lane, int slot, uint32_t srow,
-                                           bool valid, uint32_t v_units, uint32_t v_shift, bool v_pow2) {
-  const uint32_t total = 64u * v_units;
-  for (uint32_t j0 = 0; j0 < total; j0 += 64u * kCopyBatch) {
-    U v[kCopyBatch];
-    int dslot[kCopyBatch];
-    uint32_t unit[kCopyBatch];
-    bool ok[kCopyBatch];
+// One workgroup per chunk of a.chunk consecutive tuples (inside one tile).
+// Unit U is 16 bytes when rows are a multiple of 16 bytes, else 4 bytes.
+// kCap: each destination keeps its first `capacity` tuples in tuple order:
+// a tuple is kept if its rank inside the destination is below the capacity;
+// a dropped tuple moves nothing and its slot_of is -1.
+// The payload units of one batch (kCopyBatch per thread) of the chunk: unit
+// i is unit i % vu of tuple i / vu. Source rows do not depend on the slots.
+template <typename U>
+struct Batch {
+  U v[kCopyBatch];
+
+  __device__ __forceinline__ void load(const ExchangeArgs& a, uint64_t g0, uint32_t j0, uint32_t total, uint32_t vu,
+                                       bool pow2, uint32_t shift) {
 #pragma unroll
     for (uint32_t u = 0; u < kCopyBatch; ++u) {
-      const uint32_t i = j0 + u * 64u + lane;
-      const bool in = (j0 + u * 64u) < total;  // wave-uniform
-      uint32_t t = 0, k = 0;
-      if (in) {
-        if (v_pow2) {
-          t = i >> v_shift;
-          k = i & (v_units - 1);
-        } else {
-          t = i / v_units;
-          k = i - t * v_units;
+      const uint32_t i = j0 + u * kBlock + threadIdx.x;
+      if (i < total) {
+        const uint32_t t = pow2 ? i >> shift : i / vu;
+        const uint64_t g = g0 + t;
+        if (g < a.G) {
+          const U* src = reinterpret_cast<const U*>(a.src + (g / a.fanout) * a.row_bytes);
+          v[u] = __builtin_nontemporal_load(src + (i - t * vu));
         }
       }
-      const int ts = __shfl(slot, (int)t, 64);
-      const int tv = __shfl((int)valid, (int)t, 64);
-      const uint32_t tr = (uint32_t)__shfl((int)srow, (int)t, 64);
-      ok[u] = in && tv;
-      dslot[u] = ts;
-      unit[u] = k;
-      if (ok[u]) {
-        const U* src = reinterpret_cast<const U*>(a.src + (uint64_t)tr * a.row_bytes);
-        v[u] = __builtin_nontemporal_load(src + k);
-      }
     }
+  }
+
+  template <bool kAffine>
+  __device__ __forceinline__ void store(const ExchangeArgs& a, const int* s_slot, uint32_t j0, uint32_t total,
+                                        uint32_t vu, bool pow2, uint32_t shift) const {
 #pragma unroll
     for (uint32_t u = 0; u < kCopyBatch; ++u) {
-      if (ok[u]) {
-        U x = v[u];
-        if (kAffine) x = apply_a<U>(x, a);
-        U* dst = reinterpret_cast<U*>(a.dst + (uint64_t)dslot[u] * a.row_bytes);
-        __builtin_nontemporal_store(x, dst + unit[u]);
+      const uint32_t i = j0 + u * kBlock + threadIdx.x;
+      if (i < total) {
+        const uint32_t t = pow2 ? i >> shift : i / vu;
+        const int slot = s_slot[t];
+        if (slot >= 0) {
+          U x = v[u];
+          if (kAffine) x = apply_a<U>(x, a);
+          U* dst = reinterpret_cast<U*>(a.dst + (uint64_t)slot * a.row_bytes);
+          __builtin_nontemporal_store(x, dst + (i - t * vu));
+        }
       }
     }
   }
-}
+};
 
-// kCap: each destination keeps its first `capacity` tuples in tuple order.
-// Then wrun holds ranks inside the destination (not slots), a tuple is kept
-// if its rank is below the capacity, and its slot is the segment start
-// (segl) plus the rank; a dropped tuple moves nothing and its slot_of is -1.
-template <bool kAffine, bool kCap>
+// One workgroup per chunk of a.chunk consecutive tuples (inside one tile).
+// Unit U is 16 bytes when rows are a multiple of 16 bytes, else 4 bytes.
+// The chunk's first batch of payload loads is issued before the slots are
+// looked up, so the two round trips overlap. kCap: each destination keeps
+// its first `capacity` tuples in tuple order: a tuple is kept if its rank
+// inside the destination is below the capacity; a dropped tuple moves
+// nothing and its slot_of is -1.
+template <typename U, bool kAffine, bool kCap>
 __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
-  extern __shared__ uint32_t lds[];
-  const uint32_t N = a.N;
-  uint32_t* wrun = lds;            // [kWaves][N]: next slot (kCap: rank) of each destination, per wave
-  uint32_t* tcnt = lds + kWaves * N;  // [N]: tuples of this tile per destination that are kept
-  uint32_t* segl = tcnt + N;          // [N] kCap: segment starts
-  for (uint32_t i = threadIdx.x; i < kWaves * N; i += kBlock) wrun[i] = 0;
-  __syncthreads();
+  __shared__ int s_slot[kMaxChunk];  // destination slot of each tuple of the chunk, -1: nothing to move
+  __shared__ uint32_t s_last;
+  const uint32_t N = a.N, C = a.chunk;
+  const uint64_t g0 = (uint64_t)blockIdx.x * C;
+  const uint32_t tile = (uint32_t)(g0 / a.tile);
+  const uint32_t* tbase = a.tile_base + (uint64_t)tile * N;
+  const uint32_t* bbase = a.blk_base + (uint64_t)(tile / a.scan_tiles) * N;
+  const uint32_t vu = a.row_bytes / (uint32_t)sizeof(U);
+  const bool pow2 = (vu & (vu - 1)) == 0;
+  const uint32_t shift = pow2 ? (uint32_t)__builtin_ctz(vu) : 0u;
+  const uint32_t total = C * vu;
+  Batch<U> b;
+  b.load(a, g0, 0, total, vu, pow2, shift);
 
-  const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t sub = a.tile / kWaves;
-  const uint64_t g0 = (uint64_t)blockIdx.x * a.tile + (uint64_t)w * sub;
-  uint32_t* mine = wrun + w * N;
   bool bad = false;
-
-  // 1. per-wave counts of this wave's contiguous sub-tile
-  {
-    const WaveDests wd = load_wave_dests(a, g0, sub, lane, bad);
-#pragma unroll
-    for (uint32_t i = 0; i < kMaxChunks; ++i)
-      if (wd.d[i] >= 0) atomicAdd(&mine[wd.d[i]], 1u);
-  }
-  __syncthreads();
-
-  // 2. first slot of each (wave, destination): segment start + this tile's
-  //    start inside the segment + the counts of earlier waves
-  for (uint32_t d = threadIdx.x; d < N; d += kBlock) {
-    const uint32_t rank0 = a.blk_base[(uint64_t)(blockIdx.x / a.scan_tiles) * N + d] +
-                           a.tile_base[(uint64_t)blockIdx.x * N + d];
-    const uint32_t base = kCap ? rank0 : (uint32_t)a.seg[d] + rank0;
-    uint32_t run = base;
-#pragma unroll
-    for (uint32_t ww = 0; ww < kWaves; ++ww) {
-      const uint32_t c = wrun[ww * N + d];
-      wrun[ww * N + d] = run;
-      run += c;
-    }
-    if (kCap) {
-      tcnt[d] = min(run, a.capacity) - min(base, a.capacity);
-      segl[d] = (uint32_t)a.seg[d];
-    } else {
-      tcnt[d] = run - base;
-    }
-  }
-  __syncthreads();
-
-  // 3. stable rank inside each 64-tuple chunk, then move the rows
-  const uint32_t unit_bytes = (a.row_bytes % 16u == 0) ? 16u : 4u;
-  const uint32_t v_units = a.row_bytes / unit_bytes;
-  const bool v_pow2 = (v_units & (v_units - 1)) == 0;
-  const uint32_t v_shift = v_pow2 ? (uint32_t)__builtin_ctz(v_units) : 0u;
-  for (uint32_t c = 0; c < sub && g0 + c < a.G; c += 64) {
-    const uint64_t g = g0 + c + lane;
+  for (uint32_t t = threadIdx.x; t < C; t += kBlock) {
+    const uint64_t g = g0 + t;
     const int d = load_dest(a, g, bad);
-    const bool valid_d = d >= 0;
-    const uint64_t peers = match_peers(d, valid_d, a.nbits);
-    const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt(lane));
-    int slot = 0;
-    bool keep = valid_d;
-    if (valid_d) {
-      const uint32_t r = mine[d] + rank;  // kCap: rank inside d; else the slot
-      // every lane has read mine[] before the group's leader advances it
-      if (rank == 0) mine[d] = r + (uint32_t)__popcll(peers);
-      if (kCap) {
-        keep = r < a.capacity;
-        slot = (int)(segl[d] + r);
-      } else {
-        slot = (int)r;
-      }
+    int slot = -1;
+    if (d >= 0) {
+      const uint32_t r = bbase[d] + tbase[d] + a.rank[g];  // rank inside destination d
+      const bool keep = !kCap || r < a.capacity;
+      const uint64_t sl = (uint64_t)a.seg[d] + r;
+      // a slot past the end can only come from dest changing between the
+      // ranking and this pass; never write outside the output
+      const bool valid = keep && sl < a.dst_rows;
+      if (keep && !valid) bad = true;
+      if (valid) slot = (int)sl;
+      if (valid && a.src_index) a.src_index[sl] = (int32_t)g;
+      if (a.slot_of) a.slot_of[g] = slot;
     }
-    // a slot past the end can only come from dest changing between the
-    // histogram and this pass; never write outside the output
-    const bool valid = keep && (uint64_t)slot < a.dst_rows;
-    if (keep && !valid) bad = true;
-    if (valid && a.src_index) a.src_index[slot] = (int32_t)g;
-    if (valid_d && a.slot_of) a.slot_of[g] = valid ? slot : -1;
-    const uint32_t srow = valid ? (uint32_t)(g / a.fanout) : 0u;
-    if (unit_bytes == 16u)
-      copy_chunk<u32x4, kAffine>(a, lane, slot, srow, valid, v_units, v_shift, v_pow2);
-    else
-      copy_chunk<uint32_t, kAffine>(a, lane, slot, srow, valid, v_units, v_shift, v_pow2);
+    s_slot[t] = slot;
+  }
+  __syncthreads();
+
+  b.template store<kAffine>(a, s_slot, 0, total, vu, pow2, shift);
+  for (uint32_t j0 = kBlock * kCopyBatch; j0 < total; j0 += kBlock * kCopyBatch) {
+    b.load(a, g0, j0, total, vu, pow2, shift);
+    b.template store<kAffine>(a, s_slot, j0, total, vu, pow2, shift);
   }
   if (bad) latch(a.f.status, ST_BAD_DEST);
-  __syncthreads();
 
-  // 4. progress: count this tile's arrivals; completing a destination fires it
+  // progress: the last chunk of a tile to finish counts the tile's arrivals;
+  // completing a destination fires it (consumers run in later launches: the
+  // kernel boundary orders the rows before them)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t t0 = (uint64_t)tile * a.tile;
+    const uint64_t in_tile = min<uint64_t>(a.tile, a.G - t0);
+    const uint32_t chunks = (uint32_t)((in_tile + C - 1) / C);
+    const uint32_t old = __hip_atomic_fetch_add(&a.tile_done[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old + 1 == chunks;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const uint32_t* tcnt = a.tile_cnt + (uint64_t)tile * N;
   for (uint32_t d = threadIdx.x; d < N; d += kBlock) {
-    const uint32_t n = tcnt[d];
+    uint32_t n = tcnt[d];
+    if (kCap && n) {
+      const uint32_t base = bbase[d] + tbase[d];
+      n = min(base + n, a.capacity) - min(base, a.capacity);  // the tuples of the tile that d keeps
+    }
     if (n == 0) continue;
     const uint32_t old = __hip_atomic_fetch_add(&a.arrived[d], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + n == a.expected[d]) {
@@ -475,12 +490,15 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
 
 }  // namespace
 
-// wrun and tcnt, plus segl with a capacity (MOE plans only: N <= 64)
-size_t scatter_lds_bytes(uint32_t N, bool cap) { return (size_t)(kWaves + (cap ? 2 : 1)) * N * sizeof(uint32_t); }
-
-hipError_t launch_hist(const ExchangeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_hist, dim3(a.num_tiles), dim3(kBlock), a.N * sizeof(uint32_t), s, a);
+hipError_t launch_rank(const ExchangeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_rank, dim3(a.num_tiles), dim3(kBlock), (size_t)kWaves * a.N * sizeof(uint32_t), s, a);
   return hipGetLastError();
+}
+
+uint32_t scatter_chunk(uint32_t tile, uint32_t row_bytes) {
+  uint32_t c = 1;
+  while (c < kMaxChunk && c < tile && (uint64_t)c * 2 * row_bytes <= 16384) c *= 2;
+  return c;
 }
 
 hipError_t launch_src_counts(const ExchangeArgs& a, hipStream_t s) {
@@ -493,18 +511,25 @@ hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s) {
-  const bool cap = a.capacity != 0;
-  const size_t lds = scatter_lds_bytes(a.N, cap);
-  if (cap && a.a_kind == OP_AFFINE)
-    hipLaunchKernelGGL((k_scatter<true, true>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
+template <typename U>
+static hipError_t launch_scatter_u(const ExchangeArgs& a, uint32_t grid, hipStream_t s) {
+  const bool cap = a.capacity != 0, aff = a.a_kind == OP_AFFINE;
+  if (cap && aff)
+    hipLaunchKernelGGL((k_scatter<U, true, true>), dim3(grid), dim3(kBlock), 0, s, a);
   else if (cap)
-    hipLaunchKernelGGL((k_scatter<false, true>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
-  else if (a.a_kind == OP_AFFINE)
-    hipLaunchKernelGGL((k_scatter<true, false>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
+    hipLaunchKernelGGL((k_scatter<U, false, true>), dim3(grid), dim3(kBlock), 0, s, a);
+  else if (aff)
+    hipLaunchKernelGGL((k_scatter<U, true, false>), dim3(grid), dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((k_scatter<false, false>), dim3(a.num_tiles), dim3(kBlock), lds, s, a);
+    hipLaunchKernelGGL((k_scatter<U, false, false>), dim3(grid), dim3(kBlock), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s) {
+  const uint64_t grid = (a.G + a.chunk - 1) / a.chunk;
+  if (grid == 0) return hipSuccess;
+  return a.row_bytes % 16u == 0 ? launch_scatter_u<u32x4>(a, (uint32_t)grid, s)
+                                : launch_scatter_u<uint32_t>(a, (uint32_t)grid, s);
 }
 
 hipError_t launch_b(const ExchangeArgs& a, hipStream_t s) {

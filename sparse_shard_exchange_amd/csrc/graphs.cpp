@@ -247,6 +247,10 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done,
   a.ctl = m.ctl;
   a.tile_base = reinterpret_cast<uint32_t*>(base + L.tile_base);
   a.blk_base = reinterpret_cast<uint32_t*>(base + L.blk_base);
+  a.tile_cnt = reinterpret_cast<uint32_t*>(base + L.tile_cnt);
+  a.tile_done = reinterpret_cast<uint32_t*>(base + L.tile_done);
+  a.rank = reinterpret_cast<uint16_t*>(base + L.rank);
+  a.chunk = scatter_chunk(L.tile, a.row_bytes);
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
 
   hipError_t e = hipSuccess;
@@ -260,7 +264,7 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done,
   if (ph != Phase::kEnd) {
     PW_STEP("router", launch_router(m, s));
     if (io->counts) PW_STEP("src_counts", launch_src_counts(a, s));
-    PW_STEP("hist", launch_hist(a, s));
+    PW_STEP("rank", launch_rank(a, s));
     PW_STEP("scan", launch_scan(a, s));
     if (ph == Phase::kBegin) return finish_begin(p, io, s, offsets_host);
   }

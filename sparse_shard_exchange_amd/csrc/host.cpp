@@ -120,6 +120,9 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
       L.seg = c.take((size_t)(N + 1) * 8);
       L.tile_base = c.take((size_t)N * L.num_tiles * 4);
       L.blk_base = c.take((size_t)N * L.num_blk * 4);
+      L.tile_cnt = c.take((size_t)N * L.num_tiles * 4);
+      L.tile_done = c.take((size_t)L.num_tiles * 4);
+      L.rank = c.take(L.G * 2);
       if (d.kind == PW_GRAPH_MOE) {
         const uint64_t tokens = (uint64_t)S * d.tuples_per_shard;
         L.experts = c.take(tokens * d.top_k * 4);
@@ -457,6 +460,10 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   a.ctl = reinterpret_cast<uint32_t*>(base + L.ctl + 64);
   a.tile_base = reinterpret_cast<uint32_t*>(base + L.tile_base);
   a.blk_base = reinterpret_cast<uint32_t*>(base + L.blk_base);
+  a.tile_cnt = reinterpret_cast<uint32_t*>(base + L.tile_cnt);
+  a.tile_done = reinterpret_cast<uint32_t*>(base + L.tile_done);
+  a.rank = reinterpret_cast<uint16_t*>(base + L.rank);
+  a.chunk = scatter_chunk(L.tile, row);
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
 
   hipError_t e = hipSuccess;
@@ -467,10 +474,10 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
       p->launch_end(s);
       if (e != hipSuccess) return hip_fail(e, "launch src_counts");
     }
-    p->launch_begin("hist", s);
-    e = launch_hist(a, s);
+    p->launch_begin("rank", s);
+    e = launch_rank(a, s);
     p->launch_end(s);
-    if (e != hipSuccess) return hip_fail(e, "launch hist");
+    if (e != hipSuccess) return hip_fail(e, "launch rank");
     p->launch_begin("scan", s);
     e = launch_scan(a, s);
     p->launch_end(s);

@@ -59,6 +59,10 @@ struct ExchangeArgs {
   uint32_t* ctl;              // [0] result count, [1] scan done count
   uint32_t* tile_base;        // [num_tiles][N]: counts, then run starts inside the scan block
   uint32_t* blk_base;         // [num_blk][N]: block totals, then run starts inside the segment
+  uint32_t* tile_cnt;         // [num_tiles][N]: counts (kept for the arrival counters)
+  uint32_t* tile_done;        // [num_tiles]: scatter chunks finished
+  uint16_t* rank;             // [G]: rank of tuple g among its tile's tuples with the same destination
+  uint32_t chunk;             // tuples per scatter workgroup (a power of two dividing the tile)
   int64_t* seg;               // [N+1]
 };
 
@@ -122,12 +126,12 @@ struct MoeArgs {
 };
 
 // Launchers (exchange.hip).
-hipError_t launch_hist(const ExchangeArgs& a, hipStream_t s);
+hipError_t launch_rank(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_src_counts(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_b(const ExchangeArgs& a, hipStream_t s);
-size_t scatter_lds_bytes(uint32_t N, bool cap);
+uint32_t scatter_chunk(uint32_t tile, uint32_t row_bytes);
 // mode: 0 chained (one launch, all steps), 1 one node (OpByOp), 2 fused.
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);
 hipError_t launch_pipeline(const PipeArgs& a, uint32_t grid, hipStream_t s);

@@ -24,6 +24,9 @@ struct Layout {
   size_t seg = 0;         // [N+1] i64 segment offsets
   size_t tile_base = 0;   // [num_tiles][N] u32
   size_t blk_base = 0;    // [num_blk][N] u32
+  size_t tile_cnt = 0;    // [num_tiles][N] u32
+  size_t tile_done = 0;   // [num_tiles] u32
+  size_t rank = 0;        // [G] u16
   size_t experts = 0, gates = 0, slot_of = 0, hidden_act = 0;  // MOE
   size_t rb_start = 0, b_done = 0;                              // MOE
   size_t w1t = 0, w2t = 0, wrt = 0;  // packed (K-contiguous) weights: MOE W1^T, W2^T, W_r^T; PIPELINE W^T in w1t
