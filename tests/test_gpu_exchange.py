@@ -72,8 +72,9 @@ CASES = [
     (64, 300, 64, "reversed"),
     (2048, 50, 4, "uniform"),
     (2048, 33, 4, "zipf4"),
-    (8192, 3, 4, "uniform"),      # the most shards a plan takes: the scatter's LDS is then exactly 160 KiB
+    (8192, 3, 4, "uniform"),      # the most shards a plan takes: the ranking kernel's LDS is then 128 KiB
     (8192, 2, 64, "half_empty"),
+    (4, 10, 8192, "uniform"),     # 32 KiB rows: one tuple per scatter workgroup, two copy batches each
 ]
 
 
@@ -95,6 +96,23 @@ def test_exchange_parity(gpu, n, t, p, kind):
     assert np.all(ep[pw.PW_NODE_EXCHANGE, :n] == 1) and np.all(fi[pw.PW_NODE_EXCHANGE, :n] == 1)
     assert np.all(ep[pw.PW_NODE_B, :n] == 1) and np.all(fi[pw.PW_NODE_B, :n] == 1)
     assert ep[pw.PW_NODE_RESULT, 0] == 1 and fi[pw.PW_NODE_RESULT, 0] == 1
+
+
+def test_tiny_rows_full_size_chunks(gpu):
+    """16.7 M tuples of one fp32: 4096-tuple tiles and the largest scatter
+    chunk (1024 tuples per workgroup, 4 per tile)."""
+    pw = gpu
+    n, t = 64, 262144
+    print(f"exchange tiny rows N={n} T={t} P=1", flush=True)
+    x = torch.from_numpy(pw_inputs.exchange_uniform(n, t, 1).x)
+    dest = _dest_case("zipf4", n, t)
+    ex, _ = run(pw, x, dest, n, t)
+    ref = ox.exchange_step(x.numpy(), dest, n, n)
+    assert np.array_equal(ex.offsets.cpu().numpy(), ref.offsets)
+    assert np.array_equal(ex.src_index.cpu().numpy(), ref.src_index.astype(np.int32))
+    assert np.array_equal(_bits(ex.dst), ref.y.view(np.uint32))
+    ep, fi, _ = ex.plan.read_futures()
+    assert np.all(fi[pw.PW_NODE_EXCHANGE, :n] == 1) and fi[pw.PW_NODE_RESULT, 0] == 1
 
 
 def test_small_workload_a_and_b(gpu):
