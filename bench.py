@@ -1,6 +1,6 @@
 """Benchmark of the sharded-dataflow hot path on one MI355X.
 
-A step is one pass of Arg -> A -> sparse exchange (histogram, scan, stable
+A step is one pass of Arg -> A -> sparse exchange (ranking, scan, stable
 scatter, progress futures) -> B -> Result over the large exchange workload:
 256 shards x 65536 tuples, 64 fp32 payload ~ N(0, 1), each source sending to
 4 destinations drawn with Zipf(1.1) weights (A and B are identities). Inputs
@@ -13,7 +13,10 @@ synchronisations). `roofline` prices the dominant kernel (the scatter) at its
 algorithmic bytes (520 B per tuple: 256 B payload read + 256 B written, 4 B
 destination read, 4 B source index written) over its mean HIP-event duration
 in the timed region, against the 8 TB/s HBM peak. `cpu_baseline` times the
-CPU oracle (single-threaded NumPy) on the same workload.
+CPU oracle (single-threaded NumPy) on the same workload. Further sections:
+`inputs` (versions, SHA-256 of the inputs), `small_step` (the 8-shard step
+with A and B, warm and cold), `pipeline`, `moe`, the chain sweep, the vendor
+references, and the optional studies.
 """
 from __future__ import annotations
 
@@ -250,6 +253,58 @@ def multi_tenant(pw, torch, pw_inputs, point_s=1.5, target_ms=0.33):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def small_step_bench(pw, torch, pw_inputs, iters=50, cold_iters=20):
+    """The 8-shard step (8 x 4096 tuples x 64 fp32, A = 2x + 1, exchange,
+    B = per-tuple sum): 25.6 MB per step, cache-resident and launch-latency
+    bound. Timed warm (steps back to back) and cold (a 512 MiB write before
+    each step evicts the 256 MB last-level cache)."""
+    n, t, p = 8, 4096, 64
+    inp = pw_inputs.exchange_uniform(n, t, p)
+    x = torch.from_numpy(inp.x).cuda()
+    dest = torch.from_numpy(inp.dest).cuda()
+    ex = pw.Exchange(n, t, p, a_op=pw.op(pw.PW_OP_AFFINE, 2.0, 1.0), b_op=pw.op(pw.PW_OP_ROWSUM))
+    for _ in range(5):
+        f = ex.step(x, dest)
+    pw.future_wait(f, 60_000_000_000)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(iters):
+        f = ex.step(x, dest)
+    e1.record(st)
+    torch.cuda.synchronize()
+    pw.future_wait(f, 60_000_000_000)
+    warm_us = e0.elapsed_time(e1) / iters * 1e3
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(cold_iters):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        f = ex.step(x, dest)
+        b.record(st)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b) * 1e3)
+    pw.future_wait(f, 60_000_000_000)
+    cold.sort()
+    g = n * t
+    return {"workload": "8 shards x 4096 tuples x 64 fp32 ~U(-1,1), dest uniform, A = 2x+1, B = per-tuple sum",
+            "us_per_step_warm": warm_us, "us_per_step_cold_median": cold[len(cold) // 2],
+            "tuples_per_s_warm": g / (warm_us * 1e-6), "bytes_per_tuple_step": 780,
+            "gbs_warm_algorithmic": 780 * g / (warm_us * 1e-6) / 1e9}
+
+
+def input_record(np, torch, arrays):
+    """numpy / torch versions and the SHA-256 of each generated input array."""
+    rec = {"numpy": np.__version__, "torch": torch.__version__}
+    for name, a in arrays.items():
+        a = np.ascontiguousarray(a)
+        rec[name] = {"shape": list(a.shape), "dtype": str(a.dtype),
+                     "sha256": hashlib.sha256(memoryview(a).cast("B")).hexdigest()}
+    return rec
 
 
 def pipeline_bench(pw, torch, pw_inputs, passes=3):
@@ -613,6 +668,9 @@ def main():
         },
     }
 
+    result["inputs"] = input_record(np, torch, {"x": inp.x, "dest": inp.dest})
+    log("small step")
+    result["small_step"] = small_step_bench(pw, torch, pw_inputs)
     if not args.no_pipeline:
         log("pipeline")
         result["pipeline"] = pipeline_bench(pw, torch, pw_inputs)
