@@ -56,7 +56,7 @@ extern "C" {
 #define PW_ERR_BAD_DEST     -5  /* a tuple named a destination outside [0, N); the
                                    kernels dropped it                                 */
 #define PW_ERR_STATE        -6  /* wrong call order (stale future, destroyed plan, ...) */
-#define PW_ERR_UNSUPPORTED  -7  /* valid request this build does not implement          */
+#define PW_ERR_UNSUPPORTED  -7  /* a valid request the library does not implement         */
 
 /* ---- element types ------------------------------------------------------- */
 typedef enum { PW_F32 = 0, PW_BF16 = 1 } pw_dtype;

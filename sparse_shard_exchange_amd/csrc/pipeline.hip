@@ -118,7 +118,7 @@ __device__ __forceinline__ bool input_ready(const PipeArgs& a, const PipeTile& p
 
 struct Claims {
   uint32_t next;   // the ticket after the current candidate (thread 0 writes it)
-  uint32_t ready;  // thread 0's verdict on the candidate
+  uint32_t ready;  // thread 0's answer: is the candidate's input complete
 };
 
 // Thread 0's claim pipeline. A claim is an atomic add on a queue counter
