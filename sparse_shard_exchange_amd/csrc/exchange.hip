@@ -274,11 +274,6 @@ __device__ __forceinline__ uint32_t apply_a<uint32_t>(uint32_t v, const Exchange
 constexpr uint32_t kMaxChunk = 1024;
 constexpr uint32_t kCopyBatch = 4;  // units per thread loaded before any is stored (16 KiB per workgroup)
 
-// One workgroup per chunk of a.chunk consecutive tuples (inside one tile).
-// Unit U is 16 bytes when rows are a multiple of 16 bytes, else 4 bytes.
-// kCap: each destination keeps its first `capacity` tuples in tuple order:
-// a tuple is kept if its rank inside the destination is below the capacity;
-// a dropped tuple moves nothing and its slot_of is -1.
 // The payload units of one batch (kCopyBatch per thread) of the chunk: unit
 // i is unit i % vu of tuple i / vu. Source rows do not depend on the slots.
 template <typename U>
