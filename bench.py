@@ -514,7 +514,17 @@ def cpu_other_rows(pw_inputs, pipeline=True, moe=True):
     workload (reported beside the GPU numbers, never a target)."""
     import numpy as np
     from oracle import chain as oc
+    from oracle import exchange as ox
     out = {}
+    small = pw_inputs.exchange_uniform(8, 4096, 64)
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ox.exchange_step(small.x, small.dest, 8, 8, a_op=ox.op_affine(2.0, 1.0), b_op=ox.op_rowsum())
+    dt = (time.perf_counter() - t0) / reps
+    out["small_step"] = {"value": 8 * 4096 / dt, "unit": "tuples/s", "cores": 1,
+                         "sample": f"the whole 8 x 4096 x 64 step with A = 2x+1 and B = row sum "
+                                   f"(oracle.exchange.exchange_step, NumPy), mean of {reps}: {dt * 1e3:.2f} ms"}
     x0 = pw_inputs.chain_state(2048, 128)
     steps = 1000
     t0 = time.perf_counter()
