@@ -411,7 +411,8 @@ __device__ __forceinline__ uint32_t segment_of(const int64_t* seg, uint32_t N, i
   return lo;
 }
 
-constexpr uint32_t kBRows = 256;  // output slots per B workgroup
+constexpr uint32_t kBRows = 64;  // output slots per B workgroup
+constexpr uint32_t kBPasses = kBRows / 16;  // row sum: 16 rows of 16 lanes per pass
 
 __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
   __shared__ uint32_t range[2];
@@ -435,33 +436,40 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
   const float* y = reinterpret_cast<const float*>(a.dst);
   float* out = reinterpret_cast<float*>(a.b_out);
   if (a.b_kind == OP_ROWSUM) {
-    // 16 lanes per row, 16 rows per pass of the workgroup
+    // 16 lanes per row, 16 rows per pass; the passes are unrolled so that
+    // every lane's loads of all of them are in flight together
     const uint32_t l16 = threadIdx.x & 15, r = threadIdx.x >> 4;
     const bool vec = (P % 4u) == 0;
-    const int64_t passes = (s1 - s0 + 15) / 16;
-    for (int64_t p = 0; p < passes; ++p) {
+    float acc[kBPasses];
+#pragma unroll
+    for (uint32_t p = 0; p < kBPasses; ++p) {
       const int64_t s = s0 + p * 16 + r;
-      float acc = 0.f;
-      const bool in = s < s1;
-      if (in) {
+      acc[p] = 0.f;
+      if (s < s1) {
         const float* row = y + s * (int64_t)P;
         if (vec) {
           for (uint32_t e = l16; e < P / 4u; e += 16) {
             const float4 v = reinterpret_cast<const float4*>(row)[e];
-            acc += (v.x + v.y) + (v.z + v.w);
+            acc[p] += (v.x + v.y) + (v.z + v.w);
           }
         } else {
-          for (uint32_t e = l16; e < P; e += 16) acc += row[e];
+          for (uint32_t e = l16; e < P; e += 16) acc[p] += row[e];
         }
       }
-      acc += __shfl_xor(acc, 8, 16);
-      acc += __shfl_xor(acc, 4, 16);
-      acc += __shfl_xor(acc, 2, 16);
-      acc += __shfl_xor(acc, 1, 16);
-      if (in && l16 == 0) out[s] = acc;
+    }
+#pragma unroll
+    for (uint32_t p = 0; p < kBPasses; ++p) {
+      float x = acc[p];
+      x += __shfl_xor(x, 8, 16);
+      x += __shfl_xor(x, 4, 16);
+      x += __shfl_xor(x, 2, 16);
+      x += __shfl_xor(x, 1, 16);
+      const int64_t s = s0 + p * 16 + r;
+      if (s < s1 && l16 == 0) out[s] = x;
     }
   } else if (a.b_kind == OP_AFFINE) {
     const int64_t n = (s1 - s0) * (int64_t)P;
+#pragma unroll 4
     for (int64_t i = threadIdx.x; i < n; i += kBlock) {
       const int64_t k = s0 * (int64_t)P + i;
       out[k] = fmaf(a.b_a, y[k], a.b_b);
