@@ -273,7 +273,8 @@ int pw_exchange_end(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_f
  * of tuples_per_shard fp32, one tuple per shard, identity routing). The
  * Result of step k is the Arg of step k + 1; on return of the device work
  * `state` holds the last Result. `aux` (nullable, device, same shape as state)
- * receives A's last output. Mode per plan (chain_mode).
+ * receives A's last output. Mode per plan (chain_mode). `state->base` and
+ * `aux` must be 16-byte aligned (else PW_ERR_INVALID).
  * PIPELINE: steps must be 1. `state` holds the M microbatches [M][rows][d]
  * bf16; `aux` (device, required) receives every stage output [S][M][rows][d]
  * bf16. Item (s, m) runs after (s-1, m) fired its future and after (s, m-1).

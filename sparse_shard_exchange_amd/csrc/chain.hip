@@ -9,11 +9,13 @@
 // over in one message; section 4.3: under data parallelism each of the N
 // shards sends one tuple to the same shard of the next node.
 //
-// Device mapping: one wave per shard. The plan fixes the placement before the
-// chain starts, so the producer of every future (A[i] of step k, B[i] of step
-// k) and its consumer (B[i] of step k, A[i] of step k + 1) run on the same
-// wave: the gate is a load of the HBM future table ordered after the
-// producer's stores by program order, with no cross-CU fence. Node outputs
+// Device mapping: one group of lanes per shard (the whole wave, or with
+// 128-element shards and many shards half of it, so that the CUs hold fewer
+// waves). The plan fixes the placement before the chain
+// starts, so the producer of every future (A[i] of step k, B[i] of step k)
+// and its consumer (B[i] of step k, A[i] of step k + 1) run on the same lanes:
+// the gate is a load of the HBM future table ordered after the producer's
+// stores by program order, with no cross-CU fence. Node outputs
 // live in HBM buffers (state for B, a_buf for A), as the page's object store
 // keeps them in accelerator memory.
 #include "device.h"
@@ -26,11 +28,11 @@ __device__ __forceinline__ float body(uint32_t kind, float a, float b, float x) 
   return kind == OP_AFFINE ? fmaf(a, x, b) : x;
 }
 
-// Gate on a future this wave produced itself. Lane 0 both fires and reads
-// every future of its shard, so program order makes the fire visible to the
-// read and a relaxed load suffices; each lane only reads payload elements it
-// wrote itself. The result is broadcast to the wave. Bounded like every
-// device wait.
+// Gate on a future these lanes produced themselves. The first lane of the
+// shard's group both fires and reads every future of its shard, so program
+// order makes the fire visible to the read and a relaxed load suffices; each
+// lane only reads payload elements it wrote itself. The result is broadcast
+// to the group. Bounded like every device wait.
 __device__ __forceinline__ bool await_local_lane0(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
   const uint32_t* p = &f.epoch[node * f.width + shard];
   if (epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT), epoch)) return true;
@@ -45,15 +47,18 @@ __device__ __forceinline__ bool await_local_lane0(const Futures& f, uint32_t nod
   }
 }
 
+// `sub` is the lane's index inside its shard's lane group, `lead` the group's
+// first lane (0 when the whole wave serves one shard).
 __device__ __forceinline__ bool await_local(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch,
-                                            uint32_t lane) {
+                                            uint32_t sub, uint32_t lead = 0) {
   bool ok = true;
-  if (lane == 0) ok = await_local_lane0(f, node, shard, epoch);
-  return __shfl((int)ok, 0, 64) != 0;
+  if (sub == 0) ok = await_local_lane0(f, node, shard, epoch);
+  return __shfl((int)ok, (int)lead, 64) != 0;
 }
 
-__device__ __forceinline__ void finish_wave(const ChainArgs& a, uint32_t lane) {
-  if (lane == 0) {
+// One count per shard; the last of them fires the Result.
+__device__ __forceinline__ void finish_shard(const ChainArgs& a, uint32_t sub) {
+  if (sub == 0) {
     const uint32_t old = __hip_atomic_fetch_add(a.done_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1 == a.done_target) fire(a.f, NODE_RESULT, 0, a.epoch0 + a.steps, false);
   }
@@ -72,64 +77,70 @@ __device__ __forceinline__ void node_body(const float* in, float* out, uint32_t 
   if (e < E) out[e] = body(kind, ca, cb, in[e]);
 }
 
-// Fire a future whose only consumer is this wave (lane 0 calls it): a plain
-// store; the fire count and the stamp are kept in registers by the caller and
+// Fire a future whose only consumer is this lane group (its first lane calls
+// it): a plain store; the fire count and the stamp are kept in registers by the caller and
 // written once when the launch ends.
 __device__ __forceinline__ void fire_local(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
   __hip_atomic_store(&f.epoch[node * f.width + shard], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
-// One node of one shard with the gate folded in: lane 0 reads the input
-// future while every lane reads its input elements; the elements are used
-// only once the future is known to have fired (else they are read again
-// after the wait).
+// One node of one shard with the gate folded in: the group's first lane reads
+// the input future while every lane reads its input elements; the elements are
+// used only once the future is known to have fired (else they are read again
+// after the wait). With 128-element shards each of the 64/kG lanes of a group
+// owns 2·kG consecutive elements; other sizes use a whole wave (kG = 1).
+template <int kG>
 __device__ __forceinline__ bool gated_node(const ChainArgs& a, uint32_t in_node, uint32_t shard, uint32_t need,
-                                           const float* in, float* out, uint32_t lane, uint32_t kind, float ca,
-                                           float cb) {
+                                           const float* in, float* out, uint32_t sub, uint32_t lead, uint32_t kind,
+                                           float ca, float cb) {
   uint32_t v = need;
-  if (lane == 0) v = __hip_atomic_load(&a.f.epoch[in_node * a.f.width + shard], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
-  if (a.E == 128) {
-    float2 x = reinterpret_cast<const float2*>(in)[lane];
-    const bool ready = __shfl((int)epoch_reached(v, need), 0, 64) != 0;
+  if (sub == 0) v = __hip_atomic_load(&a.f.epoch[in_node * a.f.width + shard], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WAVEFRONT);
+  if (kG > 1 || a.E == 128) {
+    using V = float __attribute__((ext_vector_type(2 * kG)));
+    V x = reinterpret_cast<const V*>(in)[sub];
+    const bool ready = __shfl((int)epoch_reached(v, need), (int)lead, 64) != 0;
     if (!ready) {
-      if (!await_local(a.f, in_node, shard, need, lane)) return false;
-      x = reinterpret_cast<const float2*>(in)[lane];
+      if (!await_local(a.f, in_node, shard, need, sub, lead)) return false;
+      x = reinterpret_cast<const V*>(in)[sub];
     }
-    x.x = body(kind, ca, cb, x.x);
-    x.y = body(kind, ca, cb, x.y);
-    reinterpret_cast<float2*>(out)[lane] = x;
+#pragma unroll
+    for (int e = 0; e < 2 * kG; ++e) x[e] = body(kind, ca, cb, x[e]);
+    reinterpret_cast<V*>(out)[sub] = x;
     return true;
   }
   const bool ready = __shfl((int)epoch_reached(v, need), 0, 64) != 0;
-  if (!ready && !await_local(a.f, in_node, shard, need, lane)) return false;
-  node_body(in, out, a.E, lane, kind, ca, cb);
+  if (!ready && !await_local(a.f, in_node, shard, need, sub)) return false;
+  node_body(in, out, a.E, sub, kind, ca, cb);
   return true;
 }
 
+template <int kG>
 __global__ __launch_bounds__(256) void k_chain_chained(ChainArgs a) {
-  const uint32_t i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (i >= a.N) return;  // whole waves only; no workgroup barrier below
+  constexpr uint32_t kLanes = 64 / kG;
+  const uint32_t lane = threadIdx.x & 63, sub = lane % kLanes, lead = lane - sub;
+  const uint32_t i = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kG + lane / kLanes;
+  if (i >= a.N) return;  // whole lane groups only; no workgroup barrier below
   float* st = a.state + (uint64_t)i * a.E;
   float* ab = a.abuf + (uint64_t)i * a.E;
   uint32_t done = 0;
   for (uint32_t j = 1; j <= a.steps; ++j) {
     const uint32_t k = a.epoch0 + j;
     // A of step k consumes the Result of step k - 1 (B[i]; epoch0 = the Arg)
-    if (!gated_node(a, NODE_B, i, k - 1, st, ab, lane, a.a_kind, a.a_a, a.a_b)) break;
-    if (lane == 0) fire_local(a.f, NODE_A, i, k);
-    if (!gated_node(a, NODE_A, i, k, ab, st, lane, a.b_kind, a.b_a, a.b_b)) break;
-    if (lane == 0) fire_local(a.f, NODE_B, i, k);
+    if (!gated_node<kG>(a, NODE_B, i, k - 1, st, ab, sub, lead, a.a_kind, a.a_a, a.a_b)) break;
+    if (sub == 0) fire_local(a.f, NODE_A, i, k);
+    if (!gated_node<kG>(a, NODE_A, i, k, ab, st, sub, lead, a.b_kind, a.b_a, a.b_b)) break;
+    if (sub == 0) fire_local(a.f, NODE_B, i, k);
     done = j;
   }
-  if (lane == 0 && done) {
+  if (sub == 0 && done) {
     for (uint32_t node : {NODE_A, NODE_B}) {
       const uint32_t idx = node * a.f.width + i;
       __hip_atomic_fetch_add(&a.f.fires[idx], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (a.f.stamps) a.f.stamps[idx] = wall_clock64();
     }
   }
-  finish_wave(a, lane);
+  finish_shard(a, sub);
 }
 
 // OpByOp: one launch per node per step. The input future was fired by the
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(256) void k_chain_node(ChainArgs a) {
     if (!await_local(a.f, NODE_A, i, k, lane)) return;
     node_body(ab, st, a.E, lane, a.b_kind, a.b_a, a.b_b);
     if (lane == 0) fire(a.f, NODE_B, i, k, false);
-    if (a.done_ctr) finish_wave(a, lane);
+    if (a.done_ctr) finish_shard(a, lane);
   }
 }
 
@@ -173,16 +184,28 @@ __global__ __launch_bounds__(256) void k_chain_fused(ChainArgs a) {
     fire(a.f, NODE_A, i, a.epoch0 + a.steps, false);
     fire(a.f, NODE_B, i, a.epoch0 + a.steps, false);
   }
-  finish_wave(a, lane);
+  finish_shard(a, lane);
 }
 
 }  // namespace
 
+// Shards per wave for the chained kernel. A gated node's latency grows with
+// the waves a CU holds (measured, one shard per wave: ~300 ns per node up to
+// 4 waves per CU, ~375 at 8, ~415 at 16). Two 128-element shards per wave
+// cost ~350 ns at 2048 shards and ~390 at 4096, but ~350 already at 1024, so
+// only large shard counts pack them; four per wave were slower (~480-500).
+static uint32_t chain_pack(uint32_t N, uint32_t E) { return E == 128 && N > 1536 ? 2 : 1; }
+
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s) {
   const dim3 grid((a.N + 3) / 4), block(256);
-  if (mode == 0)
-    hipLaunchKernelGGL(k_chain_chained, grid, block, 0, s, a);
-  else if (mode == 2)
+  if (mode == 0) {
+    const uint32_t g = chain_pack(a.N, a.E), waves = (a.N + g - 1) / g;
+    const dim3 cgrid((waves + 3) / 4);
+    if (g == 2)
+      hipLaunchKernelGGL(k_chain_chained<2>, cgrid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(k_chain_chained<1>, cgrid, block, 0, s, a);
+  } else if (mode == 2)
     hipLaunchKernelGGL(k_chain_fused, grid, block, 0, s, a);
   else
     hipLaunchKernelGGL(k_chain_node, grid, block, 0, s, a);

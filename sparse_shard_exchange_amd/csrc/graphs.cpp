@@ -291,6 +291,8 @@ int run_chain(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStre
     return fail(PW_ERR_INVALID, "state must be %u shards x one tuple of %llu fp32", d.num_shards,
                 (unsigned long long)d.tuples_per_shard);
   if (steps == 0) return fail(PW_ERR_INVALID, "steps must be >= 1");
+  if ((uintptr_t)state->base % 16 || (uintptr_t)aux % 16)
+    return fail(PW_ERR_INVALID, "state and aux must be 16-byte aligned");
   if (p->epoch + steps > 0x7fffffffull) return fail(PW_ERR_INVALID, "epoch would pass 2^31");
   int st = p->begin_call(s);
   if (st) return st;

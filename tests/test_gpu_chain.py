@@ -108,3 +108,38 @@ def test_chain_rejects_bad_state(gpu):
     with pytest.raises(pw.PwError) as e:
         ch.run(st, 1)
     assert e.value.code == pw.PW_ERR_INVALID
+
+
+@pytest.mark.parametrize("n", [1537, 2049, 4099])
+def test_chain_packed_shards_bit_exact(gpu, n):
+    """Shard counts where a wave serves two shards of 128 elements, with a
+    ragged last wave: 40 steps and the fire counts equal the oracle's."""
+    pw = gpu
+    print(f"chain packed N={n}", flush=True)
+    x0 = pw_inputs.chain_state(n, 128)
+    ref = oc.chain(x0, 40, record=40)
+    ch = pw.Chain(n, 128, mode=pw.PW_CHAIN_CHAINED)
+    st = torch.from_numpy(x0).cuda()
+    f = ch.run(st, 3)
+    pw.future_wait(f, 10_000_000_000)
+    assert np.array_equal(st.cpu().numpy().view(np.uint32), ref.history[2].view(np.uint32))
+    aux = torch.empty_like(st)
+    f = ch.run(st, 37, aux=aux)
+    pw.future_wait(f, 10_000_000_000)
+    assert f.epoch == 40
+    assert np.array_equal(st.cpu().numpy().view(np.uint32), ref.state.view(np.uint32))
+    last_a = ref.history[38] + np.float32(1)          # A of step 40 reads the Result of step 39
+    assert np.array_equal(aux.cpu().numpy().view(np.uint32), last_a.view(np.uint32))
+    ep, fi, _ = ch.plan.read_futures()
+    assert np.all(ep[pw.PW_NODE_A, :n] == 40) and np.all(ep[pw.PW_NODE_B, :n] == 40)
+    assert np.all(fi[pw.PW_NODE_A, :n] == 40) and np.all(fi[pw.PW_NODE_B, :n] == 40)
+    assert ep[pw.PW_NODE_RESULT, 0] == 40 and fi[pw.PW_NODE_RESULT, 0] == 2
+
+
+def test_chain_rejects_misaligned_state(gpu):
+    pw = gpu
+    ch = pw.Chain(8, 128)
+    flat = torch.zeros(8 * 128 + 1, device="cuda")
+    with pytest.raises(pw.PwError) as e:
+        ch.run(flat[1:].view(8, 128), 1)
+    assert e.value.code == pw.PW_ERR_INVALID
