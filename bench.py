@@ -492,7 +492,9 @@ def reference_bench(torch, iters=10):
     out = {"note": "vendor BLAS via torch on the same device, for context only",
            "pipeline_stage_gemm_gelu": gemm(64, 2048, 1024, 1024, True),
            "pipeline_stage_gemm": gemm(64, 2048, 1024, 1024, False),
-           "ffn2_like_gemm": gemm(64, 4096, 4096, 1024, False)}
+           "ffn2_like_gemm": gemm(64, 4096, 4096, 1024, False),
+           # the measured dense-GEMM rate beside the published 2.5 PFLOP/s
+           "square_8192_gemm": gemm(1, 8192, 8192, 8192, False)}
     x = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
     y = torch.empty_like(x)
     for _ in range(3):

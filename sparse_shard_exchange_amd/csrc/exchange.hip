@@ -82,6 +82,92 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return pre + x - v;
 }
 
+// ------------------------------------------------------------ scan helpers
+// Exclusive running sum, in place, of the column d of rows [r0, r1) of a
+// row-major [rows][N] table; returns the column total. The loads of 16 rows
+// are issued before any is needed.
+__device__ __forceinline__ uint32_t column_scan(uint32_t* t, uint32_t N, uint32_t d, uint32_t r0, uint32_t r1) {
+  constexpr uint32_t kB = 16;
+  uint32_t run = 0;
+  for (uint32_t r = r0; r < r1; r += kB) {
+    uint32_t v[kB];
+#pragma unroll
+    for (uint32_t u = 0; u < kB; ++u) v[u] = r + u < r1 ? t[(uint64_t)(r + u) * N + d] : 0u;
+#pragma unroll
+    for (uint32_t u = 0; u < kB; ++u) {
+      if (r + u < r1) t[(uint64_t)(r + u) * N + d] = run;
+      run += v[u];
+    }
+  }
+  return run;
+}
+
+// Workgroup-shared state of the scan's last step.
+struct ScanShared {
+  uint32_t wsum[kWaves];
+  uint32_t zero_count[kWaves];
+  uint32_t is_last;
+};
+
+// True in the last workgroup of the grid to get here (counter ctl[1], reset
+// by scan_finish); its writes before the call are then visible to that one.
+__device__ __forceinline__ bool last_to_arrive(const ExchangeArgs& a, ScanShared& sh) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) sh.is_last = atomicAdd(&a.ctl[1], 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!sh.is_last) return false;
+  __threadfence();
+  return true;
+}
+
+// The scan's last step, in one workgroup, once expected[d] (the tuples d
+// keeps) is known for every destination (exp_of(d) reads it): segment
+// offsets, the arrival counters cleared, and the futures of destinations
+// that receive nothing fired now.
+template <typename ExpOf>
+__device__ __forceinline__ void scan_finish(const ExchangeArgs& a, ScanShared& sh, ExpOf exp_of) {
+  const uint32_t N = a.N;
+  const uint32_t per = (N + kBlock - 1) / kBlock;
+  const uint32_t lo = min(N, threadIdx.x * per), hi = min(N, lo + per);
+  uint32_t local = 0;
+  for (uint32_t d = lo; d < hi; ++d) local += exp_of(d);
+  uint32_t total;
+  const uint32_t ex = block_exclusive_scan(local, sh.wsum, total);
+  int64_t run = ex;
+  uint32_t zeros = 0;
+  for (uint32_t d = lo; d < hi; ++d) {
+    const uint32_t e = exp_of(d);
+    a.seg[d] = run;
+    if (a.offsets_out) a.offsets_out[d] = run;
+    run += e;
+    a.arrived[d] = 0;
+    a.b_arrived[d] = 0;
+    if (e == 0) {  // nothing will arrive: the input of B[d] is complete now
+      fire(a.f, NODE_EXCH, d, a.epoch, false);
+      fire(a.f, NODE_B, d, a.epoch, false);
+      ++zeros;
+    }
+  }
+  if (threadIdx.x == kBlock - 1) {
+    a.seg[N] = (int64_t)total;
+    if (a.offsets_out) a.offsets_out[N] = (int64_t)total;
+  }
+  // count the destinations completed here
+  uint32_t z = zeros;
+#pragma unroll
+  for (uint32_t o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+  if ((threadIdx.x & 63) == 0) sh.zero_count[threadIdx.x >> 6] = z;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t zt = 0;
+    for (uint32_t i = 0; i < kWaves; ++i) zt += sh.zero_count[i];
+    __hip_atomic_store(&a.ctl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
+    __hip_atomic_store(&a.ctl[0], zt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // B futures fired
+    if (zt == N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+  }
+}
+
 // --------------------------------------------------------------------- rank
 // A wave's destinations, loaded before any is used (up to kMaxChunks chunks
 // of 64 tuples: tile <= 4096 split over 4 waves), so that the loads of its
@@ -148,6 +234,21 @@ __global__ __launch_bounds__(kBlock) void k_rank(ExchangeArgs a) {
     }
   }
   if (bad) latch(a.f.status, ST_BAD_DEST);
+  if (!a.fuse_scan) return;
+  // Few tiles (one scan block): the last workgroup to finish ranking runs
+  // the whole scan here instead of in a launch of its own. The destination
+  // totals pass through LDS (wrun is free once every wave has ranked).
+  __shared__ ScanShared sh;
+  if (!last_to_arrive(a, sh)) return;
+  uint32_t* exp_lds = wrun;
+  for (uint32_t d = threadIdx.x; d < N; d += kBlock) {
+    const uint32_t total = column_scan(a.tile_base, N, d, 0, a.num_tiles);
+    const uint32_t e = a.capacity ? min(total, a.capacity) : total;  // the tuples d keeps
+    a.expected[d] = e;
+    exp_lds[d] = e;
+  }
+  __syncthreads();
+  scan_finish(a, sh, [&](uint32_t d) { return exp_lds[d]; });
 }
 
 // ------------------------------------------------- per-source counts export
@@ -167,29 +268,8 @@ __global__ __launch_bounds__(kBlock) void k_src_counts(ExchangeArgs a) {
 }
 
 // --------------------------------------------------------------------- scan
-// Exclusive running sum, in place, of the column d of rows [r0, r1) of a
-// row-major [rows][N] table; returns the column total. The loads of 16 rows
-// are issued before any is needed.
-__device__ __forceinline__ uint32_t column_scan(uint32_t* t, uint32_t N, uint32_t d, uint32_t r0, uint32_t r1) {
-  constexpr uint32_t kB = 16;
-  uint32_t run = 0;
-  for (uint32_t r = r0; r < r1; r += kB) {
-    uint32_t v[kB];
-#pragma unroll
-    for (uint32_t u = 0; u < kB; ++u) v[u] = r + u < r1 ? t[(uint64_t)(r + u) * N + d] : 0u;
-#pragma unroll
-    for (uint32_t u = 0; u < kB; ++u) {
-      if (r + u < r1) t[(uint64_t)(r + u) * N + d] = run;
-      run += v[u];
-    }
-  }
-  return run;
-}
-
 __global__ __launch_bounds__(kBlock) void k_scan(ExchangeArgs a) {
-  __shared__ uint32_t wsum[kWaves];
-  __shared__ uint32_t is_last;
-  __shared__ uint32_t zero_count[kWaves];
+  __shared__ ScanShared sh;
   {
     const uint32_t t0 = blockIdx.x * a.scan_tiles, t1 = min(a.num_tiles, t0 + a.scan_tiles);
     for (uint32_t d = threadIdx.x; d < a.N; d += kBlock)
@@ -197,57 +277,15 @@ __global__ __launch_bounds__(kBlock) void k_scan(ExchangeArgs a) {
   }
   // The last workgroup to finish scans the block totals and turns the
   // destination totals into segment offsets.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = atomicAdd(&a.ctl[1], 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+  if (!last_to_arrive(a, sh)) return;
   for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) {
     const uint32_t total = column_scan(a.blk_base, a.N, d, 0, a.num_blk);
     a.expected[d] = a.capacity ? min(total, a.capacity) : total;  // the tuples d keeps
   }
   __syncthreads();
-
-  const uint32_t N = a.N;
-  const uint32_t per = (N + kBlock - 1) / kBlock;
-  const uint32_t lo = min(N, threadIdx.x * per), hi = min(N, lo + per);
-  uint32_t local = 0;
-  for (uint32_t d = lo; d < hi; ++d) local += __hip_atomic_load(&a.expected[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  uint32_t total;
-  const uint32_t ex = block_exclusive_scan(local, wsum, total);
-  int64_t run = ex;
-  uint32_t zeros = 0;
-  for (uint32_t d = lo; d < hi; ++d) {
-    const uint32_t e = __hip_atomic_load(&a.expected[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.seg[d] = run;
-    if (a.offsets_out) a.offsets_out[d] = run;
-    run += e;
-    a.arrived[d] = 0;
-    a.b_arrived[d] = 0;
-    if (e == 0) {  // nothing will arrive: the input of B[d] is complete now
-      fire(a.f, NODE_EXCH, d, a.epoch, false);
-      fire(a.f, NODE_B, d, a.epoch, false);
-      ++zeros;
-    }
-  }
-  if (threadIdx.x == kBlock - 1) {
-    a.seg[N] = (int64_t)total;
-    if (a.offsets_out) a.offsets_out[N] = (int64_t)total;
-  }
-  // count the destinations completed here
-  uint32_t z = zeros;
-#pragma unroll
-  for (uint32_t o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
-  if ((threadIdx.x & 63) == 0) zero_count[threadIdx.x >> 6] = z;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t zt = 0;
-    for (uint32_t i = 0; i < kWaves; ++i) zt += zero_count[i];
-    __hip_atomic_store(&a.ctl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
-    __hip_atomic_store(&a.ctl[0], zt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // B futures fired
-    if (zt == N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
-  }
+  scan_finish(a, sh, [&](uint32_t d) {
+    return __hip_atomic_load(&a.expected[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
 }
 
 // ------------------------------------------------------------------ scatter

@@ -447,6 +447,7 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   a.num_tiles = L.num_tiles;
   a.scan_tiles = L.scan_tiles;
   a.num_blk = L.num_blk;
+  a.fuse_scan = L.num_blk == 1;
   a.nbits = ceil_log2(N);
   a.is_f32 = d.dtype == PW_F32;
   a.a_kind = d.a_op.kind; a.a_a = d.a_op.a; a.a_b = d.a_op.b;
@@ -474,14 +475,16 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
       p->launch_end(s);
       if (e != hipSuccess) return hip_fail(e, "launch src_counts");
     }
-    p->launch_begin("rank", s);
+    p->launch_begin(a.fuse_scan ? "rank_scan" : "rank", s);
     e = launch_rank(a, s);
     p->launch_end(s);
     if (e != hipSuccess) return hip_fail(e, "launch rank");
-    p->launch_begin("scan", s);
-    e = launch_scan(a, s);
-    p->launch_end(s);
-    if (e != hipSuccess) return hip_fail(e, "launch scan");
+    if (!a.fuse_scan) {
+      p->launch_begin("scan", s);
+      e = launch_scan(a, s);
+      p->launch_end(s);
+      if (e != hipSuccess) return hip_fail(e, "launch scan");
+    }
     if (ph == Phase::kBegin) return finish_begin(p, io, s, offsets_host);
   }
   p->open.active = false;

@@ -75,6 +75,8 @@ CASES = [
     (8192, 3, 4, "uniform"),      # the most shards a plan takes: the ranking kernel's LDS is then 128 KiB
     (8192, 2, 64, "half_empty"),
     (4, 10, 8192, "uniform"),     # 32 KiB rows: one tuple per scatter workgroup, two copy batches each
+    (1024, 4, 16, "zipf4"),       # <= 16 ranking tiles: the last ranking workgroup runs the scan
+    (2048, 2, 4, "uniform"),
 ]
 
 
