@@ -439,36 +439,39 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
 }
 
 // ------------------------------------------------------------------------ B
-// Largest d with seg[d] <= s (s < seg[N]).
-__device__ __forceinline__ uint32_t segment_of(const int64_t* seg, uint32_t N, int64_t s) {
-  uint32_t lo = 0, hi = N - 1;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi + 1) >> 1;
-    if (seg[mid] <= s) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 constexpr uint32_t kBRows = 64;  // output slots per B workgroup
 constexpr uint32_t kBPasses = kBRows / 16;  // row sum: 16 rows of 16 lanes per pass
 
+// B over output slots [s0, s0 + kBRows). The destinations whose non-empty
+// segments overlap those slots are found, and their exchange futures checked,
+// with one round of loads: each thread reads the segment bounds and the
+// future of the destinations it owns (d = threadIdx.x + k * kBlock), and the
+// overlapping ones (at most kBRows: each holds a slot of the range) go to an
+// LDS list. After the rows, one thread per listed destination adds its slot
+// count to the B arrivals. A segment's length is the tuple count its
+// destination keeps, so the last adder knows it completed B[d].
 __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
-  __shared__ uint32_t range[2];
-  __shared__ uint32_t go;
-  const int64_t total = a.seg[a.N];
-  const int64_t s0 = (int64_t)blockIdx.x * kBRows;
-  if (s0 >= total) return;
-  const int64_t s1 = min<int64_t>(total, s0 + kBRows);
-  if (threadIdx.x == 0) {
-    const uint32_t d0 = segment_of(a.seg, a.N, s0), d1 = segment_of(a.seg, a.N, s1 - 1);
-    bool ok = true;
-    for (uint32_t d = d0; d <= d1 && ok; ++d) ok = await_prior(a.f, NODE_EXCH, d, a.epoch);
-    range[0] = d0;
-    range[1] = d1;
-    go = ok;
-  }
+  __shared__ uint32_t n_over;
+  __shared__ uint32_t over_d[kBRows];
+  __shared__ int64_t over_lo[kBRows], over_hi[kBRows];
+  if (threadIdx.x == 0) n_over = 0;
   __syncthreads();
-  if (!go) return;
+  const int64_t s0 = (int64_t)blockIdx.x * kBRows;
+  const int64_t total = a.seg[a.N];
+  bool ok = true;
+  for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) {
+    const int64_t lo = a.seg[d], hi = a.seg[d + 1];
+    const uint32_t v = a.f.epoch[NODE_EXCH * a.f.width + d];
+    if (lo < hi && lo < s0 + kBRows && hi > s0) {
+      if (!epoch_reached(v, a.epoch)) ok = ok && await_prior(a.f, NODE_EXCH, d, a.epoch);
+      const uint32_t k = atomicAdd(&n_over, 1u);
+      over_d[k] = d;
+      over_lo[k] = lo;
+      over_hi[k] = hi;
+    }
+  }
+  if (!__syncthreads_and(ok) || s0 >= total) return;  // uniform
+  const int64_t s1 = min<int64_t>(total, s0 + kBRows);
 
   const uint32_t P = a.row_bytes / 4u;
   const float* y = reinterpret_cast<const float*>(a.dst);
@@ -514,17 +517,15 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (uint32_t d = range[0]; d <= range[1]; ++d) {
-      const int64_t lo = max<int64_t>(s0, a.seg[d]), hi = min<int64_t>(s1, a.seg[d + 1]);
-      if (hi <= lo) continue;
-      const uint32_t n = (uint32_t)(hi - lo);
-      const uint32_t old = __hip_atomic_fetch_add(&a.b_arrived[d], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old + n == a.expected[d]) {
-        fire(a.f, NODE_B, d, a.epoch, false);
-        const uint32_t r = __hip_atomic_fetch_add(&a.ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (r + 1 == a.N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
-      }
+  if (threadIdx.x < n_over) {
+    const uint32_t d = over_d[threadIdx.x];
+    const int64_t lo = max<int64_t>(s0, over_lo[threadIdx.x]), hi = min<int64_t>(s1, over_hi[threadIdx.x]);
+    const uint32_t n = (uint32_t)(hi - lo), want = (uint32_t)(over_hi[threadIdx.x] - over_lo[threadIdx.x]);
+    const uint32_t old = __hip_atomic_fetch_add(&a.b_arrived[d], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + n == want) {
+      fire(a.f, NODE_B, d, a.epoch, false);
+      const uint32_t r = __hip_atomic_fetch_add(&a.ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (r + 1 == a.N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
     }
   }
 }
