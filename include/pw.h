@@ -112,7 +112,8 @@ typedef struct {
   pw_op a_op;                /* EXCHANGE/CHAIN: A's body                                       */
   pw_op b_op;                /* EXCHANGE/CHAIN: B's body                                       */
   uint32_t top_k;            /* MOE: tuples per token (2)                                      */
-  uint32_t hidden;           /* MOE: expert FFN hidden width                                   */
+  uint32_t hidden;           /* MOE: expert FFN hidden width (multiple of 256; d = payload_elems
+                                a multiple of 256, <= 1280)                                      */
   uint32_t microbatches;     /* PIPELINE: M                                                    */
   uint32_t chain_mode;       /* CHAIN: pw_chain_mode                                           */
   uint32_t flags;            /* PW_FLAG_*                                                      */

@@ -53,8 +53,9 @@ int validate_desc_more(const pw_plan_desc* d) {
       const uint64_t S = d->num_src_shards ? d->num_src_shards : d->num_shards;
       const uint64_t tokens = S * d->tuples_per_shard;
       if (tokens == 0 || tokens > (1ull << 28)) return fail(PW_ERR_INVALID, "MOE: token count must be in [1, 2^28]");
-      if (d->payload_elems == 0 || d->payload_elems % 256 || d->payload_elems > 16384)
-        return fail(PW_ERR_INVALID, "MOE: d must be a positive multiple of 256, <= 16384");
+      // the router keeps W_r^T (64 x d bf16) in one CU's 160 KiB of LDS
+      if (d->payload_elems == 0 || d->payload_elems % 256 || d->payload_elems > 1280)
+        return fail(PW_ERR_INVALID, "MOE: d must be a positive multiple of 256, <= 1280");
       if (d->hidden == 0 || d->hidden % 256 || d->hidden > 65536)
         return fail(PW_ERR_INVALID, "MOE: hidden must be a positive multiple of 256");
       if (d->dtype != PW_BF16) return fail(PW_ERR_INVALID, "MOE: tokens and weights are bf16");

@@ -23,8 +23,10 @@ namespace pw {
 
 namespace {
 
-constexpr int kRouterTokens = 256;  // tokens per router workgroup (4 waves x 64)
+constexpr int kRouterThreads = 512;  // router workgroup: 8 waves, 2 per SIMD, one workgroup per CU
+constexpr int kRouterTokens = kRouterThreads;  // 64 tokens per wave in the GEMM, one per thread in the top-2
 constexpr int kMaxExperts = 64;
+constexpr int kRouterUnroll = 8;  // k-steps of 16 whose token loads are in flight together
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -34,16 +36,33 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 // logits (ties to the lower expert id), gates = softmax over those two.
 // LDS holds the packed W^T ([64][d], k contiguous, 16-byte chunks swizzled by
 // row), then is reused for the logits of the workgroup's tokens.
-__global__ __launch_bounds__(256, 1) void k_router(MoeArgs a) {
+__global__ __launch_bounds__(kRouterThreads, 1) void k_router(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int d = (int)a.d, E = (int)a.E;
   const int chunks = d / 8;  // 16-byte chunks per W^T row
   // packed W_r^T [64][d] (experts >= E are zero rows) -> LDS, 16-byte chunks
-  for (int i = tid; i < kMaxExperts * chunks; i += 256) {
-    const int e = i / chunks, ch = i - e * chunks;
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(a.wrt + (int64_t)e * d + ch * 8);
-    *reinterpret_cast<bf16x8*>(lds + ((int64_t)e * chunks + (ch ^ (e & 7))) * 16) = v;
+  // (16 loads per thread in flight before their LDS stores)
+  constexpr int kFill = 16;
+  for (int i0 = tid; i0 < kMaxExperts * chunks; i0 += kRouterThreads * kFill) {
+    bf16x8 v[kFill];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      const int i = i0 + u * kRouterThreads;
+      if (i < kMaxExperts * chunks) {
+        const int e = i / chunks, ch = i - e * chunks;
+        v[u] = *reinterpret_cast<const bf16x8*>(a.wrt + (int64_t)e * d + ch * 8);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      const int i = i0 + u * kRouterThreads;
+      if (i < kMaxExperts * chunks) {
+        const int e = i / chunks, ch = i - e * chunks;
+        *reinterpret_cast<bf16x8*>(lds + ((int64_t)e * chunks + (ch ^ (e & 7))) * 16) = v[u];
+      }
+    }
   }
   __syncthreads();
 
@@ -57,24 +76,36 @@ __global__ __launch_bounds__(256, 1) void k_router(MoeArgs a) {
   const int64_t r1 = min<int64_t>(t0 + 32 + (lane & 31), a.tokens - 1);
   const __bf16* x0 = a.x + r0 * d;
   const __bf16* x1 = a.x + r1 * d;
-  for (int k = 0; k < d; k += 16) {
-    const int ch = (k >> 3) + (lane >> 5);
-    const bf16x8 av0 = *reinterpret_cast<const bf16x8*>(x0 + ch * 8);
-    const bf16x8 av1 = *reinterpret_cast<const bf16x8*>(x1 + ch * 8);
-    bf16x8 bv[2];
+  // The token rows stream from HBM once: the loads of kRouterUnroll k-steps
+  // (d is a multiple of 256) are issued before their MFMAs, so each lane has
+  // 2 x kRouterUnroll 16-byte loads in flight.
+  for (int k0 = 0; k0 < d; k0 += 16 * kRouterUnroll) {
+    bf16x8 av0[kRouterUnroll], av1[kRouterUnroll];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = j * 32 + (lane & 31);
-      bv[j] = *reinterpret_cast<const bf16x8*>(lds + ((int64_t)e * chunks + (ch ^ (e & 7))) * 16);
+    for (int u = 0; u < kRouterUnroll; ++u) {
+      const int ch = ((k0 + 16 * u) >> 3) + (lane >> 5);
+      av0[u] = *reinterpret_cast<const bf16x8*>(x0 + ch * 8);
+      av1[u] = *reinterpret_cast<const bf16x8*>(x1 + ch * 8);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load above the MFMAs
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0, bv[j], acc[0][j], 0, 0, 0);
-      acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1, bv[j], acc[1][j], 0, 0, 0);
+    for (int u = 0; u < kRouterUnroll; ++u) {
+      const int ch = ((k0 + 16 * u) >> 3) + (lane >> 5);
+      bf16x8 bv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = j * 32 + (lane & 31);
+        bv[j] = *reinterpret_cast<const bf16x8*>(lds + ((int64_t)e * chunks + (ch ^ (e & 7))) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0[u], bv[j], acc[0][j], 0, 0, 0);
+        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1[u], bv[j], acc[1][j], 0, 0, 0);
+      }
     }
   }
   __syncthreads();  // every wave is done with W^T: reuse LDS for logits
-  float* lg = reinterpret_cast<float*>(lds);  // [256 tokens][65] (padded row)
+  float* lg = reinterpret_cast<float*>(lds);  // [kRouterTokens][65] (padded row)
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -360,7 +391,7 @@ hipError_t launch_router(const MoeArgs& a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)k_router, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const uint64_t blocks = (a.tokens + kRouterTokens - 1) / kRouterTokens;
-  hipLaunchKernelGGL(k_router, dim3((uint32_t)blocks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(k_router, dim3((uint32_t)blocks), dim3(kRouterThreads), lds, s, a);
   return hipGetLastError();
 }
 

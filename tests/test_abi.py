@@ -157,6 +157,26 @@ def test_chain_validation(bad):
     assert e.value.code == pw.PW_ERR_INVALID
 
 
+@pytest.mark.parametrize("bad, code", [
+    (dict(payload_elems=1536), pw.PW_ERR_INVALID),   # the router's W_r^T must fit one CU's LDS
+    (dict(payload_elems=1000), pw.PW_ERR_INVALID),
+    (dict(hidden=4000), pw.PW_ERR_INVALID),
+    (dict(top_k=1), pw.PW_ERR_UNSUPPORTED),
+    (dict(num_shards=65), pw.PW_ERR_INVALID),
+    (dict(w1=None), pw.PW_ERR_INVALID),
+    (dict(dtype=pw.PW_F32), pw.PW_ERR_INVALID),
+])
+def test_moe_validation(bad, code):
+    fake = 1 << 40  # never dereferenced: sizing is host-only
+    base = dict(kind=pw.PW_GRAPH_MOE, num_shards=64, tuples_per_shard=2048, num_src_shards=64, payload_elems=1024,
+                dtype=pw.PW_BF16, top_k=2, hidden=4096, w_router=fake, w1=fake, w2=fake)
+    assert pw.workspace_size(pw.desc(**base)) > 0
+    base.update(bad)
+    with pytest.raises(pw.PwError) as e:
+        pw.workspace_size(pw.desc(**base))
+    assert e.value.code == code
+
+
 def test_chain_sizing():
     d = pw.desc(pw.PW_GRAPH_CHAIN, 2048, 128, a_op=pw.op(pw.PW_OP_AFFINE, 1, 1))
     assert pw.workspace_size(d) >= 2048 * 128 * 4
