@@ -12,7 +12,9 @@ are resident in HBM before the timed region. One JSON line goes to stdout.
 synchronisations). `roofline` prices the dominant kernel (the scatter) at its
 algorithmic bytes (520 B per tuple: 256 B payload read + 256 B written, 4 B
 destination read, 4 B source index written) over its mean HIP-event duration
-in the timed region, against the 8 TB/s HBM peak. `cpu_baseline` times the
+in a second timed region of K steps on a plan that records events around
+every kernel (kept out of the first, whose `value` they would lower by
+~1.5%), against the 8 TB/s HBM peak. `cpu_baseline` times the
 CPU oracle (single-threaded NumPy) on the same workload. Further sections:
 `inputs` (versions, SHA-256 of the inputs), `small_step` (the 8-shard step
 with A and B, warm and cold), `pipeline`, `moe`, the chain sweep, the vendor
@@ -608,14 +610,21 @@ def main():
     x = torch.from_numpy(inp.x).cuda()
     dest = torch.from_numpy(inp.dest).cuda()
     counts = np.bincount(inp.dest, minlength=n)
-    ex = pw.Exchange(n, t, p, flags=pw.PW_FLAG_TIMING)
+    # Two plans of the same step: `ex` runs the timed steps behind `value`;
+    # `ex_k` records HIP events around every kernel (PW_FLAG_TIMING) for the
+    # per-kernel durations and the roofline, in a second timed region of the
+    # same length (the events cost ~25 us per step, so they stay out of the
+    # first).
+    ex = pw.Exchange(n, t, p)
+    ex_k = pw.Exchange(n, t, p, flags=pw.PW_FLAG_TIMING)
     torch.cuda.synchronize()
 
     log("warmup")
-    for _ in range(args.warmup):
-        f = ex.step(x, dest)
-    pw.future_wait(f, 60_000_000_000)
-    ex.plan.reset_times()
+    for plan in (ex, ex_k):
+        for _ in range(args.warmup):
+            f = plan.step(x, dest)
+        pw.future_wait(f, 60_000_000_000)
+    ex_k.plan.reset_times()
     torch.cuda.synchronize()
 
     log("timed steps")
@@ -638,7 +647,17 @@ def main():
     ms = max(ms_events, ms_wall)
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     pct = lambda q: per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))]
-    kt = ex.plan.kernel_times()
+
+    log("timed steps with kernel events")
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(args.steps):
+        f = ex_k.step(x, dest)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    pw.future_wait(f, 60_000_000_000)
+    ms_with_events = k0.elapsed_time(k1) / args.steps
+    kt = ex_k.plan.kernel_times()
     per_kernel = {k: v[1] / max(v[0], 1) for k, v in kt.items()}
     scat_ms = per_kernel["scatter"]
     achieved = BYTES_PER_TUPLE * g / (scat_ms * 1e-3) / 1e9
@@ -669,6 +688,7 @@ def main():
         "step_gbs_algorithmic": BYTES_PER_TUPLE * g / (ms * 1e-3) / 1e9,
         "step_frac_hbm_peak": BYTES_PER_TUPLE * g / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernel_ms": per_kernel,
+        "ms_per_step_with_kernel_events": ms_with_events,
         "roofline": {
             "kernel": "scatter",
             "bound": "hbm",
@@ -680,6 +700,8 @@ def main():
         },
     }
 
+    del ex, ex_k, x, dest
+    torch.cuda.empty_cache()
     result["inputs"] = input_record(np, torch, {"x": inp.x, "dest": inp.dest})
     log("small step")
     result["small_step"] = small_step_bench(pw, torch, pw_inputs)
