@@ -78,8 +78,8 @@ __device__ __forceinline__ void node_body(const float* in, float* out, uint32_t 
 }
 
 // Fire a future whose only consumer is this lane group (its first lane calls
-// it): a plain store; the fire count and the stamp are kept in registers by the caller and
-// written once when the launch ends.
+// it): a plain store; the fire count and the stamp are kept in registers by
+// the caller and written once when the launch ends.
 __device__ __forceinline__ void fire_local(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
   __hip_atomic_store(&f.epoch[node * f.width + shard], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
