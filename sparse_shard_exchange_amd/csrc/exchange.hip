@@ -556,17 +556,29 @@ hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The scatter moves rows fastest with 4 resident workgroups per CU (the
+// 160 KiB of LDS then holds 4 of them), not the 8 its registers allow:
+// 1.545-1.551 ms against 1.572-1.575 at 8, 1.571-1.575 at 6 and 1.557-1.565
+// at 3, on the large exchange. Fewer chunks in flight keep the addresses
+// being read and written in a narrower window. The launch reserves the LDS
+// that caps the count; the kernel does not use it. The MoE dispatch (fan-out
+// 2: both tuples of a token copy the same 2 KiB row, so a chunk reads half
+// the bytes it writes) is slower capped (175 against 151-163 us) and keeps
+// the register-bound count.
+constexpr size_t kScatterLdsReserve = 32 * 1024;
+
 template <typename U>
 static hipError_t launch_scatter_u(const ExchangeArgs& a, uint32_t grid, hipStream_t s) {
   const bool cap = a.capacity != 0, aff = a.a_kind == OP_AFFINE;
+  const size_t r = a.fanout == 1 ? kScatterLdsReserve : 0;
   if (cap && aff)
-    hipLaunchKernelGGL((k_scatter<U, true, true>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_scatter<U, true, true>), dim3(grid), dim3(kBlock), r, s, a);
   else if (cap)
-    hipLaunchKernelGGL((k_scatter<U, false, true>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_scatter<U, false, true>), dim3(grid), dim3(kBlock), r, s, a);
   else if (aff)
-    hipLaunchKernelGGL((k_scatter<U, true, false>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_scatter<U, true, false>), dim3(grid), dim3(kBlock), r, s, a);
   else
-    hipLaunchKernelGGL((k_scatter<U, false, false>), dim3(grid), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_scatter<U, false, false>), dim3(grid), dim3(kBlock), r, s, a);
   return hipGetLastError();
 }
 
