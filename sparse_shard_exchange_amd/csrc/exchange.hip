@@ -357,7 +357,17 @@ struct Batch {
   }
 };
 
-// One workgroup per chunk of a.chunk consecutive tuples (inside one tile).
+// Workgroup b's item out of n when the hardware deals workgroups to the 8
+// XCDs round robin (workgroup b to XCD b mod 8): XCD x takes the x-th of 8
+// contiguous ranges of items, in order, so that each XCD's L2 sees one
+// contiguous stream instead of every eighth item. A bijection for any n.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
+  const uint32_t q = n / 8, r = n % 8, x = b % 8, k = b / 8;
+  return x * q + min(x, r) + k;
+}
+
+// One workgroup per chunk of a.chunk consecutive tuples (inside one tile);
+// chunks are dealt to XCDs in 8 contiguous ranges (xcd_contiguous).
 // Unit U is 16 bytes when rows are a multiple of 16 bytes, else 4 bytes.
 // The chunk's first batch of payload loads is issued before the slots are
 // looked up, so the two round trips overlap. kCap: each destination keeps
@@ -369,7 +379,7 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
   __shared__ int s_slot[kMaxChunk];  // destination slot of each tuple of the chunk, -1: nothing to move
   __shared__ uint32_t s_last;
   const uint32_t N = a.N, C = a.chunk;
-  const uint64_t g0 = (uint64_t)blockIdx.x * C;
+  const uint64_t g0 = (uint64_t)xcd_contiguous(blockIdx.x, gridDim.x) * C;
   const uint32_t tile = (uint32_t)(g0 / a.tile);
   const uint32_t* tbase = a.tile_base + (uint64_t)tile * N;
   const uint32_t* bbase = a.blk_base + (uint64_t)(tile / a.scan_tiles) * N;
