@@ -357,15 +357,6 @@ struct Batch {
   }
 };
 
-// Workgroup b's item out of n when the hardware deals workgroups to the 8
-// XCDs round robin (workgroup b to XCD b mod 8): XCD x takes the x-th of 8
-// contiguous ranges of items, in order, so that each XCD's L2 sees one
-// contiguous stream instead of every eighth item. A bijection for any n.
-__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
-  const uint32_t q = n / 8, r = n % 8, x = b % 8, k = b / 8;
-  return x * q + min(x, r) + k;
-}
-
 // One workgroup per chunk of a.chunk consecutive tuples (inside one tile);
 // chunks are dealt to XCDs in 8 contiguous ranges (xcd_contiguous).
 // Unit U is 16 bytes when rows are a multiple of 16 bytes, else 4 bytes.
