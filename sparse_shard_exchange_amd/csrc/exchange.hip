@@ -191,25 +191,20 @@ __device__ __forceinline__ WaveDests load_wave_dests(const ExchangeArgs& a, uint
 // workgroups instead of 2.3 (rank 60 -> 58 us).
 __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
   extern __shared__ uint32_t lds[];
-  const uint32_t N = a.N, C = a.rank_copies;
-  // [kWaves][C][N]: C private count copies per wave (lane l counts into copy
-  // l % C, so an LDS atomic meets at most 64 / C lanes on one address: a
-  // tile of one source has few destinations); copy 0 then holds the wave's
-  // next rank per destination
-  uint32_t* wrun = lds;
-  for (uint32_t i = threadIdx.x; i < kWaves * C * N; i += kBlock) wrun[i] = 0;
+  const uint32_t N = a.N;
+  uint32_t* wrun = lds;  // [kWaves][N]: counts of each wave's sub-tile, then its next rank per destination
+  for (uint32_t i = threadIdx.x; i < kWaves * N; i += kBlock) wrun[i] = 0;
   __syncthreads();
   const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t sub = a.tile / kWaves;
   const uint64_t g0 = (uint64_t)blockIdx.x * a.tile + (uint64_t)w * sub;
-  uint32_t* mine = wrun + w * C * N;
+  uint32_t* mine = wrun + w * N;
   bool bad = false;
   // 1. per-wave counts of its contiguous sub-tile (order-free: LDS atomics)
   const WaveDests wd = load_wave_dests(a, g0, sub, lane, bad);
-  uint32_t* cnt = mine + (lane % C) * N;
 #pragma unroll
   for (uint32_t i = 0; i < kMaxChunks; ++i)
-    if (wd.d[i] >= 0) atomicAdd(&cnt[wd.d[i]], 1u);
+    if (wd.d[i] >= 0) atomicAdd(&mine[wd.d[i]], 1u);
   __syncthreads();
   // 2. the tile's counts (for the scan, and kept for the arrival counts) and
   //    the first rank of each (wave, destination): the counts of earlier waves
@@ -217,9 +212,8 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
     uint32_t run = 0;
 #pragma unroll
     for (uint32_t ww = 0; ww < kWaves; ++ww) {
-      uint32_t c = 0;
-      for (uint32_t k = 0; k < C; ++k) c += wrun[(ww * C + k) * N + d];
-      wrun[ww * C * N + d] = run;
+      const uint32_t c = wrun[ww * N + d];
+      wrun[ww * N + d] = run;
       run += c;
     }
     a.tile_base[(uint64_t)blockIdx.x * N + d] = run;
@@ -542,19 +536,8 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
 
 }  // namespace
 
-// Private count copies per ranking wave: as many as fit 16 KiB of LDS per
-// workgroup (8 resident workgroups per CU), at most 4.
-static uint32_t rank_copies(uint32_t N) {
-  uint32_t c = 4;
-  while (c > 1 && (size_t)kWaves * c * N * sizeof(uint32_t) > 16384) c /= 2;
-  return c;
-}
-
 hipError_t launch_rank(const ExchangeArgs& a, hipStream_t s) {
-  ExchangeArgs b = a;
-  b.rank_copies = rank_copies(a.N);
-  const size_t lds = (size_t)kWaves * b.rank_copies * a.N * sizeof(uint32_t);
-  hipLaunchKernelGGL(k_rank, dim3(a.num_tiles), dim3(kBlock), lds, s, b);
+  hipLaunchKernelGGL(k_rank, dim3(a.num_tiles), dim3(kBlock), (size_t)kWaves * a.N * sizeof(uint32_t), s, a);
   return hipGetLastError();
 }
 
