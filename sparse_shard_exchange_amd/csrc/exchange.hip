@@ -200,11 +200,26 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
   const uint64_t g0 = (uint64_t)blockIdx.x * a.tile + (uint64_t)w * sub;
   uint32_t* mine = wrun + w * N;
   bool bad = false;
-  // 1. per-wave counts of its contiguous sub-tile (order-free: LDS atomics)
+  // 1. per-wave counts of its contiguous sub-tile: each 64-tuple chunk's
+  //    lanes are matched by destination once (ballots); the lowest lane of
+  //    each group adds the group's size (one LDS atomic per group: one per
+  //    lane queued up to 64 deep on a tile's few destinations) and every lane
+  //    keeps its rank inside the group, 16 bits each, for step 3
   const WaveDests wd = load_wave_dests(a, g0, sub, lane, bad);
+  uint32_t grp[kMaxChunks];  // rank inside the chunk's group | group size << 16
 #pragma unroll
-  for (uint32_t i = 0; i < kMaxChunks; ++i)
-    if (wd.d[i] >= 0) atomicAdd(&mine[wd.d[i]], 1u);
+  for (uint32_t i = 0; i < kMaxChunks; ++i) {
+    grp[i] = 0;
+    if (i * 64 >= sub) continue;  // uniform
+    const int d = wd.d[i];
+    const bool valid = d >= 0;
+    const uint64_t peers = match_peers(d, valid, a.nbits);
+    if (valid) {
+      const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt(lane)), n = (uint32_t)__popcll(peers);
+      if (rank == 0) atomicAdd(&mine[d], n);
+      grp[i] = rank | n << 16;
+    }
+  }
   __syncthreads();
   // 2. the tile's counts (for the scan, and kept for the arrival counts) and
   //    the first rank of each (wave, destination): the counts of earlier waves
@@ -221,18 +236,17 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
   }
   if (threadIdx.x == 0) a.tile_done[blockIdx.x] = 0;
   __syncthreads();
-  // 3. stable rank inside each 64-tuple chunk of the sub-tile, in order
+  // 3. stable rank inside the tile: the chunks in order, each group starting
+  //    where the earlier chunks (and earlier waves) left its destination
 #pragma unroll
   for (uint32_t i = 0; i < kMaxChunks; ++i) {
     if (i * 64 >= sub) break;  // uniform
     const int d = wd.d[i];
-    const bool valid = d >= 0;
-    const uint64_t peers = match_peers(d, valid, a.nbits);
-    if (valid) {
-      const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt(lane));
+    if (d >= 0) {
+      const uint32_t rank = grp[i] & 0xffffu;
       const uint32_t r = mine[d] + rank;
       // every lane has read mine[] before the group's leader advances it
-      if (rank == 0) mine[d] = r + (uint32_t)__popcll(peers);
+      if (rank == 0) mine[d] = r + (grp[i] >> 16);
       a.rank[g0 + i * 64 + lane] = (uint16_t)r;
     }
   }
