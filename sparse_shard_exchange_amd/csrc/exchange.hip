@@ -7,13 +7,15 @@
 // has all of its messages; sections 4.4-4.5: the successor consumes buffer
 // futures and the interconnect writes straight into the successor's input
 // buffers. On one GPU the "interconnect" is HBM, and the exchange is a stable
-// counting sort by destination done in three launches:
+// counting sort by destination done in three launches (two for tiny ones):
 //
-//   rank    one workgroup per tile of `tile` consecutive tuples counts its
-//           destinations (LDS atomics), writes the row tile_base[tile][*]
-//           (and a copy, tile_cnt), and ranks each tuple among the tuples of
-//           the tile with the same destination, in tuple order (wave by wave;
-//           inside a wave by ballot matching), into rank[g] (16 bits);
+//   rank    one workgroup per tile of `tile` consecutive tuples matches the
+//           tuples of each 64-tuple chunk by destination (ballots), counts
+//           its destinations (one LDS atomic per group), writes the row
+//           tile_base[tile][*] (and a copy, tile_cnt), and ranks each tuple
+//           among the tuples of the tile with the same destination, in tuple
+//           order (wave by wave), into rank[g] (16 bits); with at most 16
+//           tiles its last workgroup also runs the scan below;
 //   scan    one workgroup per block of scan_tiles tiles runs, per
 //           destination, down its rows (where each tile's run of d starts
 //           inside the block) and writes the block totals; the last
@@ -25,11 +27,13 @@
 //           rows of 256 bytes) finds each tuple's slot (segment start + the
 //           tile's run start + its rank), applies A and writes each payload
 //           row with 16-byte vector stores straight into its destination
-//           segment. Chunks are dispatched in tuple order, so the workgroups
-//           in flight read one compact window of the input and append to a
-//           few destination runs: measured on this part, a copy split into
-//           16 KiB pieces per workgroup runs at ~6.3 TB/s, one whose
-//           workgroups each own 64 KiB or more at ~5.5. The last chunk of a
+//           segment. Each XCD takes one contiguous eighth of the chunks, in
+//           order, and a CU holds 4 of these workgroups, so the workgroups
+//           in flight on an XCD read one compact window of the input and
+//           append to a few destination runs through one L2: measured on
+//           this part, a copy split into 16 KiB pieces per workgroup runs at
+//           ~6.3 TB/s, one whose workgroups each own 64 KiB or more at ~5.5,
+//           and the scatter gained 8% from the per-XCD ranges. The last chunk of a
 //           tile to finish adds the tile's per-destination counts to the
 //           arrival counters; the add that completes a destination fires that
 //           destination's future.
