@@ -9,6 +9,7 @@ GPipe fill and drain over S stages and M microbatches takes M + S - 1 stage
 slots.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -83,6 +84,31 @@ def test_gpipe_ticks_closed_form(s, m):
         assert t == st + mb                              # lock-step wavefront
     bubble = 1 - (s * m) / (s * (m + s - 1))
     assert math.isclose(bubble, (s - 1) / (m + s - 1))
+
+
+def _table2_configs():
+    path = os.path.join(os.path.dirname(__file__), "golden", "pathways_table2_pipeline_configs.txt")
+    rows = []
+    for line in open(path):
+        line = line.split("#", 1)[0].split()
+        if line:
+            rows.append((int(line[0]), int(line[1])))
+    return rows
+
+
+def test_gpipe_schedule_on_the_pages_configs():
+    """The (S, M) pairs the PATHWAYS page's Table 2 runs: the oracle's GPipe
+    schedule takes M + S - 1 slots, every item once, and the bubble is
+    (S - 1) / (M + S - 1) of the stage slots (S = 16, M = 64: 15 / 79)."""
+    rows = _table2_configs()
+    assert rows == [(4, 16), (8, 32), (16, 64)]
+    for s, m in rows:
+        ticks = pp.gpipe_schedule(s, m)
+        assert len(ticks) == m + s - 1
+        assert sum(len(t) for t in ticks) == s * m
+        idle = s * len(ticks) - s * m
+        assert idle * (m + s - 1) == (s - 1) * s * len(ticks)
+    assert math.isclose(15 / 79, 0.189873417721519)
 
 
 def test_stage_against_explicit_loops():

@@ -2,6 +2,7 @@
 Figure 9: proportional shares such as 1:1:1:1 and 1:2:4:8) to facts that
 do not come from its code: closed forms of stride scheduling and orders
 derived by hand."""
+import os
 from collections import Counter
 
 from oracle import sched
@@ -61,3 +62,19 @@ def test_idle_time_earns_no_credit():
 def test_empty_and_single_client():
     assert sched.backlogged_order([1, 5], [[], []]) == []
     assert sched.backlogged_order([7], [[2, 1, 4]]) == [(0, 0), (0, 1), (0, 2)]
+
+
+def test_the_pages_share_ratios_hold_per_cycle():
+    """The weights of Figure 9 (stored in tests/golden): with backlogged
+    clients of equal program cost, every cycle of sum(weights) dispatches
+    gives client c exactly weights[c] programs."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "pathways_fig9_share_ratios.txt")
+    rows = [[int(v) for v in line.split("#", 1)[0].split()] for line in open(path)]
+    rows = [r for r in rows if r]
+    assert rows == [[1, 1, 1, 1], [1, 2, 4, 8]]
+    for w in rows:
+        order = sched.backlogged_order(w, [[1] * (16 * max(w))] * len(w))
+        cyc = sum(w)
+        for k in (1, 2, 3):
+            got = counts(order, cyc * k)
+            assert [got[c] for c in range(len(w))] == [k * x for x in w]
