@@ -99,7 +99,9 @@ __device__ __forceinline__ bool gated_node(const ChainArgs& a, uint32_t in_node,
   if (kG > 1 || a.E == 128) {
     using V = float __attribute__((ext_vector_type(2 * kG)));
     V x = reinterpret_cast<const V*>(in)[sub];
-    const bool ready = __shfl((int)epoch_reached(v, need), (int)lead, 64) != 0;
+    // the group's answer from its first lane: a ballot (scalar) rather than
+    // a lane shuffle through LDS, which cost ~50 ns per node here
+    const bool ready = (__ballot(sub == 0 && epoch_reached(v, need)) >> lead) & 1ull;
     if (!ready) {
       if (!await_local(a.f, in_node, shard, need, sub, lead)) return false;
       x = reinterpret_cast<const V*>(in)[sub];
@@ -190,10 +192,10 @@ __global__ __launch_bounds__(256) void k_chain_fused(ChainArgs a) {
 }  // namespace
 
 // Shards per wave for the chained kernel. A gated node's latency grows with
-// the waves a CU holds (measured, one shard per wave: ~300 ns per node up to
-// 4 waves per CU, ~375 at 8, ~415 at 16). Two 128-element shards per wave
-// cost ~350 ns at 2048 shards and ~390 at 4096, but ~350 already at 1024, so
-// only large shard counts pack them; four per wave were slower (~480-500).
+// the waves a CU holds (measured, one shard per wave: ~280 ns per node up to
+// 4 waves per CU, ~360 at 6 to 8, ~405 at 16). Two 128-element shards per
+// wave cost ~350 ns from 1024 to 2048 shards and ~395 at 4096, so only shard
+// counts above 1536 pack them; four per wave were slower (~480-500).
 static uint32_t chain_pack(uint32_t N, uint32_t E) { return E == 128 && N > 1536 ? 2 : 1; }
 
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s) {
