@@ -28,8 +28,9 @@
  *   - Every function returns a status code (PW_OK or a negative PW_ERR_*).
  *     On failure nothing was enqueued, and pw_last_error() (thread local)
  *     describes the cause. Errors found by kernels (a destination out of
- *     range, an expired wait) are latched in the plan's device status word
- *     and reported by the next pw_future_wait on that plan.
+ *     range, an expired wait) are latched in the plan's device status word,
+ *     tagged with the epoch of the call that raised them, and reported by the
+ *     first pw_future_wait on a future of that call or a later one.
  *   - Nothing aborts or throws across this ABI.
  *   - No HIP call is made before the first call that needs the device
  *     (sizing and validation in pw_plan with ws == NULL are host-only).
@@ -214,8 +215,12 @@ const char* pw_last_error(void);
  */
 int pw_plan(const pw_plan_desc* d, void* ws, size_t ws_bytes, size_t* ws_required, pw_plan_t* out);
 
-/* Release the plan's host metadata (not ws). PW_ERR_STATE if its last call
- * may still be running (wait on its future first). */
+/* Release the plan's host metadata (not ws; the caller owns and frees it).
+ * PATHWAYS page, section 4.2: objects are referred to by handle and their
+ * lifetime is the client's to end; section 4.6: buffers stay allocated until
+ * the client releases them. PW_ERR_STATE if the plan's last call may still be
+ * running (wait on its future first); PW_ERR_STATE for a handle that is not
+ * a live plan (destroyed twice, forged). */
 int pw_plan_destroy(pw_plan_t plan);
 
 /*
@@ -287,14 +292,32 @@ int pw_chain_run(pw_plan_t plan, uint64_t steps, pw_sharded_buf* state, void* au
 
 /*
  * pw_future_wait -- block the calling host thread until `f` fired or
- * timeout_ns passed (< 0: no limit). Returns PW_OK, PW_ERR_TIMEOUT, a status
- * latched by the plan's kernels (PW_ERR_BAD_DEST, PW_ERR_TIMEOUT), or
- * PW_ERR_STATE if the future belongs to no live plan or its epoch was never
- * launched.
+ * timeout_ns passed (< 0: no limit). PATHWAYS page, section 4.4: every
+ * computation consumes and produces futures (of sharded buffers); section 4.5:
+ * a node's successor may start as soon as the node's output future is ready,
+ * before the rest of the program finished.
+ *
+ * A shard's future (shard >= 0, any node but RESULT) is resolved from its own
+ * word in the plan's device future table, which the kernels store at system
+ * scope when the (node, shard) completes: the wait polls that word (a 4-byte
+ * read-back on a stream of the plan's own, spinning for 100 us, then every
+ * 20 us) and returns once it holds f.epoch or later, which can be long before
+ * the call's Result. The RESULT future (shard -1) waits for the call's
+ * completion. A fired future means the device work of that (node, shard) is
+ * complete in device memory; host reads of the buffers it guards still go
+ * through the caller's stream.
+ *
+ * Returns PW_OK; PW_ERR_TIMEOUT; a device error latched by f's call or an
+ * earlier call of the plan (PW_ERR_BAD_DEST, PW_ERR_TIMEOUT), reported once
+ * and then cleared (an error latched by a later call is left for the waits of
+ * that call); PW_ERR_STATE if the future belongs to no live plan, its epoch
+ * was never launched, or its call completed without firing it;
+ * PW_ERR_INVALID for a node or shard outside the plan's table.
  */
 int pw_future_wait(pw_future_t f, int64_t timeout_ns);
 
-/* Non-blocking form: *fired = 1 if f has fired, else 0. */
+/* Non-blocking form of pw_future_wait (same sections, same resolution and
+ * errors): *fired = 1 if f has fired, else 0. */
 int pw_future_query(pw_future_t f, int* fired);
 
 /*

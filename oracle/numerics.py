@@ -7,7 +7,7 @@ and rounds once where a buffer of the stated type is written.
 from __future__ import annotations
 
 import numpy as np
-from scipy.special import erf as _erf
+from scipy.special import erfc as _erfc
 
 
 def to_f32(a) -> np.ndarray:
@@ -33,10 +33,13 @@ def to_bf16(a32) -> np.ndarray:
 
 
 def gelu(z) -> np.ndarray:
-    """Exact GELU in fp64: z * Phi(z) = 0.5 * z * (1 + erf(z / sqrt(2))).
+    """Exact GELU in fp64: z * Phi(z), with Phi(z) = erfc(-z / sqrt(2)) / 2.
 
     The pages name no activation formula; the exact (erf) form is the plain
-    definition (Hendrycks & Gimpel), not the tanh approximation.
+    definition (Hendrycks & Gimpel), not the tanh approximation. Phi is taken
+    through erfc, which equals 1 + erf(z / sqrt(2)) over 2 but does not cancel
+    for negative z: the erf form loses every digit below z ~ -8 in fp64
+    (it returns 0 for GELU(-10) = -7.6e-23).
     """
     z = np.asarray(z, dtype=np.float64)
-    return 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
+    return 0.5 * z * _erfc(-z / np.sqrt(2.0))

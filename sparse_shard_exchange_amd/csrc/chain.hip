@@ -41,7 +41,7 @@ __device__ __forceinline__ bool await_local_lane0(const Futures& f, uint32_t nod
     __builtin_amdgcn_s_sleep(1);
     if (epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT), epoch)) return true;
     if (wall_clock64() - t0 > f.spin_ticks) {
-      latch(f.status, ST_TIMEOUT);
+      latch(f, ST_TIMEOUT);
       return false;
     }
   }

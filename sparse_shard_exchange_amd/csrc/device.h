@@ -27,25 +27,29 @@ __device__ __forceinline__ uint64_t match_peers(int d, bool valid, uint32_t nbit
   return valid ? m : 0ull;
 }
 
-__device__ __forceinline__ void latch(uint32_t* status, uint32_t code) {
-  uint32_t expected = ST_OK;
-  __hip_atomic_compare_exchange_strong(status, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+// Latch `code` in the plan's status word unless an error is latched already
+// (the first one wins), tagged with the epoch of the call that raised it so
+// that the host reports it to waits on that call and later ones only.
+__device__ __forceinline__ void latch(const Futures& f, uint32_t code) {
+  uint64_t expected = 0;
+  __hip_atomic_compare_exchange_strong(f.status, &expected, (uint64_t)code | (uint64_t)f.call_epoch << 32,
+                                       __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Fire future (node, shard) for `epoch`. `release` orders every earlier write
-// of this thread (and, after a workgroup barrier, of its workgroup) before the
-// epoch becomes visible to other workgroups; without it, visibility comes
-// from the end of the kernel (consumers in a later launch).
+// Fire future (node, shard) for `epoch`. The epoch is stored at system scope,
+// so that a host thread polling the future table sees it while the launch
+// still runs. `release` first orders every earlier write of this thread (and,
+// after a workgroup barrier that followed a wait for the workgroup's stores,
+// of its workgroup) before the store, for consumers in the same launch;
+// without it, visibility to device consumers comes from the end of the kernel
+// (consumers in a later launch).
 __device__ __forceinline__ void fire(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch,
                                      bool release) {
   const uint32_t i = node * f.width + shard;
   if (f.stamps) f.stamps[i] = wall_clock64();
   __hip_atomic_fetch_add(&f.fires[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (release)
-    __hip_atomic_store(&f.epoch[i], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    __hip_atomic_store(&f.epoch[i], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (release) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __hip_atomic_store(&f.epoch[i], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 __device__ __forceinline__ bool epoch_reached(uint32_t v, uint32_t epoch) {
@@ -64,7 +68,7 @@ __device__ __forceinline__ bool await(const Futures& f, uint32_t node, uint32_t 
     __builtin_amdgcn_s_sleep(1);
     if (epoch_reached(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
     if (wall_clock64() - t0 > f.spin_ticks) {
-      latch(f.status, ST_TIMEOUT);
+      latch(f, ST_TIMEOUT);
       return false;
     }
   }
@@ -85,7 +89,7 @@ __device__ __forceinline__ bool await_prior(const Futures& f, uint32_t node, uin
     __builtin_amdgcn_s_sleep(1);
     if (epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
     if (wall_clock64() - t0 > f.spin_ticks) {
-      latch(f.status, ST_TIMEOUT);
+      latch(f, ST_TIMEOUT);
       return false;
     }
   }

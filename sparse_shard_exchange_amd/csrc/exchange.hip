@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
       a.rank[g0 + i * 64 + lane] = (uint16_t)r;
     }
   }
-  if (bad) latch(a.f.status, ST_BAD_DEST);
+  if (bad) latch(a.f, ST_BAD_DEST);
   if (!a.fuse_scan) return;
   // Few tiles (one scan block): the last workgroup to finish ranking runs
   // the whole scan here instead of in a launch of its own. The destination
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
     b.load(a, g0, j0, total, vu, pow2, shift);
     b.template store<kAffine>(a, s_slot, j0, total, vu, pow2, shift);
   }
-  if (bad) latch(a.f.status, ST_BAD_DEST);
+  if (bad) latch(a.f, ST_BAD_DEST);
 
   // progress: the last chunk of a tile to finish counts the tile's arrivals;
   // completing a destination fires it (consumers run in later launches: the

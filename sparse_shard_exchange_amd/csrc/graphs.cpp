@@ -15,6 +15,7 @@ constexpr uint32_t kQueues = 8;  // one claim queue per XCD
 struct KindState {
   uint64_t calls = 0;  // calls launched so far (targets of the cumulative device counters)
   uint32_t grid = 0;   // PIPELINE, MOE: persistent workgroups (one per CU)
+  uint32_t nq = 0;     // PIPELINE: claim queues (one per XCD; never more than workgroups)
 };
 
 }  // namespace
@@ -85,10 +86,17 @@ int plan_init_kind(Plan* p) {
     const pw_plan_desc& d = p->desc;
     const uint32_t S = d.num_shards, M = d.microbatches;
     const uint32_t RB = (uint32_t)((d.tuples_per_shard + 255) / 256), CT = d.payload_elems / 256;
-    std::vector<std::vector<uint32_t>> queues(kQueues);
+    int cus = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    ks->grid = (uint32_t)std::max(1, cus);
+    // every queue needs owner workgroups (workgroup b owns queue b mod nq)
+    const uint32_t nq = std::min<uint32_t>(kQueues, ks->grid);
+    ks->nq = nq;
+    std::vector<std::vector<uint32_t>> queues(nq);
     uint32_t item = 0;
     auto deal = [&](uint32_t s, uint32_t m) {
-      auto& q = queues[item++ % kQueues];
+      auto& q = queues[item++ % nq];
       for (uint32_t r = 0; r < RB; ++r)
         for (uint32_t c = 0; c < CT; ++c) q.push_back(s | m << 8 | r << 16 | c << 24);
     };
@@ -102,22 +110,18 @@ int plan_init_kind(Plan* p) {
         for (uint32_t s = 0; s < S; ++s)
           if (t >= s && t - s < M) deal(s, t - s);
     }
-    std::vector<uint32_t> order, head(kQueues), len(kQueues);
+    std::vector<uint32_t> order, head(nq), len(nq);
     order.reserve((size_t)S * M * RB * CT);
-    for (uint32_t q = 0; q < kQueues; ++q) {
+    for (uint32_t q = 0; q < nq; ++q) {
       head[q] = (uint32_t)order.size();
       len[q] = (uint32_t)queues[q].size();
       order.insert(order.end(), queues[q].begin(), queues[q].end());
     }
-    hipError_t e0 = hipMemcpy(p->base() + p->L.pipe_ctl + 64, head.data(), kQueues * 4, hipMemcpyHostToDevice);
-    if (e0 == hipSuccess) e0 = hipMemcpy(p->base() + p->L.pipe_ctl + 128, len.data(), kQueues * 4, hipMemcpyHostToDevice);
+    hipError_t e0 = hipMemcpy(p->base() + p->L.pipe_ctl + 64, head.data(), nq * 4, hipMemcpyHostToDevice);
+    if (e0 == hipSuccess) e0 = hipMemcpy(p->base() + p->L.pipe_ctl + 128, len.data(), nq * 4, hipMemcpyHostToDevice);
     if (e0 != hipSuccess) return hip_fail(e0, "uploading the pipeline queues");
-    hipError_t e = hipMemcpy(p->base() + p->L.order, order.data(), order.size() * 4, hipMemcpyHostToDevice);
+    e = hipMemcpy(p->base() + p->L.order, order.data(), order.size() * 4, hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "uploading the pipeline order");
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    ks->grid = (uint32_t)std::max(1, cus);
     // stage weights [S][d][d] -> packed W_s^T, once
     e = hipDeviceSynchronize();
     if (e == hipSuccess)
@@ -371,7 +375,7 @@ int run_pipeline(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipS
   a.qctr = ctl + 4;
   a.qstart = ctl + 16;
   a.qlen = ctl + 32;
-  a.nq = kQueues;
+  a.nq = ks->nq;
   a.rb_ctr = reinterpret_cast<uint32_t*>(p->base() + p->L.rb_ctr);
   a.item_ctr = reinterpret_cast<uint32_t*>(p->base() + p->L.item_ctr);
   a.rb_target = (uint32_t)(call * CT);

@@ -81,6 +81,8 @@ struct Carver {
   }
 };
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 static uint32_t ceil_log2(uint32_t n) {
   uint32_t b = 0;
   while ((1ull << b) < n) ++b;
@@ -294,52 +296,35 @@ hipEvent_t Plan::event_for(uint64_t epoch) const {
 Futures Plan::futures() const {
   Futures f{};
   auto* base = static_cast<unsigned char*>(ws);
-  f.status = reinterpret_cast<uint32_t*>(base + L.ctl);
+  f.status = reinterpret_cast<uint64_t*>(base + L.ctl);
   f.epoch = reinterpret_cast<uint32_t*>(base + L.fut);
   f.fires = reinterpret_cast<uint32_t*>(base + L.fires);
   f.stamps = (desc.flags & PW_FLAG_TRACE) ? reinterpret_cast<uint64_t*>(base + L.stamps) : nullptr;
   f.width = L.width;
   const uint64_t ns = desc.spin_limit_ns ? desc.spin_limit_ns : 2000000000ull;
   f.spin_ticks = (uint32_t)std::min<uint64_t>(0xffffffffull, ns / 10);  // 100 MHz wall clock
+  f.call_epoch = (uint32_t)(epoch + 1);  // the call about to be launched
   return f;
 }
 
-int Plan::read_status(uint32_t* status, bool clear) {
-  if (!aux) {
-    hipError_t e = hipStreamCreateWithFlags(&aux, hipStreamNonBlocking);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamCreate");
-  }
-  uint32_t* st = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + L.ctl);
-  hipError_t e = hipMemcpyAsync(status, st, 4, hipMemcpyDeviceToHost, aux);
+int Plan::clear_status() {
+  uint64_t* st = reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(ws) + L.ctl);
+  hipError_t e = hipMemsetAsync(st, 0, 8, aux);
   if (e == hipSuccess) e = hipStreamSynchronize(aux);
-  if (e != hipSuccess) return hip_fail(e, "reading the status word");
-  if (clear && *status) {
-    e = hipMemsetAsync(st, 0, 4, aux);
-    if (e == hipSuccess) e = hipStreamSynchronize(aux);
-    if (e != hipSuccess) return hip_fail(e, "clearing the status word");
-  }
-  return PW_OK;
-}
-
-int Plan::read_epoch(uint32_t node, uint32_t shard, uint32_t* v) {
-  if (node >= kNodes || shard >= L.width) return fail(PW_ERR_INVALID, "future (%u, %u) outside the table", node, shard);
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<unsigned char*>(ws) + L.fut) + node * L.width + shard;
-  hipError_t e = hipMemcpyAsync(v, p, 4, hipMemcpyDeviceToHost, aux);
-  if (e == hipSuccess) e = hipStreamSynchronize(aux);
-  if (e != hipSuccess) return hip_fail(e, "reading the future table");
+  if (e != hipSuccess) return hip_fail(e, "clearing the status word");
   return PW_OK;
 }
 
 // The status word and one future's epoch with a single round trip: two small
 // copies into pinned host memory on the read-back stream, one synchronize.
-int Plan::read_status_and_epoch(uint32_t node, uint32_t shard, uint32_t* status, uint32_t* epoch) {
+int Plan::read_status_and_epoch(uint32_t node, uint32_t shard, uint64_t* status, uint32_t* epoch) {
   if (node >= kNodes || shard >= L.width) return fail(PW_ERR_INVALID, "future (%u, %u) outside the table", node, shard);
   if (!aux) {
     hipError_t e = hipStreamCreateWithFlags(&aux, hipStreamNonBlocking);
     if (e != hipSuccess) return hip_fail(e, "hipStreamCreate");
   }
   if (!host_words) {
-    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&host_words), 2 * sizeof(uint32_t), hipHostMallocDefault);
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&host_words), 4 * sizeof(uint32_t), hipHostMallocDefault);
     if (e != hipSuccess) {
       host_words = nullptr;
       return hip_fail(e, "hipHostMalloc");
@@ -347,12 +332,12 @@ int Plan::read_status_and_epoch(uint32_t node, uint32_t shard, uint32_t* status,
   }
   auto* base = static_cast<unsigned char*>(ws);
   const uint32_t* fut = reinterpret_cast<const uint32_t*>(base + L.fut) + node * L.width + shard;
-  hipError_t e = hipMemcpyAsync(host_words, base + L.ctl, 4, hipMemcpyDeviceToHost, aux);
-  if (e == hipSuccess) e = hipMemcpyAsync(host_words + 1, fut, 4, hipMemcpyDeviceToHost, aux);
+  hipError_t e = hipMemcpyAsync(host_words, base + L.ctl, 8, hipMemcpyDeviceToHost, aux);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_words + 2, fut, 4, hipMemcpyDeviceToHost, aux);
   if (e == hipSuccess) e = hipStreamSynchronize(aux);
   if (e != hipSuccess) return hip_fail(e, "reading the status word and the future table");
-  *status = host_words[0];
-  *epoch = host_words[1];
+  *status = (uint64_t)host_words[0] | (uint64_t)host_words[1] << 32;
+  *epoch = host_words[2];
   return PW_OK;
 }
 
@@ -366,7 +351,6 @@ static int status_to_code(uint32_t st) {
 }
 
 // ------------------------------------------------------------ exchange call
-static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // After the first half of a split step: wait for it, hand the segment
 // offsets to the host and remember the inputs the second half must match.
@@ -400,33 +384,35 @@ int check_end(Plan* p, const pw_exchange_io* io) {
   return PW_OK;
 }
 
-int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host) {
-  const pw_plan_desc& d = p->desc;
-  const Layout& L = p->L;
-  const uint32_t N = d.num_shards;
-  const uint32_t S = d.num_src_shards ? d.num_src_shards : N;
-  const uint32_t esz = d.dtype == PW_F32 ? 4 : 2;
-  const uint32_t row = esz * d.payload_elems;
-  const bool need_dst = ph != Phase::kBegin;
+// The io of an EXCHANGE step against its descriptor (need_dst: the step
+// writes dst and B's output; dst_rows: the rows dst must hold).
+int validate_exchange_io(const pw_plan_desc& d, const Layout& L, const pw_exchange_io* io, bool need_dst,
+                         uint64_t dst_rows) {
   if (L.G && (!io->src.base || !io->dest || (need_dst && !io->dst.base)))
     return fail(PW_ERR_INVALID, "src, dest and dst are required");
   if (io->src.num_tuples != L.G || io->src.elems_per_tuple != d.payload_elems || io->src.dtype != d.dtype)
     return fail(PW_ERR_INVALID, "src does not match the plan (tuples %llu, elems %u, dtype %u)",
                 (unsigned long long)io->src.num_tuples, io->src.elems_per_tuple, io->src.dtype);
   if (io->src.shard_offsets) return fail(PW_ERR_UNSUPPORTED, "non-uniform source shards");
-  if (need_dst && (io->dst.num_tuples < (ph == Phase::kEnd ? p->open.rows : L.G) ||
-                   io->dst.elems_per_tuple != d.payload_elems || io->dst.dtype != d.dtype))
+  if (need_dst && (io->dst.num_tuples < dst_rows || io->dst.elems_per_tuple != d.payload_elems ||
+                   io->dst.dtype != d.dtype))
     return fail(PW_ERR_INVALID, "dst does not match the plan");
   if (!aligned16(io->src.base) || (need_dst && !aligned16(io->dst.base)))
     return fail(PW_ERR_INVALID, "src/dst must be 16-byte aligned");
   if (need_dst && d.b_op.kind != PW_OP_IDENTITY && !io->b_out)
     return fail(PW_ERR_INVALID, "b_out is required when B is not IDENTITY");
-  int st = ph == Phase::kEnd ? check_end(p, io) : PW_OK;
-  if (st) return st;
-  if ((st = p->begin_call(s))) return st;
+  return PW_OK;
+}
 
-  ExchangeArgs a{};
-  auto* base = static_cast<unsigned char*>(p->ws);
+// Kernel arguments of an EXCHANGE step whose tables are laid out by L from
+// `base` (a plan's workspace, or the static scratch array).
+void exchange_args(const pw_plan_desc& d, const Layout& L, unsigned char* base, const pw_exchange_io* io,
+                   uint32_t epoch, const Futures& f, ExchangeArgs& a) {
+  const uint32_t N = d.num_shards;
+  const uint32_t S = d.num_src_shards ? d.num_src_shards : N;
+  const uint32_t esz = d.dtype == PW_F32 ? 4 : 2;
+  const uint32_t row = esz * d.payload_elems;
+  a = ExchangeArgs{};
   a.src = static_cast<const unsigned char*>(io->src.base);
   a.dest = io->dest;
   a.dst = static_cast<unsigned char*>(io->dst.base);
@@ -452,9 +438,9 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   a.is_f32 = d.dtype == PW_F32;
   a.a_kind = d.a_op.kind; a.a_a = d.a_op.a; a.a_b = d.a_op.b;
   a.b_kind = d.b_op.kind; a.b_a = d.b_op.a; a.b_b = d.b_op.b;
-  a.epoch = (uint32_t)(p->epoch + 1);
+  a.epoch = epoch;
   a.b_gated = d.b_op.kind != PW_OP_IDENTITY;
-  a.f = p->futures();
+  a.f = f;
   a.arrived = reinterpret_cast<uint32_t*>(base + L.arrived);
   a.expected = reinterpret_cast<uint32_t*>(base + L.expected);
   a.b_arrived = reinterpret_cast<uint32_t*>(base + L.b_arrived);
@@ -466,6 +452,19 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   a.rank = reinterpret_cast<uint16_t*>(base + L.rank);
   a.chunk = scatter_chunk(L.tile, row);
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
+}
+
+int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host) {
+  const pw_plan_desc& d = p->desc;
+  const Layout& L = p->L;
+  const bool need_dst = ph != Phase::kBegin;
+  int st = validate_exchange_io(d, L, io, need_dst, ph == Phase::kEnd ? p->open.rows : L.G);
+  if (st) return st;
+  if (ph == Phase::kEnd && (st = check_end(p, io))) return st;
+  if ((st = p->begin_call(s))) return st;
+
+  ExchangeArgs a;
+  exchange_args(d, L, p->base(), io, (uint32_t)(p->epoch + 1), p->futures(), a);
 
   hipError_t e = hipSuccess;
   if (ph != Phase::kEnd) {
@@ -643,20 +642,45 @@ static int future_common(pw_future_t f, Plan** out) {
   return PW_OK;
 }
 
-static int check_fired(Plan* p, pw_future_t f) {
-  uint32_t st = 0, v = 0;
+// One read of the status word and of future f's epoch. A latched device
+// error counts for f if the call that raised it is f's call or an earlier
+// one (its epoch tag <= f.epoch): it is then reported, and cleared for later
+// calls; an error raised by a later call is left for the waits of that call.
+// *fired = 1 once the future holds f.epoch (or a later one).
+static int poll_future(Plan* p, pw_future_t f, int* fired) {
+  uint64_t st = 0;
+  uint32_t v = 0;
   const uint32_t shard = f.shard < 0 ? 0u : (uint32_t)f.shard;
   int rc = p->read_status_and_epoch(f.node, shard, &st, &v);
   if (rc) return rc;
-  if (st) {  // latched device error: report it and clear it for the next call
-    uint32_t again = 0;
-    if ((rc = p->read_status(&again, true))) return rc;
-    return status_to_code(st);
+  const uint32_t code = (uint32_t)st, at = (uint32_t)(st >> 32);
+  if (code && (int32_t)((uint32_t)f.epoch - at) >= 0) {
+    if ((rc = p->clear_status())) return rc;
+    return status_to_code(code);
   }
-  if ((int32_t)(v - (uint32_t)f.epoch) < 0)
-    return fail(PW_ERR_STATE, "future (%u, %d) holds epoch %u < %llu after its call completed", f.node, f.shard, v,
-                (unsigned long long)f.epoch);
+  *fired = (int32_t)(v - (uint32_t)f.epoch) >= 0;
   return PW_OK;
+}
+
+// After the call of f completed: its status, and f must have fired.
+static int check_fired(Plan* p, pw_future_t f) {
+  int fired = 0;
+  int rc = poll_future(p, f, &fired);
+  if (rc) return rc;
+  if (!fired)
+    return fail(PW_ERR_STATE, "future (%u, %d) did not fire for epoch %llu although its call completed", f.node,
+                f.shard, (unsigned long long)f.epoch);
+  return PW_OK;
+}
+
+static int64_t elapsed_ns(std::chrono::steady_clock::time_point t0) {
+  return std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count();
+}
+
+// Spin for the first 100 us (short device work completes with no sleep
+// latency), then poll every 20 us.
+static void backoff(int64_t el) {
+  if (el > 100000) std::this_thread::sleep_for(std::chrono::microseconds(20));
 }
 
 int pw_future_wait(pw_future_t f, int64_t timeout_ns) {
@@ -667,20 +691,37 @@ int pw_future_wait(pw_future_t f, int64_t timeout_ns) {
   std::lock_guard<std::mutex> lk(p->mu);
   hipEvent_t e = p->event_for(f.epoch);
   if (!e) return fail(PW_ERR_STATE, "no call recorded");
+  const auto t0 = std::chrono::steady_clock::now();
+  if (f.shard >= 0 && f.node != PW_NODE_RESULT) {
+    // A shard's future: poll its own word in the device future table (the
+    // kernels store it at system scope), so the wait returns as soon as that
+    // (node, shard) fired, possibly long before the rest of the call.
+    if ((uint32_t)f.shard >= p->L.width) return fail(PW_ERR_INVALID, "shard %d outside the future table", f.shard);
+    while (true) {
+      int fired = 0;
+      if ((rc = poll_future(p, f, &fired))) return rc;
+      if (fired) return PW_OK;
+      const hipError_t q = hipEventQuery(e);
+      if (q == hipSuccess) return check_fired(p, f);  // the call is over: one last read decides
+      if (q != hipErrorNotReady) return hip_fail(q, "hipEventQuery");
+      const int64_t el = elapsed_ns(t0);
+      if (timeout_ns >= 0 && el >= timeout_ns)
+        return fail(PW_ERR_TIMEOUT, "future not fired within %lld ns", (long long)timeout_ns);
+      backoff(el);
+    }
+  }
+  // The Result (the whole call): its completion event.
   if (timeout_ns < 0) {
     hipError_t err = hipEventSynchronize(e);
     if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
   } else {
-    // spin for the first 100 us (short device work completes with no sleep
-    // latency), then poll every 20 us
-    const auto t0 = std::chrono::steady_clock::now();
     while (true) {
       hipError_t err = hipEventQuery(e);
       if (err == hipSuccess) break;
       if (err != hipErrorNotReady) return hip_fail(err, "hipEventQuery");
-      const auto el = std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count();
+      const int64_t el = elapsed_ns(t0);
       if (el >= timeout_ns) return fail(PW_ERR_TIMEOUT, "future not fired within %lld ns", (long long)timeout_ns);
-      if (el > 100000) std::this_thread::sleep_for(std::chrono::microseconds(20));
+      backoff(el);
     }
   }
   return check_fired(p, f);
@@ -695,6 +736,12 @@ int pw_future_query(pw_future_t f, int* fired) {
   if (rc) return rc;
   std::lock_guard<std::mutex> lk(p->mu);
   hipEvent_t e = p->event_for(f.epoch);
+  const bool shard_future = f.shard >= 0 && f.node != PW_NODE_RESULT;
+  if (shard_future && (uint32_t)f.shard >= p->L.width) return fail(PW_ERR_INVALID, "shard %d outside the future table", f.shard);
+  if (shard_future) {
+    if ((rc = poll_future(p, f, fired))) return rc;
+    if (*fired) return PW_OK;
+  }
   hipError_t err = hipEventQuery(e);
   if (err == hipErrorNotReady) return PW_OK;
   if (err != hipSuccess) return hip_fail(err, "hipEventQuery");

@@ -17,12 +17,13 @@ constexpr uint32_t kNodes = 6;
 enum : uint32_t { OP_IDENTITY = 0, OP_AFFINE = 1, OP_ROWSUM = 2 };
 
 struct Futures {
-  uint32_t* status;     // 1 word
+  uint64_t* status;     // 1 word: the first error latched, code | (epoch of the call that latched it) << 32
   uint32_t* epoch;      // [kNodes][width]
   uint32_t* fires;      // [kNodes][width]
   uint64_t* stamps;     // [kNodes][width] or nullptr
   uint32_t width;
   uint32_t spin_ticks;  // bound of a device wait, in wall-clock ticks (100 MHz)
+  uint32_t call_epoch;  // first epoch of the launching call (tags a latched error)
 };
 
 // Arguments of the exchange kernels (passed by value).

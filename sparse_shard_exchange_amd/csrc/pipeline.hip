@@ -28,16 +28,10 @@ __device__ __forceinline__ bool reached(uint32_t v, uint32_t target) { return (i
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
-// Which XCD (accelerator complex die, with its own L2) this wave runs on.
-__device__ __forceinline__ uint32_t xcc_id() {
-  uint32_t v;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
-  return v;
-}
-
-// Claim the next tile, blocking: queue q first, then the others in turn.
-// Returns an index into the order table (and the queue it came from in q) or
-// kNone.
+// Claim the next tile from the queues other than the workgroup's own one
+// (already exhausted), starting at queue q: one atomic add per queue tried.
+// Returns an index into the order table (and leaves q at the queue it came
+// from) or kNone once every queue is empty.
 __device__ __forceinline__ uint32_t claim_from(const PipeArgs& a, uint32_t& q) {
   for (uint32_t n = 0; n < a.nq; ++n, q = (q + 1) % a.nq) {
     const uint32_t k = __hip_atomic_fetch_add(&a.qctr[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -110,7 +104,7 @@ __device__ __forceinline__ bool input_ready(const PipeArgs& a, const PipeTile& p
     __builtin_amdgcn_s_sleep(2);
     if (reached(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), a.rb_target)) return true;
     if (wall_clock64() - t0 > a.f.spin_ticks) {
-      latch(a.f.status, ST_TIMEOUT);
+      latch(a.f, ST_TIMEOUT);
       return false;
     }
   }
@@ -119,60 +113,104 @@ __device__ __forceinline__ bool input_ready(const PipeArgs& a, const PipeTile& p
 struct Claims {
   uint32_t next;   // the ticket after the current candidate (thread 0 writes it)
   uint32_t ready;  // thread 0's answer: is the candidate's input complete
+  uint32_t start;  // start_blocking: the ticket thread 0 chose to start, or kNone
+  uint32_t cand;   // start_blocking: the candidate after an expired wait
 };
 
 // Thread 0's claim pipeline. A claim is an atomic add on a queue counter
 // shared by the CUs of an XCD, a round trip of several microseconds; its
-// result is needed only a whole tile later. So take() hands out the ticket
-// claimed on the previous call and issues the next claim without waiting for
-// it (`raw` holds the counter value in flight, for queue q); the next take()
-// turns it into a ticket, falling back to the other queues (blocking) once
-// queue q is exhausted.
+// result is needed only a whole tile later. So while the workgroup's own
+// queue q has tiles, take() hands out the ticket claimed on the previous call
+// and issues the next claim without waiting for it (`raw` holds the counter
+// value in flight). Once q is exhausted, tickets come from the other queues,
+// one blocking claim per take() and none ahead: a workgroup never reserves a
+// foreign tile before it needs one (see start_blocking for why that matters).
 struct Claimer {
   uint32_t raw;   // value returned by the add in flight on queue q
-  uint32_t q;     // the queue being drained
-  bool live;      // an add is in flight
+  uint32_t q;     // own queue while `own`, then the foreign queue claimed from last
+  bool own;       // q is the workgroup's own queue and still had tiles at the last claim
+  bool done;      // every queue is empty
   __device__ void issue(const PipeArgs& a) {
     raw = __hip_atomic_fetch_add(&a.qctr[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    live = true;
   }
   __device__ uint32_t take(const PipeArgs& a) {  // thread 0
-    if (!live) return kNone;
-    uint32_t t;
-    if (raw < a.qlen[q]) {
-      t = a.qstart[q] + raw;
-    } else {
+    if (done) return kNone;
+    if (own) {
+      if (raw < a.qlen[q]) {
+        const uint32_t t = a.qstart[q] + raw;
+        issue(a);
+        return t;
+      }
+      own = false;
       q = (q + 1) % a.nq;
-      t = claim_from(a, q);  // blocking; leaves q at the queue that had work
     }
-    if (t == kNone) {
-      live = false;
-    } else {
-      issue(a);
-    }
+    const uint32_t t = claim_from(a, q);
+    done = t == kNone;
     return t;
   }
 };
 
-// Starting from candidate ticket t (cl.next holds the one after it), wait for
-// a tile's input and issue its first stages. A tile whose wait expires is
-// published as done (so nothing downstream waits forever) and the next ticket
-// is taken. Returns false once the queues are empty.
+// Thread 0: which of the tiles at tickets t and n (n may be kNone) has its
+// input complete first: 0 for t, 1 for n, -1 once the spin limit expired
+// (latched as a timeout).
+__device__ int await_either(const PipeArgs& a, uint32_t t, uint32_t n) {
+  const PipeTile pt = unpack(a.order[t]);
+  const bool has_n = n != kNone;
+  const PipeTile pn = has_n ? unpack(a.order[n]) : pt;
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+    if (input_ready(a, pt, false)) return 0;
+    if (has_n && input_ready(a, pn, false)) return 1;
+    if (wall_clock64() - t0 > a.f.spin_ticks) {
+      latch(a.f, ST_TIMEOUT);
+      return -1;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Starting from candidate ticket t (cl.next holds the one after it), wait
+// until one of the two held tiles has its input complete and issue its first
+// stages; if that is cl.next, t stays the candidate after it. Waiting on both
+// is what guarantees progress: a workgroup holds at most these two unstarted
+// tickets while it waits (its claim in flight, if any, is on its own queue,
+// behind both in queue order), and t may depend on cl.next when they come from
+// different queues. Let E be the earliest unfinished tile in the plan's claim
+// order (each queue is a subsequence of that order, and every tile's inputs
+// come earlier in it): E's input is complete; if a waiting workgroup holds E,
+// it polls E and starts it; if nobody holds E, E's queue is not exhausted, so
+// its owner workgroups hold no tickets of their own queue that precede E
+// (those would be earlier unfinished tiles) and will claim E next. A tile
+// whose wait expires (the spin limit) is published as done, so nothing
+// downstream waits forever, and the next ticket is taken. Returns false once
+// the queues are empty.
 __device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl, Claimer& cr, uint32_t t,
                                uint32_t& code) {
   while (t != kNone) {
-    code = code_at(a, t);
-    const PipeTile p = unpack(code);
-    if (threadIdx.x == 0) cl.ready = input_ready(a, p, true);
+    if (threadIdx.x == 0) {
+      const uint32_t n = cl.next;
+      const int which = await_either(a, t, n);
+      if (which == 0) {
+        cl.start = t;
+      } else if (which == 1) {
+        cl.start = n;
+        cl.next = t;
+      } else {
+        publish(a, unpack(a.order[t]));
+        cl.start = kNone;
+        cl.cand = n;
+        cl.next = n != kNone ? cr.take(a) : kNone;
+      }
+    }
     __syncthreads();
-    if (uniform(cl.ready)) {
-      mm::tile_start(tile_of(a, p), lds);
+    const uint32_t s = uniform(cl.start);
+    if (s != kNone) {
+      code = code_at(a, s);
+      mm::tile_start(tile_of(a, unpack(code)), lds);
       return true;
     }
-    if (threadIdx.x == 0) publish(a, p);
-    t = uniform(cl.next);
-    __syncthreads();  // every thread has read next and ready
-    if (threadIdx.x == 0 && t != kNone) cl.next = cr.take(a);
+    t = uniform(cl.cand);
+    __syncthreads();  // every thread has read start and cand before thread 0 writes them again
   }
   return false;
 }
@@ -210,9 +248,11 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
   __shared__ Claims cl;
   const uint32_t tid = threadIdx.x;
   const uint64_t item_elems = (uint64_t)a.rows * a.d;
-  Claimer cr{0, 0, false};
+  // Own queue by workgroup number: the hardware deals workgroup b to XCD
+  // b mod 8, so with 8 queues a queue's tiles stay on one XCD, and every
+  // queue has owner workgroups whatever the XCD count.
+  Claimer cr{0, blockIdx.x % a.nq, true, false};
   if (tid == 0) {
-    cr.q = xcc_id() % a.nq;
     cr.issue(a);
     cl.next = cr.take(a);
   }

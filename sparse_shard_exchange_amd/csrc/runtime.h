@@ -56,7 +56,7 @@ struct Plan {
   std::deque<Done> done;  // completion events of the latest calls
   std::vector<hipEvent_t> done_pool;
   hipStream_t aux = nullptr;  // non-blocking stream for small read-backs
-  uint32_t* host_words = nullptr;  // pinned: status word and one future epoch, read back together
+  uint32_t* host_words = nullptr;  // pinned: [0..1] status word, [2] one future epoch, read back together
 
   struct Pending {
     const char* name;
@@ -93,9 +93,8 @@ struct Plan {
   int end_call(hipStream_t s, uint64_t epoch_hi);
   hipEvent_t event_for(uint64_t epoch) const;
   Futures futures() const;
-  int read_status(uint32_t* status, bool clear);
-  int read_status_and_epoch(uint32_t node, uint32_t shard, uint32_t* status, uint32_t* epoch);
-  int read_epoch(uint32_t node, uint32_t shard, uint32_t* v);
+  int clear_status();
+  int read_status_and_epoch(uint32_t node, uint32_t shard, uint64_t* status, uint32_t* epoch);
   unsigned char* base() const { return static_cast<unsigned char*>(ws); }
 };
 
@@ -114,6 +113,12 @@ void plan_release_kind(Plan* p);
 // host; kEnd runs the rest.
 enum class Phase { kAll, kBegin, kEnd };
 int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host);
+int plan_layout(const pw_plan_desc& d, Layout& L);
+int validate_desc(const pw_plan_desc* d);
+int validate_exchange_io(const pw_plan_desc& d, const Layout& L, const pw_exchange_io* io, bool need_dst,
+                         uint64_t dst_rows);
+void exchange_args(const pw_plan_desc& d, const Layout& L, unsigned char* base, const pw_exchange_io* io,
+                   uint32_t epoch, const Futures& f, ExchangeArgs& a);
 int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host);
 int finish_begin(Plan* p, const pw_exchange_io* io, hipStream_t s, int64_t* offsets_host);
 uint64_t moe_static_rows(const pw_plan_desc& d);  // dispatched rows at most (graphs.cpp)

@@ -180,3 +180,4 @@ def test_moe_validation(bad, code):
 def test_chain_sizing():
     d = pw.desc(pw.PW_GRAPH_CHAIN, 2048, 128, a_op=pw.op(pw.PW_OP_AFFINE, 1, 1))
     assert pw.workspace_size(d) >= 2048 * 128 * 4
+

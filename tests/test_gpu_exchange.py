@@ -3,9 +3,13 @@ oracle, through the C ABI.
 
 Bar: routing, indices, offsets, counts and payload bits are bit-exact; the
 fp32 A = 2x + 1 is bit-exact (one rounding, 2x exact); B = per-tuple sum is
-within 1e-6 of the sum of magnitudes of its terms (fp32 summation bound, a
-depth-6 tree: 6 * 2^-24 * sum|x| < 1e-6 * sum|x|); every future fires
-exactly once per call and only after its inputs.
+within 1e-6 relative of the oracle's fp64 sum: the GPU sums 64 fp32 terms in
+a tree of depth 6, whose error is at most 6 * 2^-24 * sum|x| (plus one final
+rounding), and on these inputs sum|x| / |sum x| <= 2.1, so the error stays
+below 7.6e-7 |sum x|. Rows whose sum nearly cancels (|sum x| < 1e-3 sum|x|)
+would need the absolute form of that bound; none occur on the workload and
+the test counts them. Every future fires exactly once per call and only
+after its inputs.
 """
 import numpy as np
 import pytest
@@ -48,6 +52,21 @@ def run(pw, x, dest, n, t, a_op=None, b_op=None, dtype=None, flags=0, counts=Tru
     pw.future_wait(futs[-1], 30_000_000_000)
     torch.cuda.synchronize()
     return ex, futs
+
+
+def check_rowsum(got, y, ref_sum):
+    """B = per-tuple sum against the oracle's fp64 sum: within 1e-6 relative;
+    a row whose sum nearly cancels is held to the fp32 tree bound instead."""
+    got = got.astype(np.float64)
+    ref = np.asarray(ref_sum, dtype=np.float64)
+    mag = np.abs(y.astype(np.float64)).sum(axis=1)
+    err = np.abs(got - ref)
+    cancel = np.abs(ref) < 1e-3 * mag
+    assert np.all(err[~cancel] <= 1e-6 * np.abs(ref[~cancel])), float((err[~cancel] / np.abs(ref[~cancel])).max())
+    assert np.all(err[cancel] <= 7 * 2.0 ** -24 * mag[cancel])
+    print(f"row sums: max relative error {float((err[~cancel] / np.abs(ref[~cancel])).max()):.2e}, "
+          f"{int(cancel.sum())} near-cancelling rows", flush=True)
+    return int(cancel.sum())
 
 
 def _bits(t):
@@ -127,9 +146,7 @@ def test_small_workload_a_and_b(gpu):
     ref = ox.exchange_step(inp.x, inp.dest, 8, 8, a_op=ox.op_affine(2.0, 1.0), b_op=ox.op_rowsum())
     assert np.array_equal(ex.src_index.cpu().numpy(), ref.src_index.astype(np.int32))
     assert np.array_equal(_bits(ex.dst), ref.y.view(np.uint32))          # A bit-exact
-    got = ex.b_out.cpu().numpy().astype(np.float64)
-    mag = np.abs(ref.y.astype(np.float64)).sum(axis=1)
-    assert np.all(np.abs(got - ref.b_out.astype(np.float64)) <= 1e-6 * mag)
+    check_rowsum(ex.b_out.cpu().numpy(), ref.y, ref.b_out)
     ep, fi, st = ex.plan.read_futures(trace=True)
     assert np.all(fi[pw.PW_NODE_EXCHANGE, :8] == 1) and np.all(fi[pw.PW_NODE_B, :8] == 1)
     # fire order respects the graph: exchange[d] before B[d] before Result
@@ -212,8 +229,11 @@ def test_bad_destination_is_reported(gpu):
 
 
 def test_large_zipf_exchange_full_size(gpu):
-    """256 shards x 65536 tuples x 64 fp32, Zipf(1.1) choice of 4 destinations:
-    indices and offsets checked in full, payload rows on a sample."""
+    """256 shards x 65536 tuples x 64 fp32, Zipf(1.1) choice of 4 destinations,
+    the configuration the bench times: offsets, counts and source indices in
+    full against the oracle, and every one of the 16,777,216 payload rows bit
+    for bit against the source row its index names (compared in 1 Mi-row
+    chunks on the host)."""
     pw = gpu
     inp = pw_inputs.exchange_zipf(256, 65536, 64)
     print("full-size zipf exchange: inputs ready", flush=True)
@@ -225,7 +245,61 @@ def test_large_zipf_exchange_full_size(gpu):
     assert np.array_equal(ex.counts.cpu().numpy(), counts.astype(np.int32))
     si = ex.src_index.cpu().numpy()
     assert np.array_equal(si, src_index.astype(np.int32))
-    rng = np.random.default_rng(0)
-    sample = np.sort(rng.choice(si.size, size=200_000, replace=False))
-    got = ex.dst[torch.from_numpy(sample).cuda()].cpu().numpy()
-    assert np.array_equal(got.view(np.uint32), inp.x[src_index[sample]].view(np.uint32))
+    g = si.size
+    xb = inp.x.view(np.uint32)
+    step = 1 << 20
+    for i in range(0, g, step):
+        got = ex.dst[i:i + step].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, xb[src_index[i:i + step]]), i
+    print(f"full-size zipf exchange: all {g} payload rows bit-exact", flush=True)
+
+
+def test_every_shard_future_waited_individually(gpu):
+    """PATHWAYS page, sections 4.4-4.5: computations consume buffer futures.
+    Each EXCHANGE[d] and B[d] future of a step is waited on by itself (the wait
+    polls that future's own word in the device table) and queried, for two
+    calls in a row: each returns with its call's epoch and no error."""
+    pw = gpu
+    n, t = 16, 2000
+    x = torch.from_numpy(pw_inputs.exchange_uniform(n, t, 16).x).cuda()
+    dest = torch.from_numpy(_dest_case("zipf4", n, t)).cuda()
+    ex = pw.Exchange(n, t, 16, b_op=pw.op(pw.PW_OP_ROWSUM))
+    for call in (1, 2):
+        f = ex.step(x, dest)
+        assert f.epoch == call
+        for node in (pw.PW_NODE_EXCHANGE, pw.PW_NODE_B):
+            for d in range(n):
+                fd = pw.pw_future_t(f.plan_id, node, d, f.epoch)
+                pw.future_wait(fd, 10_000_000_000)
+                assert pw.future_query(fd)
+        pw.future_wait(f, 10_000_000_000)
+    ep, fi, _ = ex.plan.read_futures()
+    assert np.all(ep[pw.PW_NODE_EXCHANGE, :n] == 2) and np.all(fi[pw.PW_NODE_B, :n] == 2)
+    later = pw.pw_future_t(f.plan_id, pw.PW_NODE_B, 0, 3)  # an epoch never launched
+    with pytest.raises(pw.PwError) as e:
+        pw.future_wait(later, 1_000_000)
+    assert e.value.code == pw.PW_ERR_STATE
+
+
+def test_device_error_is_reported_to_its_own_call(gpu):
+    """A destination out of range in the second of three calls is latched
+    with that call's epoch: waits on the first call return OK, the second
+    reports PW_ERR_BAD_DEST, the third OK."""
+    pw = gpu
+    n, t = 4, 100
+    x = torch.from_numpy(pw_inputs.exchange_uniform(n, t, 4).x).cuda()
+    good = _dest_case("uniform", n, t)
+    bad = good.copy()
+    bad[17] = 9
+    ex = pw.Exchange(n, t, 4)
+    g, b = torch.from_numpy(good).cuda(), torch.from_numpy(bad).cuda()
+    f1 = ex.step(x, g)
+    f2 = ex.step(x, b)
+    f3 = ex.step(x, g)
+    torch.cuda.synchronize()
+    pw.future_wait(pw.pw_future_t(f1.plan_id, pw.PW_NODE_EXCHANGE, 0, f1.epoch), 10_000_000_000)
+    pw.future_wait(f1, 10_000_000_000)
+    with pytest.raises(pw.PwError) as e:
+        pw.future_wait(f2, 10_000_000_000)
+    assert e.value.code == pw.PW_ERR_BAD_DEST
+    pw.future_wait(f3, 10_000_000_000)

@@ -120,21 +120,23 @@ def test_moe_small(gpu, tokens, d, experts, hidden, shards):
     assert np.all(st[pw.PW_NODE_B, :experts] <= st[pw.PW_NODE_RESULT, 0])
 
 
-def test_moe_full_size_sampled(gpu):
-    """131072 tokens x 1024, 64 experts, FFN 1024 -> 4096 -> 1024: routing and
-    the exchange in full (conditionally on the GPU's logits), logits, expert
-    outputs and combined outputs on sampled tokens."""
+def test_moe_full_size(gpu):
+    """131072 tokens x 1024, 64 experts, FFN 1024 -> 4096 -> 1024, the
+    configuration the bench times. In full: every router logit against fp64,
+    routing and the exchange (conditionally on the GPU's logits), every
+    dispatched row bit for bit, the expert outputs of two whole experts (the
+    largest and the smallest segment), and the combine of every token
+    (conditionally on the GPU's expert outputs and gates). End to end from the
+    tokens on a sample (the full oracle FFN is 4.4 TFLOP of fp64)."""
     pw = gpu
     tokens, d, experts, hidden = 131072, 1024, 64, 4096
     inp, m = run(pw, tokens, d, experts, hidden, 64)
     print("full-size moe: step done", flush=True)
     lg = m.logits.cpu().numpy()
-    x_t = inp.x
-    rng = np.random.default_rng(9)
-    sample = np.sort(rng.choice(tokens, size=48, replace=False))
-    xs = x_t[torch.from_numpy(sample)].float().numpy()
+    x = inp.x.float().numpy()
     wr = inp.w_router.float().numpy()
-    check_logits(xs, wr, lg[sample])
+    for i in range(0, tokens, 16384):
+        check_logits(x[i:i + 16384], wr, lg[i:i + 16384])
     experts_c, gates_c, dest_c, counts_c, offsets_c, si_c = om.route(lg, experts, 64)
     assert np.array_equal(m.experts.cpu().numpy(), experts_c.astype(np.int32))
     g = m.gates.cpu().numpy()
@@ -143,26 +145,43 @@ def test_moe_full_size_sampled(gpu):
     assert np.array_equal(m.counts.cpu().numpy(), counts_c.astype(np.int32))
     si = m.src_index.cpu().numpy()
     assert np.array_equal(si, si_c.astype(np.int32))
-    print("full-size moe: routing and exchange exact", flush=True)
-    # expert outputs and combine for the sampled tokens (both slots)
-    w1 = inp.w1
-    w2 = inp.w2
+    print("full-size moe: logits within bounds, routing and exchange exact", flush=True)
+    xbits = inp.x.view(torch.int16).numpy()
+    xd = m.xd.view(torch.int16).cpu().numpy()
+    assert np.array_equal(xd, xbits[si // 2])
+    print(f"full-size moe: all {si.size} dispatched rows bit-exact", flush=True)
+    y = m.y.float().cpu().numpy()
+    sizes = np.diff(offsets_c)
+    for e in (int(np.argmax(sizes)), int(np.argmin(sizes))):
+        lo, hi = int(offsets_c[e]), int(offsets_c[e + 1])
+        xr = x[si[lo:hi] // 2]  # the dispatched rows (equal to xd bit for bit, checked above)
+        check_expert_rows(xr, inp.w1[e].float().numpy(), inp.w2[e].float().numpy(), y[lo:hi])
+        print(f"full-size moe: expert {e}, all {hi - lo} rows within bounds", flush=True)
     pos = np.empty(2 * tokens, np.int64)
     pos[si] = np.arange(2 * tokens)
-    y_rows = m.y[torch.from_numpy(np.concatenate([pos[2 * sample], pos[2 * sample + 1]])).cuda()].float().cpu().numpy()
-    for i, t in enumerate(sample):
-        for j in range(2):
-            e = int(experts_c[t, j])
-            check_expert_rows(xs[i:i + 1], w1[e].float().numpy(), w2[e].float().numpy(), y_rows[j * len(sample) + i:j * len(sample) + i + 1])
-    out = m.out[torch.from_numpy(sample).cuda()].float().cpu().numpy().astype(np.float64)
+    out_all = m.out.float().cpu().numpy()
+    for i in range(0, tokens, 16384):
+        sl = slice(i, i + 16384)
+        y0, y1 = y[pos[0::2][sl]], y[pos[1::2][sl]]
+        comb = om.combine_rows(g[sl], y0, y1).astype(np.float64)
+        out = out_all[sl].astype(np.float64)
+        terms = np.abs(g[sl, :1] * y0.astype(np.float64)) + np.abs(g[sl, 1:] * y1.astype(np.float64))
+        assert np.all(np.abs(out - comb) <= 2.0 ** -7 * np.maximum(np.abs(comb), np.abs(out)) + 2.0 ** -23 * terms
+                      + 1e-30), i
+    print(f"full-size moe: combine of all {tokens} tokens within bounds", flush=True)
+    # end to end from the tokens on a sample (both slots through the oracle's FFN)
+    rng = np.random.default_rng(9)
+    sample = np.sort(rng.choice(tokens, size=48, replace=False))
+    xs = x[sample]
     ref = []
     for i, t in enumerate(sample):
         ys = []
         for j in range(2):
             e = int(experts_c[t, j])
-            ys.append(om.expert_ffn(xs[i:i + 1], w1[e].float().numpy(), w2[e].float().numpy())[0])
+            ys.append(om.expert_ffn(xs[i:i + 1], inp.w1[e].float().numpy(), inp.w2[e].float().numpy())[0])
         ref.append(om.combine_rows(gates_c[t:t + 1], ys[0][None], ys[1][None])[0])
     ref = np.array(ref, dtype=np.float64)
+    out = out_all[sample].astype(np.float64)
     assert np.all(np.abs(out - ref) <= 1e-2 + 2e-2 * np.abs(ref)), float(np.abs(out - ref).max())
 
 

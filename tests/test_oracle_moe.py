@@ -37,6 +37,23 @@ def test_gelu_values_and_identity():
         assert math.isclose(float(nm.gelu(v)), 0.5 * v * (1 + math.erf(v / math.sqrt(2))), rel_tol=1e-14)
 
 
+def test_gelu_negative_tail_relative_accuracy():
+    """GELU(-a) = -a Phi(-a). For large a the asymptotic series of the normal
+    tail, Phi(-a) = phi(a) / a (1 - 1/a^2 + 3/a^4 - 15/a^6 + 105/a^8 - ...),
+    fixes it to ~945 / a^10 relative; arbitrary-precision erfc (mpmath, 50
+    digits) fixes it everywhere. The oracle must hold its relative accuracy
+    there (the erf form, 1 + erf(z / sqrt 2), cancels to 0 below z ~ -8)."""
+    import mpmath
+    for a in (8.0, 10.0, 12.0, 14.0):
+        phi = math.exp(-a * a / 2) / math.sqrt(2 * math.pi)
+        series = phi / a * (1 - 1 / a**2 + 3 / a**4 - 15 / a**6 + 105 / a**8)
+        assert math.isclose(float(nm.gelu(-a)), -a * series, rel_tol=1000 / a**10)
+    mpmath.mp.dps = 50
+    for z in np.concatenate([-np.geomspace(1e-3, 14.0, 400), np.geomspace(1e-3, 14.0, 400)]):
+        ref = float(mpmath.mpf(z) * mpmath.erfc(-mpmath.mpf(z) / mpmath.sqrt(2)) / 2)
+        assert math.isclose(float(nm.gelu(z)), ref, rel_tol=1e-13), z
+
+
 def _tiny(tokens=40, d=8, e=6, h=5, seed=5):
     rng = np.random.default_rng(seed)
     x = nm.to_bf16(rng.standard_normal((tokens, d)).astype(np.float32))
