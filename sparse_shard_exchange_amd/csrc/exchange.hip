@@ -266,6 +266,7 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
     const uint32_t total = column_scan(a.tile_base, N, d, 0, a.num_tiles);
     const uint32_t e = a.capacity ? min(total, a.capacity) : total;  // the tuples d keeps
     a.expected[d] = e;
+    a.blk_base[d] = 0;  // the one scan block starts every run at 0 (the scatter adds this row)
     exp_lds[d] = e;
   }
   __syncthreads();
