@@ -271,6 +271,27 @@ int pw_exchange_begin(pw_plan_t plan, const pw_exchange_io* io, void* stream, in
 int pw_exchange_end(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done);
 
 /*
+ * pw_exchange_scratch -- the EXCHANGE step of pw_exchange with no plan and no
+ * workspace, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. It
+ * allocates nothing (no hipMalloc, hipFree, events or pinned memory) and
+ * enqueues only kernel launches on `stream`.
+ *
+ * `d` is an EXCHANGE descriptor with flags = 0; `io` as for pw_exchange, with
+ * dst of G rows and dst.shard_offsets (device, N + 1 int64) required: tuples
+ * whose destination is outside [0, N) are dropped, and G - offsets[N] tells
+ * how many (there is no future to report it through). The step's tables live
+ * in a static device array of 8 MiB per GPU, held from the library's load
+ * until the process ends; a descriptor whose tables need more returns
+ * PW_ERR_INVALID before anything is enqueued (the error text names both
+ * sizes). Each call clears what must start at zero; every call on one GPU
+ * shares the array, so calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. Results are those of
+ * pw_exchange on the same inputs, bit for bit.
+ */
+int pw_exchange_scratch(const pw_plan_desc* d, const pw_exchange_io* io, void* stream);
+
+/*
  * pw_chain_run -- run a chained program in one call (PATHWAYS page, section
  * 3 "program tracer", section 4.5 parallel asynchronous dispatch, section 5.1
  * chained execution).

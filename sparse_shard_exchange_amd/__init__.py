@@ -110,6 +110,7 @@ _SIGNATURES = {
     "pw_exchange": (C.c_int, [C.c_void_p, C.POINTER(pw_exchange_io), C.c_void_p, C.POINTER(pw_future_t)]),
     "pw_exchange_begin": (C.c_int, [C.c_void_p, C.POINTER(pw_exchange_io), C.c_void_p, C.c_void_p]),
     "pw_exchange_end": (C.c_int, [C.c_void_p, C.POINTER(pw_exchange_io), C.c_void_p, C.POINTER(pw_future_t)]),
+    "pw_exchange_scratch": (C.c_int, [C.POINTER(pw_plan_desc), C.POINTER(pw_exchange_io), C.c_void_p]),
     "pw_chain_run": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(pw_sharded_buf), C.c_void_p, C.c_void_p,
                                C.POINTER(pw_future_t)]),
     "pw_future_wait": (C.c_int, [pw_future_t, C.c_int64]),
@@ -297,6 +298,12 @@ class Plan:
 
     def reset_times(self):
         check(lib.pw_plan_reset_times(self.handle))
+
+
+def exchange_scratch(d: pw_plan_desc, io: pw_exchange_io, stream=None) -> None:
+    """One EXCHANGE step with the library's static scratch tables (no plan,
+    no workspace, nothing allocated); stream ordered, no future."""
+    check(lib.pw_exchange_scratch(C.byref(d), C.byref(io), _stream(stream)))
 
 
 def future_wait(f: pw_future_t, timeout_ns: int = -1) -> None:

@@ -181,3 +181,15 @@ def test_chain_sizing():
     d = pw.desc(pw.PW_GRAPH_CHAIN, 2048, 128, a_op=pw.op(pw.PW_OP_AFFINE, 1, 1))
     assert pw.workspace_size(d) >= 2048 * 128 * 4
 
+
+def test_scratch_exchange_size_limit_needs_no_device():
+    """The allocation-free step rejects a descriptor whose tables outgrow its
+    8 MiB static array before any device call, naming both sizes."""
+    d = pw.desc(pw.PW_GRAPH_EXCHANGE, 256, 65536, 64)
+    io = pw.pw_exchange_io()
+    rc = pw.lib.pw_exchange_scratch(C.byref(d), C.byref(io), None)
+    assert rc == pw.PW_ERR_INVALID
+    msg = pw.lib.pw_last_error().decode()
+    assert "8388608" in msg, msg
+    d2 = pw.desc(pw.PW_GRAPH_CHAIN, 8, 128, 0)
+    assert pw.lib.pw_exchange_scratch(C.byref(d2), C.byref(io), None) == pw.PW_ERR_INVALID
