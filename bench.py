@@ -261,42 +261,61 @@ def small_step_bench(pw, torch, pw_inputs, iters=50, cold_iters=20):
     """The 8-shard step (8 x 4096 tuples x 64 fp32, A = 2x + 1, exchange,
     B = per-tuple sum): 25.6 MB per step, cache-resident and launch-latency
     bound. Timed warm (steps back to back) and cold (a 512 MiB write before
-    each step evicts the 256 MB last-level cache)."""
+    each step evicts the 256 MB last-level cache), as the default separate
+    launches and as one launch in which B waits on the exchange futures inside
+    the launch (PW_FLAG_ONE_LAUNCH). With tracing, the one-launch steps where
+    some B[d] fired before the last EXCHANGE[d'] are counted."""
     n, t, p = 8, 4096, 64
     inp = pw_inputs.exchange_uniform(n, t, p)
     x = torch.from_numpy(inp.x).cuda()
     dest = torch.from_numpy(inp.dest).cuda()
-    ex = pw.Exchange(n, t, p, a_op=pw.op(pw.PW_OP_AFFINE, 2.0, 1.0), b_op=pw.op(pw.PW_OP_ROWSUM))
-    for _ in range(5):
-        f = ex.step(x, dest)
-    pw.future_wait(f, 60_000_000_000)
-    torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(iters):
-        f = ex.step(x, dest)
-    e1.record(st)
-    torch.cuda.synchronize()
-    pw.future_wait(f, 60_000_000_000)
-    warm_us = e0.elapsed_time(e1) / iters * 1e3
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold = []
-    for _ in range(cold_iters):
-        flush.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(st)
-        f = ex.step(x, dest)
-        b.record(st)
-        torch.cuda.synchronize()
-        cold.append(a.elapsed_time(b) * 1e3)
-    pw.future_wait(f, 60_000_000_000)
-    cold.sort()
     g = n * t
-    return {"workload": "8 shards x 4096 tuples x 64 fp32 ~U(-1,1), dest uniform, A = 2x+1, B = per-tuple sum",
-            "us_per_step_warm": warm_us, "us_per_step_cold_median": cold[len(cold) // 2],
-            "tuples_per_s_warm": g / (warm_us * 1e-6), "bytes_per_tuple_step": 780,
-            "gbs_warm_algorithmic": 780 * g / (warm_us * 1e-6) / 1e9}
+
+    def timed(flags):
+        ex = pw.Exchange(n, t, p, a_op=pw.op(pw.PW_OP_AFFINE, 2.0, 1.0), b_op=pw.op(pw.PW_OP_ROWSUM), flags=flags)
+        for _ in range(5):
+            f = ex.step(x, dest)
+        pw.future_wait(f, 60_000_000_000)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(iters):
+            f = ex.step(x, dest)
+        e1.record(st)
+        torch.cuda.synchronize()
+        pw.future_wait(f, 60_000_000_000)
+        warm_us = e0.elapsed_time(e1) / iters * 1e3
+        cold = []
+        for _ in range(cold_iters):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            f = ex.step(x, dest)
+            b.record(st)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b) * 1e3)
+        pw.future_wait(f, 60_000_000_000)
+        cold.sort()
+        return {"us_per_step_warm": warm_us, "us_per_step_cold_median": cold[len(cold) // 2],
+                "tuples_per_s_warm": g / (warm_us * 1e-6), "gbs_warm_algorithmic": 780 * g / (warm_us * 1e-6) / 1e9}
+
+    out = {"workload": "8 shards x 4096 tuples x 64 fp32 ~U(-1,1), dest uniform, A = 2x+1, B = per-tuple sum",
+           "bytes_per_tuple_step": 780, "path": "separate launches (rank, scan, scatter, B)"}
+    out.update(timed(0))
+    out["one_launch"] = timed(pw.PW_FLAG_ONE_LAUNCH)
+    tr = pw.Exchange(n, t, p, a_op=pw.op(pw.PW_OP_AFFINE, 2.0, 1.0), b_op=pw.op(pw.PW_OP_ROWSUM),
+                     flags=pw.PW_FLAG_TRACE | pw.PW_FLAG_ONE_LAUNCH)
+    overlap = 0
+    for _ in range(20):
+        pw.future_wait(tr.step(x, dest), 60_000_000_000)
+        _, _, stamps = tr.plan.read_futures(trace=True)
+        xs = stamps[pw.PW_NODE_EXCHANGE, :n].astype("int64")
+        bs = stamps[pw.PW_NODE_B, :n].astype("int64")
+        overlap += int(bs.min() < xs.max())
+    out["one_launch"]["traced_steps_with_b_before_last_exchange"] = f"{overlap} of 20"
+    return out
 
 
 def input_record(np, torch, arrays):

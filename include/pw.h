@@ -98,6 +98,12 @@ typedef enum {
 #define PW_FLAG_STAGE_WINDOWS 0x4u /* PIPELINE: claim tiles stage by stage within windows of 16
                                       microbatches instead of in GPipe lock-step ticks; the same
                                       dependencies and per-stage microbatch order, fewer waits  */
+#define PW_FLAG_ONE_LAUNCH 0x8u /* EXCHANGE: where the step is small enough (<= 64 destinations,
+                                   <= 256 slabs of <= 32 KiB of payload, rows of 16..512 bytes),
+                                   run the whole step as one co-resident launch in which B of each
+                                   segment waits on that segment's EXCHANGE future inside the
+                                   launch (sections 4.4-4.5); otherwise, and by default, as
+                                   separate launches (rank, scan, scatter, B). Same results      */
 
 /* ---- plan descriptor ------------------------------------------------------ */
 typedef struct {

@@ -29,7 +29,7 @@ PW_F32, PW_BF16 = 0, 1
 PW_GRAPH_EXCHANGE, PW_GRAPH_CHAIN, PW_GRAPH_MOE, PW_GRAPH_PIPELINE = 0, 1, 2, 3
 PW_OP_IDENTITY, PW_OP_AFFINE, PW_OP_ROWSUM = 0, 1, 2
 PW_CHAIN_CHAINED, PW_CHAIN_OPBYOP, PW_CHAIN_FUSED = 0, 1, 2
-PW_FLAG_TRACE, PW_FLAG_TIMING, PW_FLAG_STAGE_WINDOWS = 0x1, 0x2, 0x4
+PW_FLAG_TRACE, PW_FLAG_TIMING, PW_FLAG_STAGE_WINDOWS, PW_FLAG_ONE_LAUNCH = 0x1, 0x2, 0x4, 0x8
 PW_NODE_ARG, PW_NODE_A, PW_NODE_EXCHANGE, PW_NODE_B, PW_NODE_RESULT, PW_NODE_STAGE = 0, 1, 2, 3, 4, 5
 
 

@@ -57,21 +57,26 @@ __device__ __forceinline__ bool epoch_reached(uint32_t v, uint32_t epoch) {
 }
 
 // Wait (acquire) until future (node, shard) fired for `epoch` or later. The
-// wait is bounded by f.spin_ticks of the 100 MHz wall clock; on expiry it
-// latches ST_TIMEOUT and returns false so the caller skips its work and the
-// wave still exits.
+// word is polled with relaxed agent-scope loads and the acquire is one fence
+// once it is seen: an acquire load in the loop would invalidate the XCD's L2
+// at every poll, under the feet of every other workgroup on it. The wait is
+// bounded by f.spin_ticks of the 100 MHz wall clock; on expiry it latches
+// ST_TIMEOUT and returns false so the caller skips its work and the wave
+// still exits.
 __device__ __forceinline__ bool await(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
   const uint32_t* p = &f.epoch[node * f.width + shard];
-  if (epoch_reached(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
-  const uint64_t t0 = wall_clock64();
-  while (true) {
+  bool ok = epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
+  const uint64_t t0 = ok ? 0 : wall_clock64();
+  while (!ok) {
     __builtin_amdgcn_s_sleep(1);
-    if (epoch_reached(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
-    if (wall_clock64() - t0 > f.spin_ticks) {
+    ok = epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
+    if (!ok && wall_clock64() - t0 > f.spin_ticks) {
       latch(f, ST_TIMEOUT);
       return false;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
 }
 
 // Wait on a future fired by an EARLIER launch on the same stream: the kernel

@@ -10,7 +10,7 @@ namespace pw {
 
 namespace {
 
-constexpr uint32_t kQueues = 8;  // one claim queue per XCD
+constexpr uint32_t kQueues = 8;  // claim queues at most (one per XCD)
 
 struct KindState {
   uint64_t calls = 0;  // calls launched so far (targets of the cumulative device counters)
@@ -90,8 +90,12 @@ int plan_init_kind(Plan* p) {
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     ks->grid = (uint32_t)std::max(1, cus);
-    // every queue needs owner workgroups (workgroup b owns queue b mod nq)
-    const uint32_t nq = std::min<uint32_t>(kQueues, ks->grid);
+    // one queue per XCD: a workgroup owns the queue of the XCD it runs on, so
+    // every queue has owners (the grid fills every CU) and an item's tiles
+    // share one L2
+    int xccs = 0;
+    if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, p->device) != hipSuccess || xccs <= 0) xccs = 1;
+    const uint32_t nq = std::min<uint32_t>(std::min<uint32_t>(kQueues, (uint32_t)xccs), ks->grid);
     ks->nq = nq;
     std::vector<std::vector<uint32_t>> queues(nq);
     uint32_t item = 0;

@@ -125,6 +125,15 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
       L.tile_cnt = c.take((size_t)N * L.num_tiles * 4);
       L.tile_done = c.take((size_t)L.num_tiles * 4);
       L.rank = c.take(L.G * 2);
+      if (d.kind == PW_GRAPH_EXCHANGE) {
+        const uint32_t row = (d.dtype == PW_F32 ? 4u : 2u) * d.payload_elems;
+        L.slab = exchange_small_slab(L.G, N, row, d.b_op.kind, d.dtype == PW_F32);
+        if (L.slab) {
+          L.small_grid = (uint32_t)((L.G + L.slab - 1) / L.slab);
+          L.slab_cnt = c.take((size_t)L.small_grid * N * 4);
+          L.small_tab = c.take((size_t)2 * (2 * N + 1) * 4);
+        }
+      }
       if (d.kind == PW_GRAPH_MOE) {
         const uint64_t tokens = (uint64_t)S * d.tuples_per_shard;
         L.experts = c.take(tokens * d.top_k * 4);
@@ -178,8 +187,10 @@ int validate_desc(const pw_plan_desc* d) {
   if (!d) return fail(PW_ERR_INVALID, "descriptor is NULL");
   if (d->abi_version != PW_ABI_VERSION)
     return fail(PW_ERR_INVALID, "abi_version %u != %u", d->abi_version, PW_ABI_VERSION);
-  if (d->flags & ~(PW_FLAG_TRACE | PW_FLAG_TIMING | PW_FLAG_STAGE_WINDOWS))
+  if (d->flags & ~(PW_FLAG_TRACE | PW_FLAG_TIMING | PW_FLAG_STAGE_WINDOWS | PW_FLAG_ONE_LAUNCH))
     return fail(PW_ERR_INVALID, "unknown flags 0x%x", d->flags);
+  if ((d->flags & PW_FLAG_ONE_LAUNCH) && d->kind != PW_GRAPH_EXCHANGE)
+    return fail(PW_ERR_INVALID, "PW_FLAG_ONE_LAUNCH is for EXCHANGE plans");
   if ((d->flags & PW_FLAG_STAGE_WINDOWS) && d->kind != PW_GRAPH_PIPELINE)
     return fail(PW_ERR_INVALID, "PW_FLAG_STAGE_WINDOWS is for PIPELINE plans");
   if (d->capacity && d->kind != PW_GRAPH_MOE) return fail(PW_ERR_INVALID, "capacity is for MOE plans only");
@@ -452,6 +463,11 @@ void exchange_args(const pw_plan_desc& d, const Layout& L, unsigned char* base, 
   a.rank = reinterpret_cast<uint16_t*>(base + L.rank);
   a.chunk = scatter_chunk(L.tile, row);
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
+  a.slab = L.slab;
+  a.call = 0;
+  a.slab_cnt = L.slab ? reinterpret_cast<uint32_t*>(base + L.slab_cnt) : nullptr;
+  a.small_ctr = reinterpret_cast<uint32_t*>(base + L.ctl + 64) + 4;
+  a.small_tab = L.slab ? reinterpret_cast<uint32_t*>(base + L.small_tab) : nullptr;
 }
 
 int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done, Phase ph, int64_t* offsets_host) {
@@ -467,6 +483,25 @@ int run_exchange(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* 
   exchange_args(d, L, p->base(), io, (uint32_t)(p->epoch + 1), p->futures(), a);
 
   hipError_t e = hipSuccess;
+  if (ph == Phase::kAll && p->small_ok) {  // the whole step in one launch
+    if (io->counts) {
+      p->launch_begin("src_counts", s);
+      e = launch_src_counts(a, s);
+      p->launch_end(s);
+      if (e != hipSuccess) return hip_fail(e, "launch src_counts");
+    }
+    a.call = (uint32_t)(p->small_calls + 1);
+    p->launch_begin("exchange_small", s);
+    e = launch_exchange_small(a, s);
+    p->launch_end(s);
+    if (e != hipSuccess) return hip_fail(e, "launch exchange_small");
+    p->small_calls += 1;
+    p->epoch += 1;
+    st = p->end_call(s, p->epoch);
+    if (st) return st;
+    if (done) *done = pw_future_t{p->id, PW_NODE_RESULT, -1, p->epoch};
+    return PW_OK;
+  }
   if (ph != Phase::kEnd) {
     if (io->counts) {
       p->launch_begin("src_counts", s);
@@ -561,6 +596,8 @@ int pw_plan(const pw_plan_desc* d, void* ws, size_t ws_bytes, size_t* ws_require
     p->id = g_next_id++;
     g_plans[p->id] = p;
   }
+  if (d->kind == PW_GRAPH_EXCHANGE && L.slab && (d->flags & PW_FLAG_ONE_LAUNCH))
+    p->small_ok = exchange_small_resident(dev) >= L.small_grid;  // the one launch needs every workgroup resident
   st = plan_init_kind(p);
   if (st) {
     std::lock_guard<std::mutex> lk(g_reg_mu);

@@ -66,6 +66,12 @@ struct ExchangeArgs {
   uint16_t* rank;             // [G]: rank of tuple g among its tile's tuples with the same destination
   uint32_t chunk;             // tuples per scatter workgroup (a power of two dividing the tile)
   int64_t* seg;               // [N+1]
+  // one-launch path (exchange_small.hip)
+  uint32_t slab;              // tuples per workgroup (0: path not available)
+  uint32_t call;              // one-launch calls of the plan so far, this one included
+  uint32_t* slab_cnt;         // [grid][N] tuples per (slab, destination)
+  uint32_t* small_ctr;        // cumulative publish counter (target: call x grid)
+  uint32_t* small_tab;        // [2][2N + 1]: arrivals, B arrivals, finished destinations, by call parity
 };
 
 // Arguments of the chain kernels (chain.hip).
@@ -133,6 +139,10 @@ hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_src_counts(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_b(const ExchangeArgs& a, hipStream_t s);
+// exchange_small.hip: the whole step in one co-resident launch
+uint32_t exchange_small_slab(uint64_t G, uint32_t N, uint32_t row_bytes, uint32_t b_kind, bool f32);
+hipError_t launch_exchange_small(const ExchangeArgs& a, hipStream_t s);
+uint32_t exchange_small_resident(int device);  // workgroups of the one-launch kernel the device holds at once
 uint32_t scatter_chunk(uint32_t tile, uint32_t row_bytes);
 // mode: 0 chained (one launch, all steps), 1 one node (OpByOp), 2 fused.
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);

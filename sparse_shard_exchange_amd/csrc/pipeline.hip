@@ -28,10 +28,16 @@ __device__ __forceinline__ bool reached(uint32_t v, uint32_t target) { return (i
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
-// Claim the next tile from the queues other than the workgroup's own one
-// (already exhausted), starting at queue q: one atomic add per queue tried.
-// Returns an index into the order table (and leaves q at the queue it came
-// from) or kNone once every queue is empty.
+// Which XCD (accelerator complex die, with its own L2) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
+
+// Claim the next tile, blocking: queue q first, then the others in turn (one
+// atomic add per queue tried). Returns an index into the order table (and
+// leaves q at the queue it came from) or kNone once every queue is empty.
 __device__ __forceinline__ uint32_t claim_from(const PipeArgs& a, uint32_t& q) {
   for (uint32_t n = 0; n < a.nq; ++n, q = (q + 1) % a.nq) {
     const uint32_t k = __hip_atomic_fetch_add(&a.qctr[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -92,22 +98,32 @@ __device__ __forceinline__ void publish(const PipeArgs& a, const PipeTile& p) {
   }
 }
 
+// Thread 0: is tile p's input row block complete (relaxed: no ordering yet)?
+__device__ __forceinline__ bool gate_open(const PipeArgs& a, const PipeTile& p) {
+  return p.s == 0 ||
+         reached(__hip_atomic_load(gate_of(a, p.s, p.m, p.r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), a.rb_target);
+}
+
 // Thread 0: is tile p's input row block complete (acquire)? With `block`,
-// wait for it, bounded by the spin limit (false once it expires).
+// wait for it, bounded by the spin limit (false once it expires). The gate is
+// polled with relaxed loads and acquired with one fence once open: an acquire
+// load per poll would invalidate the XCD's L2 each time, under the operand
+// streams of the other workgroups on it.
 __device__ __forceinline__ bool input_ready(const PipeArgs& a, const PipeTile& p, bool block) {
   if (p.s == 0) return true;
-  const uint32_t* ctr = gate_of(a, p.s, p.m, p.r);
-  if (reached(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), a.rb_target)) return true;
-  if (!block) return false;
-  const uint64_t t0 = wall_clock64();
-  while (true) {
+  bool ok = gate_open(a, p);
+  if (!ok && !block) return false;
+  const uint64_t t0 = ok ? 0 : wall_clock64();
+  while (!ok) {
     __builtin_amdgcn_s_sleep(2);
-    if (reached(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), a.rb_target)) return true;
-    if (wall_clock64() - t0 > a.f.spin_ticks) {
+    ok = gate_open(a, p);
+    if (!ok && wall_clock64() - t0 > a.f.spin_ticks) {
       latch(a.f, ST_TIMEOUT);
       return false;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
 }
 
 struct Claims {
@@ -119,48 +135,83 @@ struct Claims {
 
 // Thread 0's claim pipeline. A claim is an atomic add on a queue counter
 // shared by the CUs of an XCD, a round trip of several microseconds; its
-// result is needed only a whole tile later. So while the workgroup's own
-// queue q has tiles, take() hands out the ticket claimed on the previous call
-// and issues the next claim without waiting for it (`raw` holds the counter
-// value in flight). Once q is exhausted, tickets come from the other queues,
-// one blocking claim per take() and none ahead: a workgroup never reserves a
-// foreign tile before it needs one (see start_blocking for why that matters).
+// result is needed only a whole tile later. So take() hands out the ticket
+// claimed on the previous call and issues the next claim without waiting for
+// it (`raw` holds the counter value in flight, for queue q), falling back to
+// the other queues (blocking) once queue q is exhausted, and claiming ahead
+// on the queue that had work. Before the workgroup waits for an input,
+// resolve() turns the claim in flight into a held ticket, so that the wait
+// can take it too (see start_blocking); take() hands out a held ticket first.
 struct Claimer {
   uint32_t raw;   // value returned by the add in flight on queue q
-  uint32_t q;     // own queue while `own`, then the foreign queue claimed from last
-  bool own;       // q is the workgroup's own queue and still had tiles at the last claim
+  uint32_t q;     // the queue being drained
+  uint32_t held;  // a claimed ticket not handed out yet, or kNone
+  bool live;      // an add is in flight
   bool done;      // every queue is empty
   __device__ void issue(const PipeArgs& a) {
     raw = __hip_atomic_fetch_add(&a.qctr[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    live = true;
   }
   __device__ uint32_t take(const PipeArgs& a) {  // thread 0
-    if (done) return kNone;
-    if (own) {
-      if (raw < a.qlen[q]) {
-        const uint32_t t = a.qstart[q] + raw;
-        issue(a);
-        return t;
-      }
-      own = false;
-      q = (q + 1) % a.nq;
+    if (held != kNone) {
+      const uint32_t t = held;
+      held = kNone;
+      if (!live && !done) issue(a);  // claim ahead again (if q is exhausted, the next take moves on)
+      return t;
     }
-    const uint32_t t = claim_from(a, q);
-    done = t == kNone;
+    if (done) return kNone;
+    if (!live) issue(a);  // nothing in flight (resolved into a ticket earlier): claim now
+    uint32_t t;
+    if (raw < a.qlen[q]) {
+      t = a.qstart[q] + raw;
+    } else {
+      q = (q + 1) % a.nq;
+      t = claim_from(a, q);  // blocking; leaves q at the queue that had work
+    }
+    if (t == kNone) {
+      done = true;
+      live = false;
+    } else {
+      issue(a);
+    }
     return t;
+  }
+  __device__ void resolve(const PipeArgs& a) {  // thread 0
+    if (live && held == kNone && raw < a.qlen[q]) {
+      held = a.qstart[q] + raw;
+      live = false;
+    }
   }
 };
 
-// Thread 0: which of the tiles at tickets t and n (n may be kNone) has its
-// input complete first: 0 for t, 1 for n, -1 once the spin limit expired
-// (latched as a timeout).
-__device__ int await_either(const PipeArgs& a, uint32_t t, uint32_t n) {
-  const PipeTile pt = unpack(a.order[t]);
-  const bool has_n = n != kNone;
-  const PipeTile pn = has_n ? unpack(a.order[n]) : pt;
+// Thread 0: which of the tiles at tickets t, n and h (n, h may be kNone) has
+// its input complete first: 0, 1 or 2, or -1 once the spin limit expired
+// (latched as a timeout). The gates are polled with relaxed loads, all in
+// flight together, and acquired with one fence once one is open.
+__device__ int await_any(const PipeArgs& a, uint32_t t, uint32_t n, uint32_t h) {
+  const uint32_t* g[3] = {nullptr, nullptr, nullptr};
+  const uint32_t tk[3] = {t, n, h};
+  bool open0[3] = {false, false, false};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (tk[i] == kNone) continue;
+    const PipeTile p = unpack(a.order[tk[i]]);
+    if (p.s == 0) open0[i] = true;
+    else g[i] = gate_of(a, p.s, p.m, p.r);
+  }
   const uint64_t t0 = wall_clock64();
   while (true) {
-    if (input_ready(a, pt, false)) return 0;
-    if (has_n && input_ready(a, pn, false)) return 1;
+    uint32_t v[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) v[i] = g[i] ? __hip_atomic_load(g[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    int which = -1;
+#pragma unroll
+    for (int i = 2; i >= 0; --i)
+      if (open0[i] || (g[i] && reached(v[i], a.rb_target))) which = i;  // the earliest held ticket wins ties
+    if (which >= 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      return which;
+    }
     if (wall_clock64() - t0 > a.f.spin_ticks) {
       latch(a.f, ST_TIMEOUT);
       return -1;
@@ -170,30 +221,35 @@ __device__ int await_either(const PipeArgs& a, uint32_t t, uint32_t n) {
 }
 
 // Starting from candidate ticket t (cl.next holds the one after it), wait
-// until one of the two held tiles has its input complete and issue its first
-// stages; if that is cl.next, t stays the candidate after it. Waiting on both
-// is what guarantees progress: a workgroup holds at most these two unstarted
-// tickets while it waits (its claim in flight, if any, is on its own queue,
-// behind both in queue order), and t may depend on cl.next when they come from
-// different queues. Let E be the earliest unfinished tile in the plan's claim
-// order (each queue is a subsequence of that order, and every tile's inputs
-// come earlier in it): E's input is complete; if a waiting workgroup holds E,
-// it polls E and starts it; if nobody holds E, E's queue is not exhausted, so
-// its owner workgroups hold no tickets of their own queue that precede E
-// (those would be earlier unfinished tiles) and will claim E next. A tile
-// whose wait expires (the spin limit) is published as done, so nothing
-// downstream waits forever, and the next ticket is taken. Returns false once
-// the queues are empty.
+// until one of the tiles the workgroup holds has its input complete and issue
+// its first stages. The workgroup holds at most three unstarted tickets: t,
+// cl.next, and the claim that was in flight, resolved into a ticket first;
+// the others stay held, t still the candidate. Waiting on all of them is what
+// guarantees progress, since a held ticket may come from another queue and
+// be an input of t. Let E be the earliest unfinished tile in the plan's
+// claim order (each queue is a subsequence of that order, and every tile's
+// inputs come earlier in it): E's input is complete; if a waiting workgroup
+// holds E, it polls E and starts it; if nobody holds E, E's queue is not
+// exhausted, and a workgroup claiming from that queue holds no unstarted
+// ticket of it (those would precede E) so it is not waiting, and claims E
+// when it has finished its tile. A tile whose wait expires (the spin limit) is
+// published as done, so nothing downstream waits forever, and the next ticket
+// is taken. Returns false once the queues are empty.
 __device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl, Claimer& cr, uint32_t t,
                                uint32_t& code) {
   while (t != kNone) {
     if (threadIdx.x == 0) {
-      const uint32_t n = cl.next;
-      const int which = await_either(a, t, n);
+      cr.resolve(a);
+      const uint32_t n = cl.next, h = cr.held;
+      const int which = await_any(a, t, n, h);
       if (which == 0) {
         cl.start = t;
       } else if (which == 1) {
         cl.start = n;
+        cl.next = t;
+      } else if (which == 2) {
+        cl.start = h;
+        cr.held = n;  // handed out after t
         cl.next = t;
       } else {
         publish(a, unpack(a.order[t]));
@@ -248,10 +304,9 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
   __shared__ Claims cl;
   const uint32_t tid = threadIdx.x;
   const uint64_t item_elems = (uint64_t)a.rows * a.d;
-  // Own queue by workgroup number: the hardware deals workgroup b to XCD
-  // b mod 8, so with 8 queues a queue's tiles stay on one XCD, and every
-  // queue has owner workgroups whatever the XCD count.
-  Claimer cr{0, blockIdx.x % a.nq, true, false};
+  // Own queue: the one of the XCD this workgroup runs on (the plan makes one
+  // queue per XCD and the grid fills every CU, so every queue has owners).
+  Claimer cr{0, xcc_id() % a.nq, kNone, false, false};
   if (tid == 0) {
     cr.issue(a);
     cl.next = cr.take(a);

@@ -27,6 +27,8 @@ struct Layout {
   size_t tile_cnt = 0;    // [num_tiles][N] u32
   size_t tile_done = 0;   // [num_tiles] u32
   size_t rank = 0;        // [G] u16
+  size_t slab_cnt = 0;    // [grid][N] u32 (one-launch path)
+  size_t small_tab = 0;   // [2][2N + 1] u32 (one-launch path counters, by call parity)
   size_t experts = 0, gates = 0, slot_of = 0, hidden_act = 0;  // MOE
   size_t rb_start = 0, b_done = 0;                              // MOE
   size_t w1t = 0, w2t = 0, wrt = 0;  // packed (K-contiguous) weights: MOE W1^T, W2^T, W_r^T; PIPELINE W^T in w1t
@@ -37,6 +39,7 @@ struct Layout {
   uint64_t G = 0;         // tuples per exchange
   uint32_t tile = 0, num_tiles = 0, width = 0;
   uint32_t scan_tiles = 0, num_blk = 0;  // tiles per scan block, scan blocks
+  uint32_t slab = 0, small_grid = 0;     // one-launch path: tuples per workgroup, workgroups (0: none)
 };
 
 struct Plan {
@@ -47,6 +50,8 @@ struct Plan {
   size_t ws_bytes = 0;
   int device = -1;
   uint64_t epoch = 0;     // last epoch launched
+  bool small_ok = false;  // EXCHANGE: whole steps run as one co-resident launch
+  uint64_t small_calls = 0;  // one-launch calls so far
   std::mutex mu;
 
   struct Done {

@@ -20,9 +20,13 @@ instruction is), with random tile, epilogue and poll times, and checks:
   * the order table is a bijection over the tiles and keeps every tile after
     its inputs (the deal of the plan, re-derived here from its description).
 
-The rules before the fix (foreign claims taken a tile ahead, the blocked
-workgroup waiting on its candidate only) are simulated too: they can leave a
-workgroup waiting for a tile it holds itself.
+The kernel's rules: a claim is always in flight a tile ahead (on the own
+queue, then on whichever queue had work); before waiting for an input, the
+workgroup turns that claim into a held ticket and then waits for whichever
+of its (at most three) held tickets becomes ready first. The rules before
+the fix (the same claims ahead, but waiting on the candidate alone) are
+simulated too: they can leave a workgroup waiting for a tile it holds
+itself.
 """
 import heapq
 import random
@@ -93,10 +97,13 @@ class Sim:
     def workgroup(self, b):
         sim, rng = self, self.rng
         nq = self.nq
-        st = {"q": b % nq, "own": True, "done": False, "raw": None, "next": None}
+        # raw: the counter value of the claim in flight on queue q; held: a
+        # claimed ticket not handed out yet
+        st = {"q": b % nq, "raw": None, "held": None, "live": False, "done": False, "next": None}
 
         def issue():
             st["raw"] = sim.claim(st["q"])
+            st["live"] = True
 
         def claim_from():
             for _ in range(nq):
@@ -107,26 +114,30 @@ class Sim:
             return None
 
         def take():
+            if st["held"] is not None:
+                t, st["held"] = st["held"], None
+                if not st["live"] and not st["done"]:
+                    issue()
+                return t
             if st["done"]:
                 return None
-            if st["own"]:
-                if st["raw"] < sim.qlen[st["q"]]:
-                    t = sim.qstart[st["q"]] + st["raw"]
-                    issue()
-                    return t
-                st["own"] = False
+            if not st["live"]:
+                issue()
+            if st["raw"] < sim.qlen[st["q"]]:
+                t = sim.qstart[st["q"]] + st["raw"]
+            else:
                 st["q"] = (st["q"] + 1) % nq
-                if sim.legacy:  # old rule: keep claiming a tile ahead on the foreign queue
-                    t = claim_from()
-                    if t is None:
-                        st["done"] = True
-                    else:
-                        st["own"] = True
-                        issue()
-                    return t
-            t = claim_from()
-            st["done"] = t is None
+                t = claim_from()
+            if t is None:
+                st["done"], st["live"] = True, False
+            else:
+                issue()
             return t
+
+        def resolve():
+            if st["live"] and st["held"] is None and st["raw"] < sim.qlen[st["q"]]:
+                st["held"] = sim.qstart[st["q"]] + st["raw"]
+                st["live"] = False
 
         def start(t):
             tile = sim.order[t]
@@ -136,15 +147,18 @@ class Sim:
 
         def start_blocking(t):
             while t is not None:
-                n = st["next"]
+                if not sim.legacy:
+                    resolve()
+                n, h = st["next"], st["held"]
+                cands = [t] if sim.legacy else [t, n, h]
                 t0 = sim.now
                 which = -1
                 while sim.now - t0 <= sim.spin_limit:
-                    if sim.ready(sim.order[t]):
-                        which = 0
-                        break
-                    if not sim.legacy and n is not None and sim.ready(sim.order[n]):
-                        which = 1
+                    for i, c in enumerate(cands):
+                        if c is not None and sim.ready(sim.order[c]):
+                            which = i
+                            break
+                    if which >= 0:
                         break
                     yield rng.uniform(0.005, 0.02)
                 if which == 0:
@@ -154,6 +168,10 @@ class Sim:
                     st["next"] = t
                     start(n)
                     return n
+                if which == 2:
+                    st["held"], st["next"] = n, t
+                    start(h)
+                    return h
                 sim.expired += 1
                 sim.publish(sim.order[t])
                 t = n
@@ -246,11 +264,11 @@ def test_claim_protocol_full_pass(windows):
 
 @pytest.mark.parametrize("S,M,RB,CT,nwg", [(8, 16, 2, 2, 32)])
 def test_old_claim_rules_could_wait_on_a_held_tile(S, M, RB, CT, nwg):
-    """Before the fix a workgroup whose queue ran dry claimed foreign tiles a
-    tile ahead and then waited on its candidate alone; the candidate could
-    need the foreign tile it held. With tile times spread over 0.3-3 units and
-    start times over 8, some of 20 random schedules reach the spin limit under
-    the old rules; none does under the new ones on the same schedules."""
+    """Before the fix a workgroup waited on its candidate alone while it could
+    hold, claimed ahead from another queue, a tile that the candidate needed.
+    With tile times spread over 0.3-3 units and start times over 8, some of
+    20 random schedules reach the spin limit under the old rules; none does
+    under the new ones on the same schedules."""
     hits = 0
     for seed in range(20):
         kw = dict(tile=(0.3, 3.0), start=(0.0, 8.0))
