@@ -78,8 +78,12 @@ def traffic_for(kernel_src: str, kernel: str, launches_g: int):
 def chain_sweep(pw, torch, pw_inputs, steps):
     """Chained Arg -> A -> B -> Result steps (A = x + 1, B = x / 2, 128 fp32 per
     shard) per second against N, for the three submission modes."""
-    modes = {"chained": pw.PW_CHAIN_CHAINED, "opbyop": pw.PW_CHAIN_OPBYOP, "fused": pw.PW_CHAIN_FUSED}
-    out = {"steps": steps, "elems_per_shard": 128, "steps_per_s": {}, "ns_per_node": {}}
+    modes = {"chained": pw.PW_CHAIN_CHAINED, "split": pw.PW_CHAIN_SPLIT, "opbyop": pw.PW_CHAIN_OPBYOP,
+             "fused": pw.PW_CHAIN_FUSED}
+    out = {"steps": steps, "elems_per_shard": 128, "steps_per_s": {}, "ns_per_node": {},
+           "placement": "chained: A[i] and B[i] on the same lanes (gate ordered by program order); split: A[i] "
+                        "and B[i] on different workgroups, normally different XCDs (cross-CU release/acquire)",
+           "split_cross_xcd_fraction": {}}
     for name, mode in modes.items():
         out["steps_per_s"][name] = {}
         out["ns_per_node"][name] = {}
@@ -100,6 +104,9 @@ def chain_sweep(pw, torch, pw_inputs, steps):
             sec = max(e0.elapsed_time(e1) * 1e-3, wall)
             out["steps_per_s"][name][n] = steps / sec
             out["ns_per_node"][name][n] = sec / (2 * steps) * 1e9
+            if name == "split":
+                pl = ch.placement()
+                out["split_cross_xcd_fraction"][n] = float((pl[:, 0] != pl[:, 1]).mean())
             ch.plan.destroy()
     return out
 

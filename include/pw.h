@@ -89,7 +89,12 @@ typedef enum {
   PW_CHAIN_CHAINED = 0, /* one launch runs every step; each node waits on its input futures
                            in the HBM future table and fires its own                        */
   PW_CHAIN_OPBYOP  = 1, /* one host launch per node per step                                 */
-  PW_CHAIN_FUSED   = 2  /* one launch, one node per shard looping over the steps, no futures */
+  PW_CHAIN_FUSED   = 2, /* one launch, one node per shard looping over the steps, no futures */
+  PW_CHAIN_SPLIT   = 3  /* as CHAINED, but A[i] and B[i] run on different waves, of different
+                           workgroups, with A preferably on the first half of the XCDs and B on
+                           the other: every gate is a cross-workgroup acquire of the producer's
+                           release (section 4.5, parallel asynchronous dispatch). Needs all 2 N
+                           waves resident at once (else pw_plan returns PW_ERR_UNSUPPORTED)  */
 } pw_chain_mode;
 
 /* ---- plan flags ----------------------------------------------------------- */
@@ -357,6 +362,17 @@ int pw_future_query(pw_future_t f, int* fired);
  */
 int pw_plan_read_futures(pw_plan_t plan, uint32_t* epochs, uint32_t* fires, uint64_t* stamps,
                          size_t capacity, uint32_t* nodes, uint32_t* width);
+
+/*
+ * pw_plan_chain_placement -- where the last PW_CHAIN_SPLIT call of a CHAIN
+ * plan ran each node (PATHWAYS page, section 4.1: the system, not the
+ * program, maps computations onto physical devices; section 4.5: the nodes of
+ * a chain are dispatched to their devices ahead of time). Waits for the
+ * plan's last call, then copies 2 N words: xcc[2 i] the XCD (accelerator die)
+ * of the wave that ran A[i], xcc[2 i + 1] that of B[i]. PW_ERR_INVALID if the
+ * plan is not a CHAIN plan in PW_CHAIN_SPLIT mode or capacity < 2 N.
+ */
+int pw_plan_chain_placement(pw_plan_t plan, uint32_t* xcc, size_t capacity);
 
 /* Per-kernel launch counts and HIP-event times accumulated under
  * PW_FLAG_TIMING (waits for pending events). *n receives the entry count. */

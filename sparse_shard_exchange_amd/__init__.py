@@ -28,7 +28,7 @@ PW_ERR_TIMEOUT, PW_ERR_BAD_DEST, PW_ERR_STATE, PW_ERR_UNSUPPORTED = -4, -5, -6, 
 PW_F32, PW_BF16 = 0, 1
 PW_GRAPH_EXCHANGE, PW_GRAPH_CHAIN, PW_GRAPH_MOE, PW_GRAPH_PIPELINE = 0, 1, 2, 3
 PW_OP_IDENTITY, PW_OP_AFFINE, PW_OP_ROWSUM = 0, 1, 2
-PW_CHAIN_CHAINED, PW_CHAIN_OPBYOP, PW_CHAIN_FUSED = 0, 1, 2
+PW_CHAIN_CHAINED, PW_CHAIN_OPBYOP, PW_CHAIN_FUSED, PW_CHAIN_SPLIT = 0, 1, 2, 3
 PW_FLAG_TRACE, PW_FLAG_TIMING, PW_FLAG_STAGE_WINDOWS, PW_FLAG_ONE_LAUNCH = 0x1, 0x2, 0x4, 0x8
 PW_NODE_ARG, PW_NODE_A, PW_NODE_EXCHANGE, PW_NODE_B, PW_NODE_RESULT, PW_NODE_STAGE = 0, 1, 2, 3, 4, 5
 
@@ -117,6 +117,7 @@ _SIGNATURES = {
     "pw_future_query": (C.c_int, [pw_future_t, C.POINTER(C.c_int)]),
     "pw_plan_read_futures": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                        C.POINTER(C.c_uint32), C.POINTER(C.c_uint32)]),
+    "pw_plan_chain_placement": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
     "pw_plan_kernel_times": (C.c_int, [C.c_void_p, C.POINTER(pw_kernel_time), C.c_int, C.POINTER(C.c_int)]),
     "pw_plan_reset_times": (C.c_int, [C.c_void_p]),
     "pw_sched_create": (C.c_int, [C.c_uint32, C.POINTER(C.c_void_p)]),
@@ -384,6 +385,14 @@ class Chain:
 
     def run(self, state, steps, aux=None, stream=None) -> pw_future_t:
         return self.plan.chain_run(steps, sharded(state, self.N, self.E, PW_F32), aux, stream)
+
+    def placement(self):
+        """PW_CHAIN_SPLIT plans: numpy [N, 2] XCD of the waves that ran A[i], B[i]
+        in the last call."""
+        import numpy as np
+        out = np.zeros(2 * self.N, np.uint32)
+        check(lib.pw_plan_chain_placement(self.plan.handle, out.ctypes.data, out.size))
+        return out.reshape(self.N, 2)
 
 
 class Pipeline:

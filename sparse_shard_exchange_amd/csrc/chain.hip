@@ -9,7 +9,10 @@
 // over in one message; section 4.3: under data parallelism each of the N
 // shards sends one tuple to the same shard of the next node.
 //
-// Device mapping: one group of lanes per shard (the whole wave, or with
+// Split placement (k_chain_split): A[i] and B[i] on different workgroups,
+// normally on different XCDs, so every gate is a cross-CU release/acquire.
+//
+// Device mapping of the default chained kernel: one group of lanes per shard (the whole wave, or with
 // 128-element shards and many shards half of it, so that the CUs hold fewer
 // waves). The plan fixes the placement before the chain
 // starts, so the producer of every future (A[i] of step k, B[i] of step k)
@@ -130,19 +133,128 @@ __global__ __launch_bounds__(256) void k_chain_chained(ChainArgs a) {
     const uint32_t k = a.epoch0 + j;
     // A of step k consumes the Result of step k - 1 (B[i]; epoch0 = the Arg)
     if (!gated_node<kG>(a, NODE_B, i, k - 1, st, ab, sub, lead, a.a_kind, a.a_a, a.a_b)) break;
+    if (sub == 0 && a.f.stamps && j == a.steps) a.f.stamps[NODE_A * a.f.width + i] = wall_clock64();
     if (sub == 0) fire_local(a.f, NODE_A, i, k);
     if (!gated_node<kG>(a, NODE_A, i, k, ab, st, sub, lead, a.b_kind, a.b_a, a.b_b)) break;
+    if (sub == 0 && a.f.stamps && j == a.steps) a.f.stamps[NODE_B * a.f.width + i] = wall_clock64();
     if (sub == 0) fire_local(a.f, NODE_B, i, k);
     done = j;
   }
   if (sub == 0 && done) {
-    for (uint32_t node : {NODE_A, NODE_B}) {
-      const uint32_t idx = node * a.f.width + i;
-      __hip_atomic_fetch_add(&a.f.fires[idx], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (a.f.stamps) a.f.stamps[idx] = wall_clock64();
-    }
+    for (uint32_t node : {NODE_A, NODE_B})
+      __hip_atomic_fetch_add(&a.f.fires[node * a.f.width + i], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   finish_shard(a, sub);
+}
+
+// Split placement: each wave claims one role (A or B) and a group of shards,
+// so A[i] and B[i] run on different waves of different workgroups; A prefers
+// the first half of the XCDs and B the second, so the two nodes of a shard
+// normally sit on different XCDs and every future crosses them: the producer
+// writes its node's output, releases (agent scope) and stores the epoch; the
+// consumer polls the epoch with relaxed loads, acquires with one fence, then
+// reads. The claim counters give every shard exactly one wave per role (the
+// grid has one wave per (role, group) slot, plus at most three spare waves
+// that find nothing and leave). With PW_FLAG_TRACE each node stamps its last
+// fire at the moment it fires.
+// kG shards per wave (64 / kG lanes each; with kG > 1 the shards have 128
+// elements, 2 kG per lane): a wave claims a group of kG consecutive shards for
+// one role, waits until every one of its shards' inputs fired, and releases
+// once for all of their outputs. Every release writes back the XCD's L2, and
+// thousands of single-shard waves releasing every step queue behind each other.
+template <int kG>
+__global__ __launch_bounds__(256) void k_chain_split(ChainArgs a) {
+  constexpr uint32_t kLanes = 64 / kG;
+  const uint32_t lane = threadIdx.x & 63, sub = lane % kLanes, grp = lane / kLanes;
+  const uint32_t groups = (a.N + kG - 1) / kG;
+  uint32_t role = 2, gi = 0;
+  if (lane == 0) {
+    const uint32_t x = xcc_id();
+    const uint32_t pref = a.nxcc > 1 ? (x % a.nxcc < a.nxcc / 2 ? 0u : 1u) : ((blockIdx.x * 4 + (threadIdx.x >> 6)) & 1u);
+    uint32_t k = __hip_atomic_fetch_add(&a.role_ctr[pref], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (k < groups) {
+      role = pref;
+      gi = k;
+    } else {
+      k = __hip_atomic_fetch_add(&a.role_ctr[pref ^ 1u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (k < groups) {
+        role = pref ^ 1u;
+        gi = k;
+      }
+    }
+  }
+  role = __shfl(role, 0, 64);
+  gi = __shfl(gi, 0, 64);
+  if (role == 2) return;  // a spare wave
+  const uint32_t i = gi * kG + grp;  // this lane group's shard
+  const bool mine = i < a.N;
+  if (mine && sub == 0) a.place[2 * i + role] = xcc_id();
+  const uint32_t node = role == 0 ? NODE_A : NODE_B, in_node = role == 0 ? NODE_B : NODE_A;
+  const uint32_t kind = role == 0 ? a.a_kind : a.b_kind;
+  const float ca = role == 0 ? a.a_a : a.b_a, cb = role == 0 ? a.a_b : a.b_b;
+  float* st = a.state + (uint64_t)(mine ? i : 0) * a.E;
+  float* ab = a.abuf + (uint64_t)(mine ? i : 0) * a.E;
+  const float* in = role == 0 ? st : ab;
+  float* out = role == 0 ? ab : st;
+  const uint32_t* gate = &a.f.epoch[in_node * a.f.width + (mine ? i : 0)];
+  uint32_t done = 0;
+  for (uint32_t j = 1; j <= a.steps; ++j) {
+    const uint32_t k = a.epoch0 + j;
+    // A of step k consumes B of step k - 1 (the Result; epoch0 = the Arg), B consumes A of step k.
+    // Each group's first lane polls its shard's input future (relaxed); the
+    // wave goes on once all have fired, with one acquire fence.
+    const uint32_t need = role == 0 ? k - 1 : k;
+    bool ok = true;
+    if (sub == 0 && mine) ok = epoch_reached(__hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), need);
+    if (__ballot(!ok)) {
+      const uint64_t t0 = wall_clock64();
+      while (true) {
+        __builtin_amdgcn_s_sleep(1);
+        if (!ok) ok = epoch_reached(__hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), need);
+        if (!__ballot(!ok)) break;
+        if (wall_clock64() - t0 > a.f.spin_ticks) {
+          if (lane == 0) latch(a.f, ST_TIMEOUT);
+          break;
+        }
+      }
+      if (__ballot(!ok)) break;  // expired
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if constexpr (kG > 1) {  // 2 kG consecutive elements per lane, as kG / 2 float4 (16-byte aligned)
+      if (mine) {
+        constexpr int kQ = kG > 1 ? kG / 2 : 1;
+        const float4* src = reinterpret_cast<const float4*>(in) + sub * kQ;
+        float4* dst = reinterpret_cast<float4*>(out) + sub * kQ;
+        float4 x[kQ];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) x[q] = src[q];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+          x[q].x = body(kind, ca, cb, x[q].x);
+          x[q].y = body(kind, ca, cb, x[q].y);
+          x[q].z = body(kind, ca, cb, x[q].z);
+          x[q].w = body(kind, ca, cb, x[q].w);
+          dst[q] = x[q];
+        }
+      }
+    } else {
+      node_body(in, out, a.E, lane, kind, ca, cb);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the wave's stores of every output, then the epochs
+    if (sub == 0 && mine) {
+      const uint32_t idx = node * a.f.width + i;
+      if (a.f.stamps && j == a.steps) a.f.stamps[idx] = wall_clock64();
+      __hip_atomic_store(&a.f.epoch[idx], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    done = j;
+  }
+  if (sub == 0 && mine && done)
+    __hip_atomic_fetch_add(&a.f.fires[node * a.f.width + i], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (role == 1 && mine) finish_shard(a, sub);
+}
+
+__global__ void k_chain_reset(ChainArgs a) {
+  if (threadIdx.x < 2) a.role_ctr[threadIdx.x] = 0;
 }
 
 // OpByOp: one launch per node per step. The input future was fired by the
@@ -198,8 +310,51 @@ __global__ __launch_bounds__(256) void k_chain_fused(ChainArgs a) {
 // counts above 1536 pack them; four per wave were slower (~480-500).
 static uint32_t chain_pack(uint32_t N, uint32_t E) { return E == 128 && N > 1536 ? 2 : 1; }
 
+// Shards per wave of the split placement: one below 256 shards, more above
+// (128-element shards only), so that a step's releases stay few.
+static uint32_t split_pack(uint32_t N, uint32_t E) {
+  if (E != 128) return 1;
+  return N <= 128 ? 1 : N <= 512 ? 2 : N <= 1024 ? 4 : 8;
+}
+
+// Workgroups of the split-placement kernel: one wave per (role, group of shards).
+static uint32_t split_grid(uint32_t N, uint32_t g) { return (2 * ((N + g - 1) / g) + 3) / 4; }
+
+static const void* split_kernel(uint32_t g) {
+  switch (g) {
+    case 8: return (const void*)k_chain_split<8>;
+    case 4: return (const void*)k_chain_split<4>;
+    case 2: return (const void*)k_chain_split<2>;
+    default: return (const void*)k_chain_split<1>;
+  }
+}
+
+bool chain_split_fits(int device, uint32_t N, uint32_t E) {
+  int cus = 0, per_cu = 0;
+  const uint32_t g = split_pack(N, E);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return false;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel(g), 256, 0) != hipSuccess) return false;
+  return (uint64_t)cus * per_cu >= split_grid(N, g);
+}
+
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s) {
   const dim3 grid((a.N + 3) / 4), block(256);
+  if (mode == 3) {
+    hipLaunchKernelGGL(k_chain_reset, dim3(1), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const uint32_t g = split_pack(a.N, a.E);
+    const dim3 sgrid(split_grid(a.N, g));
+    if (g == 8)
+      hipLaunchKernelGGL(k_chain_split<8>, sgrid, block, 0, s, a);
+    else if (g == 4)
+      hipLaunchKernelGGL(k_chain_split<4>, sgrid, block, 0, s, a);
+    else if (g == 2)
+      hipLaunchKernelGGL(k_chain_split<2>, sgrid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(k_chain_split<1>, sgrid, block, 0, s, a);
+    return hipGetLastError();
+  }
   if (mode == 0) {
     const uint32_t g = chain_pack(a.N, a.E), waves = (a.N + g - 1) / g;
     const dim3 cgrid((waves + 3) / 4);

@@ -100,6 +100,13 @@ __device__ __forceinline__ bool await_prior(const Futures& f, uint32_t node, uin
   }
 }
 
+// Which XCD (accelerator complex die, with its own L2) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
+
 // Workgroup b's item out of n when the hardware deals workgroups to the 8
 // XCDs round robin (workgroup b to XCD b mod 8): XCD x takes the x-th of 8
 // contiguous ranges of items, in order, so that each XCD's L2 sees one

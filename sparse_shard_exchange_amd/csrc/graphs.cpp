@@ -32,7 +32,7 @@ int validate_desc_more(const pw_plan_desc* d) {
       for (const pw_op* o : {&d->a_op, &d->b_op})
         if (o->kind != PW_OP_IDENTITY && o->kind != PW_OP_AFFINE)
           return fail(PW_ERR_INVALID, "CHAIN: A and B must be IDENTITY or AFFINE");
-      if (d->chain_mode > PW_CHAIN_FUSED) return fail(PW_ERR_INVALID, "CHAIN: unknown chain_mode %u", d->chain_mode);
+      if (d->chain_mode > PW_CHAIN_SPLIT) return fail(PW_ERR_INVALID, "CHAIN: unknown chain_mode %u", d->chain_mode);
       return PW_OK;
     }
     case PW_GRAPH_PIPELINE: {
@@ -133,6 +133,13 @@ int plan_init_kind(Plan* p) {
                         d.payload_elems, d.payload_elems, d.payload_elems, nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "packing the stage weights");
+  }
+  if (p->desc.kind == PW_GRAPH_CHAIN && p->desc.chain_mode == PW_CHAIN_SPLIT) {
+    if (!chain_split_fits(p->device, p->desc.num_shards, (uint32_t)p->desc.tuples_per_shard))
+      return fail(PW_ERR_UNSUPPORTED, "CHAIN split placement: %u waves must be resident at once", 2 * p->desc.num_shards);
+    int xccs = 0;
+    if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, p->device) != hipSuccess || xccs <= 0) xccs = 1;
+    ks->nq = (uint32_t)xccs;
   }
   if (p->desc.kind == PW_GRAPH_MOE) {
     // expert and router weights -> packed K-contiguous copies, once
@@ -317,6 +324,9 @@ int run_chain(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStre
   a.f = p->futures();
   a.done_ctr = reinterpret_cast<uint32_t*>(p->base() + p->L.ctl + 64);
   a.done_target = (uint32_t)((ks->calls + 1) * (uint64_t)d.num_shards);
+  a.role_ctr = a.done_ctr + 8;
+  a.place = reinterpret_cast<uint32_t*>(p->base() + p->L.place);
+  a.nxcc = ks->nq ? ks->nq : 1;
 
   hipError_t e = hipSuccess;
   if (d.chain_mode == PW_CHAIN_OPBYOP) {
@@ -340,9 +350,9 @@ int run_chain(Plan* p, uint64_t steps, pw_sharded_buf* state, void* aux, hipStre
   } else {
     a.epoch0 = (uint32_t)p->epoch;
     a.steps = (uint32_t)steps;
-    const bool fused = d.chain_mode == PW_CHAIN_FUSED;
-    p->launch_begin(fused ? "chain_fused" : "chain_chained", s);
-    e = launch_chain(a, fused ? 2 : 0, s);
+    const bool fused = d.chain_mode == PW_CHAIN_FUSED, split = d.chain_mode == PW_CHAIN_SPLIT;
+    p->launch_begin(fused ? "chain_fused" : split ? "chain_split" : "chain_chained", s);
+    e = launch_chain(a, fused ? 2 : split ? 3 : 0, s);
     p->launch_end(s);
   }
   if (e != hipSuccess) return hip_fail(e, "launch chain");

@@ -154,6 +154,7 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
       L.fires = c.take((size_t)kNodes * L.width * 4);
       if (d.flags & PW_FLAG_TRACE) L.stamps = c.take((size_t)kNodes * L.width * 8);
       L.a_buf = c.take((size_t)d.num_shards * d.tuples_per_shard * 4);
+      L.place = c.take((size_t)d.num_shards * 2 * 4);
       break;
     }
     case PW_GRAPH_PIPELINE: {
@@ -815,6 +816,24 @@ int pw_plan_read_futures(pw_plan_t plan, uint32_t* epochs, uint32_t* fires, uint
   }
   if (e == hipSuccess) e = hipStreamSynchronize(p->aux);
   if (e != hipSuccess) return hip_fail(e, "reading the future table");
+  return PW_OK;
+}
+
+int pw_plan_chain_placement(pw_plan_t plan, uint32_t* xcc, size_t capacity) {
+  g_last_error.clear();
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (!is_live(p)) return fail(PW_ERR_STATE, "not a live plan");
+  if (p->desc.kind != PW_GRAPH_CHAIN || p->desc.chain_mode != PW_CHAIN_SPLIT)
+    return fail(PW_ERR_INVALID, "a CHAIN plan in PW_CHAIN_SPLIT mode is needed");
+  const size_t n = (size_t)p->desc.num_shards * 2;
+  if (!xcc || capacity < n) return fail(PW_ERR_INVALID, "capacity %zu < %zu", capacity, n);
+  std::lock_guard<std::mutex> lk(p->mu);
+  if (!p->done.empty()) {
+    hipError_t e = hipEventSynchronize(p->done.back().event);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  hipError_t e = hipMemcpy(xcc, p->base() + p->L.place, n * 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the placement table");
   return PW_OK;
 }
 

@@ -86,6 +86,9 @@ struct ChainArgs {
   uint32_t node;     // OpByOp: NODE_A or NODE_B
   uint32_t done_target;  // Result fires when the done counter reaches it
   uint32_t* done_ctr;
+  uint32_t* role_ctr;    // split placement: [2] shards claimed for A, for B (cleared before each call)
+  uint32_t* place;       // split placement: [N][2] XCD of the wave that ran A[i], B[i]
+  uint32_t nxcc;         // XCDs of the device
   Futures f;
 };
 
@@ -145,7 +148,9 @@ hipError_t launch_exchange_small(const ExchangeArgs& a, hipStream_t s);
 uint32_t exchange_small_resident(int device);  // workgroups of the one-launch kernel the device holds at once
 uint32_t scatter_chunk(uint32_t tile, uint32_t row_bytes);
 // mode: 0 chained (one launch, all steps), 1 one node (OpByOp), 2 fused.
+// mode 3: split placement (A and B of a shard on different workgroups).
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);
+bool chain_split_fits(int device, uint32_t N, uint32_t E);  // every wave of the split placement resident at once
 hipError_t launch_pipeline(const PipeArgs& a, uint32_t grid, hipStream_t s);
 hipError_t launch_router(const MoeArgs& a, hipStream_t s);
 hipError_t launch_moe_prefix(const MoeArgs& a, hipStream_t s);

@@ -28,13 +28,6 @@ __device__ __forceinline__ bool reached(uint32_t v, uint32_t target) { return (i
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
-// Which XCD (accelerator complex die, with its own L2) this wave runs on.
-__device__ __forceinline__ uint32_t xcc_id() {
-  uint32_t v;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
-  return v & 0xf;
-}
-
 // Claim the next tile, blocking: queue q first, then the others in turn (one
 // atomic add per queue tried). Returns an index into the order table (and
 // leaves q at the queue it came from) or kNone once every queue is empty.

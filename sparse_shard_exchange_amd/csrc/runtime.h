@@ -33,6 +33,7 @@ struct Layout {
   size_t rb_start = 0, b_done = 0;                              // MOE
   size_t w1t = 0, w2t = 0, wrt = 0;  // packed (K-contiguous) weights: MOE W1^T, W2^T, W_r^T; PIPELINE W^T in w1t
   size_t a_buf = 0;       // CHAIN: A's output buffer
+  size_t place = 0;       // CHAIN: [N][2] u32 XCD of the waves that ran A[i] and B[i] (split placement)
   size_t pipe_ctl = 0;    // PIPELINE: [0] ticket, [1] done counter
   size_t rb_ctr = 0, item_ctr = 0, order = 0;  // PIPELINE tables
   size_t total = 0;

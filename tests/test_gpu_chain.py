@@ -12,11 +12,12 @@ from oracle import chain as oc
 
 pytestmark = pytest.mark.gpu
 
-MODES = ["chained", "opbyop", "fused"]
+MODES = ["chained", "opbyop", "fused", "split"]
 
 
 def _mode(pw, name):
-    return {"chained": pw.PW_CHAIN_CHAINED, "opbyop": pw.PW_CHAIN_OPBYOP, "fused": pw.PW_CHAIN_FUSED}[name]
+    return {"chained": pw.PW_CHAIN_CHAINED, "opbyop": pw.PW_CHAIN_OPBYOP, "fused": pw.PW_CHAIN_FUSED,
+            "split": pw.PW_CHAIN_SPLIT}[name]
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -143,3 +144,30 @@ def test_chain_rejects_misaligned_state(gpu):
     with pytest.raises(pw.PwError) as e:
         ch.run(flat[1:].view(8, 128), 1)
     assert e.value.code == pw.PW_ERR_INVALID
+
+
+@pytest.mark.parametrize("n", [8, 256, 2048])
+def test_chain_split_placement_crosses_xcds(gpu, n):
+    """PW_CHAIN_SPLIT: A[i] and B[i] run on different waves of different
+    workgroups, A preferably on the first half of the XCDs and B on the
+    second, so each gate is a cross-workgroup release/acquire. 200 steps are
+    bit-exact with the oracle; the placement table shows where each node ran;
+    and the last step's fire stamps, taken when each node fired, put A[i]
+    before B[i] before the Result for every shard (B waits on A across
+    workgroups, so this order is the gate's, not program order's)."""
+    pw = gpu
+    x0 = pw_inputs.chain_state(n, 128)
+    ref = oc.chain(x0, 200)
+    ch = pw.Chain(n, 128, mode=pw.PW_CHAIN_SPLIT, flags=pw.PW_FLAG_TRACE)
+    st = torch.from_numpy(x0).cuda()
+    pw.future_wait(ch.run(st, 200), 30_000_000_000)
+    assert np.array_equal(st.cpu().numpy().view(np.uint32), ref.state.view(np.uint32))
+    pl = ch.placement()
+    cross = float((pl[:, 0] != pl[:, 1]).mean())
+    print(f"split placement N={n}: {cross:.1%} of shards have A and B on different XCDs", flush=True)
+    if torch.cuda.get_device_properties(0).multi_processor_count >= 64:
+        assert cross > 0.5
+    ep, fi, stamps = ch.plan.read_futures(trace=True)
+    assert np.all(fi[pw.PW_NODE_A, :n] == 200) and np.all(fi[pw.PW_NODE_B, :n] == 200)
+    sa, sb = stamps[pw.PW_NODE_A, :n].astype(np.int64), stamps[pw.PW_NODE_B, :n].astype(np.int64)
+    assert np.all(sa < sb) and np.all(sb <= stamps[pw.PW_NODE_RESULT, 0])
