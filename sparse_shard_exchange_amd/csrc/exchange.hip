@@ -336,7 +336,10 @@ constexpr uint32_t kCopyBatch = 4;  // units per thread loaded before any is sto
 
 // The payload units of one batch (kCopyBatch per thread) of the chunk: unit
 // i is unit i % vu of tuple i / vu. Source rows do not depend on the slots.
-template <typename U>
+// kPairs (fan-out 2: tuples 2k and 2k + 1 carry the same row k): unit i is
+// unit i % vu of the chunk's row i / vu, loaded once and stored to the slots
+// of both its tuples.
+template <typename U, bool kPairs>
 struct Batch {
   U v[kCopyBatch];
 
@@ -347,9 +350,9 @@ struct Batch {
       const uint32_t i = j0 + u * kBlock + threadIdx.x;
       if (i < total) {
         const uint32_t t = pow2 ? i >> shift : i / vu;
-        const uint64_t g = g0 + t;
+        const uint64_t g = g0 + (kPairs ? 2 * t : t);  // the (first) tuple of the unit
         if (g < a.G) {
-          const U* src = reinterpret_cast<const U*>(a.src + (g / a.fanout) * a.row_bytes);
+          const U* src = reinterpret_cast<const U*>(a.src + (kPairs ? g / 2 : g / a.fanout) * a.row_bytes);
           v[u] = __builtin_nontemporal_load(src + (i - t * vu));
         }
       }
@@ -364,12 +367,15 @@ struct Batch {
       const uint32_t i = j0 + u * kBlock + threadIdx.x;
       if (i < total) {
         const uint32_t t = pow2 ? i >> shift : i / vu;
-        const int slot = s_slot[t];
-        if (slot >= 0) {
-          U x = v[u];
-          if (kAffine) x = apply_a<U>(x, a);
-          U* dst = reinterpret_cast<U*>(a.dst + (uint64_t)slot * a.row_bytes);
-          __builtin_nontemporal_store(x, dst + (i - t * vu));
+        U x = v[u];
+        if (kAffine) x = apply_a<U>(x, a);
+#pragma unroll
+        for (uint32_t c = 0; c < (kPairs ? 2u : 1u); ++c) {
+          const int slot = s_slot[kPairs ? 2 * t + c : t];
+          if (slot >= 0) {
+            U* dst = reinterpret_cast<U*>(a.dst + (uint64_t)slot * a.row_bytes);
+            __builtin_nontemporal_store(x, dst + (i - t * vu));
+          }
         }
       }
     }
@@ -383,8 +389,9 @@ struct Batch {
 // looked up, so the two round trips overlap. kCap: each destination keeps
 // its first `capacity` tuples in tuple order: a tuple is kept if its rank
 // inside the destination is below the capacity; a dropped tuple moves
-// nothing and its slot_of is -1.
-template <typename U, bool kAffine, bool kCap>
+// nothing and its slot_of is -1. kPairs: fan-out 2 with 16-byte units (the
+// chunk is even and starts at an even tuple), each row loaded once.
+template <typename U, bool kAffine, bool kCap, bool kPairs>
 __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
   __shared__ int s_slot[kMaxChunk];  // destination slot of each tuple of the chunk, -1: nothing to move
   __shared__ uint32_t s_last;
@@ -396,8 +403,8 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
   const uint32_t vu = a.row_bytes / (uint32_t)sizeof(U);
   const bool pow2 = (vu & (vu - 1)) == 0;
   const uint32_t shift = pow2 ? (uint32_t)__builtin_ctz(vu) : 0u;
-  const uint32_t total = C * vu;
-  Batch<U> b;
+  const uint32_t total = (kPairs ? C / 2 : C) * vu;  // units to load
+  Batch<U, kPairs> b;
   b.load(a, g0, 0, total, vu, pow2, shift);
 
   bool bad = false;
@@ -560,9 +567,12 @@ hipError_t launch_rank(const ExchangeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-uint32_t scatter_chunk(uint32_t tile, uint32_t row_bytes) {
-  uint32_t c = 1;
-  while (c < kMaxChunk && c < tile && (uint64_t)c * 2 * row_bytes <= 16384) c *= 2;
+uint32_t scatter_chunk(uint32_t tile, uint32_t row_bytes, uint32_t fanout) {
+  // about 16 KiB loaded per chunk: with fan-out 2 (16-byte units) a chunk
+  // loads each row once for two tuples, so it holds twice the tuples
+  const uint32_t f = fanout == 2 && row_bytes % 16 == 0 ? 2 : 1;
+  uint32_t c = f;
+  while (c < kMaxChunk && c < tile && (uint64_t)c * 2 * row_bytes <= 16384ull * f) c *= 2;
   return c;
 }
 
@@ -587,26 +597,29 @@ hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s) {
 // the register-bound count.
 constexpr size_t kScatterLdsReserve = 32 * 1024;
 
-template <typename U>
+template <typename U, bool kPairs>
 static hipError_t launch_scatter_u(const ExchangeArgs& a, uint32_t grid, hipStream_t s) {
   const bool cap = a.capacity != 0, aff = a.a_kind == OP_AFFINE;
   const size_t r = a.fanout == 1 ? kScatterLdsReserve : 0;
   if (cap && aff)
-    hipLaunchKernelGGL((k_scatter<U, true, true>), dim3(grid), dim3(kBlock), r, s, a);
+    hipLaunchKernelGGL((k_scatter<U, true, true, kPairs>), dim3(grid), dim3(kBlock), r, s, a);
   else if (cap)
-    hipLaunchKernelGGL((k_scatter<U, false, true>), dim3(grid), dim3(kBlock), r, s, a);
+    hipLaunchKernelGGL((k_scatter<U, false, true, kPairs>), dim3(grid), dim3(kBlock), r, s, a);
   else if (aff)
-    hipLaunchKernelGGL((k_scatter<U, true, false>), dim3(grid), dim3(kBlock), r, s, a);
+    hipLaunchKernelGGL((k_scatter<U, true, false, kPairs>), dim3(grid), dim3(kBlock), r, s, a);
   else
-    hipLaunchKernelGGL((k_scatter<U, false, false>), dim3(grid), dim3(kBlock), r, s, a);
+    hipLaunchKernelGGL((k_scatter<U, false, false, kPairs>), dim3(grid), dim3(kBlock), r, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s) {
   const uint64_t grid = (a.G + a.chunk - 1) / a.chunk;
   if (grid == 0) return hipSuccess;
-  return a.row_bytes % 16u == 0 ? launch_scatter_u<u32x4>(a, (uint32_t)grid, s)
-                                : launch_scatter_u<uint32_t>(a, (uint32_t)grid, s);
+  if (a.row_bytes % 16u != 0) return launch_scatter_u<uint32_t, false>(a, (uint32_t)grid, s);
+  // the pair path needs even chunks (scatter_chunk gives them for fan-out 2)
+  if (a.fanout == 2 && a.chunk % 2 == 0) return launch_scatter_u<u32x4, true>(a, (uint32_t)grid, s);
+  if (a.fanout > 2) return hipErrorInvalidValue;
+  return launch_scatter_u<u32x4, false>(a, (uint32_t)grid, s);
 }
 
 hipError_t launch_b(const ExchangeArgs& a, hipStream_t s) {

@@ -266,7 +266,7 @@ int run_moe(Plan* p, const pw_exchange_io* io, hipStream_t s, pw_future_t* done,
   a.tile_cnt = reinterpret_cast<uint32_t*>(base + L.tile_cnt);
   a.tile_done = reinterpret_cast<uint32_t*>(base + L.tile_done);
   a.rank = reinterpret_cast<uint16_t*>(base + L.rank);
-  a.chunk = scatter_chunk(L.tile, a.row_bytes);
+  a.chunk = scatter_chunk(L.tile, a.row_bytes, a.fanout);
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
 
   hipError_t e = hipSuccess;

@@ -462,7 +462,7 @@ void exchange_args(const pw_plan_desc& d, const Layout& L, unsigned char* base, 
   a.tile_cnt = reinterpret_cast<uint32_t*>(base + L.tile_cnt);
   a.tile_done = reinterpret_cast<uint32_t*>(base + L.tile_done);
   a.rank = reinterpret_cast<uint16_t*>(base + L.rank);
-  a.chunk = scatter_chunk(L.tile, row);
+  a.chunk = scatter_chunk(L.tile, row, a.fanout);
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
   a.slab = L.slab;
   a.call = 0;

@@ -146,7 +146,7 @@ hipError_t launch_b(const ExchangeArgs& a, hipStream_t s);
 uint32_t exchange_small_slab(uint64_t G, uint32_t N, uint32_t row_bytes, uint32_t b_kind, bool f32);
 hipError_t launch_exchange_small(const ExchangeArgs& a, hipStream_t s);
 uint32_t exchange_small_resident(int device);  // workgroups of the one-launch kernel the device holds at once
-uint32_t scatter_chunk(uint32_t tile, uint32_t row_bytes);
+uint32_t scatter_chunk(uint32_t tile, uint32_t row_bytes, uint32_t fanout);
 // mode: 0 chained (one launch, all steps), 1 one node (OpByOp), 2 fused.
 // mode 3: split placement (A and B of a shard on different workgroups).
 hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s);

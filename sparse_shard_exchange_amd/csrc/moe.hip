@@ -26,7 +26,7 @@ namespace {
 constexpr int kRouterThreads = 512;  // router workgroup: 8 waves, 2 per SIMD, one workgroup per CU
 constexpr int kRouterTokens = kRouterThreads;  // 64 tokens per wave in the GEMM, one per thread in the top-2
 constexpr int kMaxExperts = 64;
-constexpr int kRouterUnroll = 8;  // k-steps of 16 whose token loads are in flight together
+constexpr int kRouterUnroll = 8;  // k-steps of 16 per block of token loads (128 k)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -36,11 +36,33 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 // logits (ties to the lower expert id), gates = softmax over those two.
 // LDS holds the packed W^T ([64][d], k contiguous, 16-byte chunks swizzled by
 // row), then is reused for the logits of the workgroup's tokens.
+//
+// The token rows stream from HBM once, in blocks of kRouterUnroll k-steps
+// (128 k): each lane keeps two blocks of 16-byte loads in registers, and the
+// loads of block s + 1 are issued before the MFMAs of block s, so a wave
+// never waits a whole memory round trip between blocks. Block 0's loads are
+// issued before the W^T fill. kBlocks = d / 128 (d a multiple of 256).
+template <int kBlocks>
 __global__ __launch_bounds__(kRouterThreads, 1) void k_router(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int d = (int)a.d, E = (int)a.E;
   const int chunks = d / 8;  // 16-byte chunks per W^T row
+  const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens + w * 64;  // this wave's 64 tokens
+  const int64_t r0 = min<int64_t>(t0 + (lane & 31), a.tokens - 1);
+  const int64_t r1 = min<int64_t>(t0 + 32 + (lane & 31), a.tokens - 1);
+  // lanes 32..63 hold the second 8 k of each 16-k step (MFMA operand layout)
+  const __bf16* x0 = a.x + r0 * d + (lane >> 5) * 8;
+  const __bf16* x1 = a.x + r1 * d + (lane >> 5) * 8;
+  bf16x8 buf[2][2][kRouterUnroll];  // [register buffer][token half][k-step]
+  auto load_block = [&](bf16x8 (&b)[2][kRouterUnroll], int k0) {
+#pragma unroll
+    for (int u = 0; u < kRouterUnroll; ++u) {
+      b[0][u] = *reinterpret_cast<const bf16x8*>(x0 + k0 + 16 * u);
+      b[1][u] = *reinterpret_cast<const bf16x8*>(x1 + k0 + 16 * u);
+    }
+  };
+  load_block(buf[0], 0);
   // packed W_r^T [64][d] (experts >= E are zero rows) -> LDS, 16-byte chunks
   // (16 loads per thread in flight before their LDS stores)
   constexpr int kFill = 16;
@@ -66,31 +88,18 @@ __global__ __launch_bounds__(kRouterThreads, 1) void k_router(MoeArgs a) {
   }
   __syncthreads();
 
-  const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens + w * 64;  // this wave's 64 tokens
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  const int64_t r0 = min<int64_t>(t0 + (lane & 31), a.tokens - 1);
-  const int64_t r1 = min<int64_t>(t0 + 32 + (lane & 31), a.tokens - 1);
-  const __bf16* x0 = a.x + r0 * d;
-  const __bf16* x1 = a.x + r1 * d;
-  // The token rows stream from HBM once: the loads of kRouterUnroll k-steps
-  // (d is a multiple of 256) are issued before their MFMAs, so each lane has
-  // 2 x kRouterUnroll 16-byte loads in flight.
-  for (int k0 = 0; k0 < d; k0 += 16 * kRouterUnroll) {
-    bf16x8 av0[kRouterUnroll], av1[kRouterUnroll];
+#pragma unroll
+  for (int s = 0; s < kBlocks; ++s) {
+    if (s + 1 < kBlocks) load_block(buf[(s + 1) & 1], (s + 1) * 16 * kRouterUnroll);
+    __builtin_amdgcn_sched_barrier(0);  // the next block's loads stay above these MFMAs
 #pragma unroll
     for (int u = 0; u < kRouterUnroll; ++u) {
-      const int ch = ((k0 + 16 * u) >> 3) + (lane >> 5);
-      av0[u] = *reinterpret_cast<const bf16x8*>(x0 + ch * 8);
-      av1[u] = *reinterpret_cast<const bf16x8*>(x1 + ch * 8);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep every load above the MFMAs
-#pragma unroll
-    for (int u = 0; u < kRouterUnroll; ++u) {
-      const int ch = ((k0 + 16 * u) >> 3) + (lane >> 5);
+      const int ch = ((s * 16 * kRouterUnroll + 16 * u) >> 3) + (lane >> 5);
       bf16x8 bv[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -99,8 +108,8 @@ __global__ __launch_bounds__(kRouterThreads, 1) void k_router(MoeArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0[u], bv[j], acc[0][j], 0, 0, 0);
-        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1[u], bv[j], acc[1][j], 0, 0, 0);
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[s & 1][0][u], bv[j], acc[0][j], 0, 0, 0);
+        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[s & 1][1][u], bv[j], acc[1][j], 0, 0, 0);
       }
     }
   }
@@ -333,50 +342,84 @@ __global__ __launch_bounds__(256, 1) void k_ffn(MoeArgs a, uint32_t nb) {
 
 // out[t] = bf16(g0 * Y[slot(2t)] + g1 * Y[slot(2t + 1)]), fp32 sum with the
 // top-1 term first; a tuple dropped by the expert capacity (slot -1) adds
-// nothing (its row is not read); one wave per token at a time, 16-byte
-// chunks. The grid is
-// bounded (grid-stride over tokens): every workgroup adds once to the done
-// counter, and adds to one address serialize at the memory side (one per
-// 4-token workgroup cost ~0.3 ms at 131072 tokens).
+// nothing. Gating: each workgroup first checks the B futures of all experts
+// (thread e: expert e) and combines only the tokens whose two experts fired.
+// Then one wave handles kCombineTokens tokens per pass: their metadata
+// (experts, gates, slots) in one round of loads, then every row chunk of both
+// tokens in flight before any is used (16-byte chunks, lane l: chunks l and
+// l + 64 of each row). The row loads are unconditional (a dropped tuple reads
+// row 0 and masks it to zero), since a load under a branch would make the
+// compiler wait for each load in turn. Rows are read and written
+// nontemporally: the gather reads each Y row once (measured on this shape:
+// 142 against 153 us with cached loads), nothing in the step reads the output
+// again, and output rows left dirty in the caches would be written back while
+// the next step's router streams the tokens (a read-bound kernel after 256 MiB
+// of plain stores runs 30-35 us longer). The grid is bounded (grid-stride over
+// tokens): every workgroup adds once to the done counter, and adds to one
+// address serialize at the memory side.
 constexpr uint32_t kCombineBlocks = 2048;
+constexpr int kCombineTokens = 2;
 
 __global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
-  const int lane = threadIdx.x & 63;
-  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < a.tokens; t += (int64_t)gridDim.x * 4) {
-    const int e0 = a.experts[t * 2], e1 = a.experts[t * 2 + 1];
-    bool ok = true;
-    if (lane == 0) ok = await_prior(a.f, NODE_B, e0, a.epoch) && await_prior(a.f, NODE_B, e1, a.epoch);
-    ok = __shfl((int)ok, 0, 64) != 0;
-    if (!ok) continue;  // uniform per wave
-    const float g0 = a.gates[t * 2], g1 = a.gates[t * 2 + 1];
-    const int s0 = a.slot_of[t * 2], s1 = a.slot_of[t * 2 + 1];  // wave-uniform
-    const bf16x8* y0 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)max(s0, 0) * a.d);
-    const bf16x8* y1 = reinterpret_cast<const bf16x8*>(a.y + (int64_t)max(s1, 0) * a.d);
-    bf16x8* o = reinterpret_cast<bf16x8*>(a.out + t * a.d);
-    // two chunks of each row per lane per pass: all four loads in flight
-    // before the first is used (d = 1024 is exactly one pass)
-    const uint32_t nch = a.d / 8;
-    for (uint32_t ch = lane; ch < nch; ch += 128) {
-      const bool two = ch + 64 < nch;
-      bf16x8 u0 = {}, v0 = {}, u1 = {}, v1 = {};
-      if (s0 >= 0) u0 = y0[ch];
-      if (s1 >= 0) v0 = y1[ch];
-      if (two) {
-        if (s0 >= 0) u1 = y0[ch + 64];
-        if (s1 >= 0) v1 = y1[ch + 64];
-      }
-      bf16x8 r0, r1;
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  __shared__ uint32_t s_ok[2];
+  const uint32_t tid = threadIdx.x;
+  const int lane = tid & 63;
+  if (tid < 2) s_ok[tid] = 0;
+  __syncthreads();
+  if (tid < a.E && await_prior(a.f, NODE_B, tid, a.epoch)) atomicOr(&s_ok[tid >> 5], 1u << (tid & 31));
+  __syncthreads();
+  const uint64_t ok = (uint64_t)s_ok[0] | (uint64_t)s_ok[1] << 32;
+  const uint32_t nch = a.d / 8;  // 16-byte chunks per row
+  const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
+  u32x4* out = reinterpret_cast<u32x4*>(a.out);
+  const int64_t stride = (int64_t)gridDim.x * 4 * kCombineTokens;
+  for (int64_t t0 = ((int64_t)blockIdx.x * 4 + (tid >> 6)) * kCombineTokens; t0 < (int64_t)a.tokens; t0 += stride) {
+    int slot[kCombineTokens][2];
+    float gate[kCombineTokens][2];
+    bool live[kCombineTokens];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        r0[j] = (__bf16)fmaf(g1, (float)v0[j], g0 * (float)u0[j]);
-        r1[j] = (__bf16)fmaf(g1, (float)v1[j], g0 * (float)u1[j]);
+    for (int k = 0; k < kCombineTokens; ++k) {
+      const int64_t t = min<int64_t>(t0 + k, (int64_t)a.tokens - 1);
+      const int2 e = *reinterpret_cast<const int2*>(a.experts + t * 2);
+      const float2 g = *reinterpret_cast<const float2*>(a.gates + t * 2);
+      const int2 sl = *reinterpret_cast<const int2*>(a.slot_of + t * 2);
+      const int e0 = __builtin_amdgcn_readfirstlane(e.x), e1 = __builtin_amdgcn_readfirstlane(e.y);
+      live[k] = t0 + k < (int64_t)a.tokens && ((ok >> (e0 & 63)) & (ok >> (e1 & 63)) & 1u);
+      slot[k][0] = __builtin_amdgcn_readfirstlane(sl.x);
+      slot[k][1] = __builtin_amdgcn_readfirstlane(sl.y);
+      gate[k][0] = g.x;
+      gate[k][1] = g.y;
+    }
+    for (uint32_t c0 = 0; c0 < nch; c0 += 128) {
+      u32x4 v[kCombineTokens][2][2];  // [token][tuple][chunk]
+#pragma unroll
+      for (int k = 0; k < kCombineTokens; ++k)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint32_t ch = min(c0 + lane + 64 * c, nch - 1);
+            v[k][r][c] = __builtin_nontemporal_load(y + (int64_t)max(slot[k][r], 0) * nch + ch);
+          }
+#pragma unroll
+      for (int k = 0; k < kCombineTokens; ++k) {
+        const uint32_t m0 = slot[k][0] >= 0 ? ~0u : 0u, m1 = slot[k][1] >= 0 ? ~0u : 0u;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t ch = c0 + lane + 64 * c;
+          const bf16x8 u = __builtin_bit_cast(bf16x8, v[k][0][c] & m0);
+          const bf16x8 w = __builtin_bit_cast(bf16x8, v[k][1][c] & m1);
+          bf16x8 r;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) r[j] = (__bf16)fmaf(gate[k][1], (float)w[j], gate[k][0] * (float)u[j]);
+          if (live[k] && ch < nch) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, r), out + (t0 + k) * nch + ch);
+        }
       }
-      o[ch] = r0;
-      if (two) o[ch + 64] = r1;
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&a.ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1 == gridDim.x) fire(a.f, NODE_RESULT, 0, a.epoch, false);
   }
@@ -386,13 +429,26 @@ __global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
 
 size_t router_lds_bytes(uint32_t d) { return (size_t)kMaxExperts * d * 2 > (size_t)kRouterTokens * 65 * 4 ? (size_t)kMaxExperts * d * 2 : (size_t)kRouterTokens * 65 * 4; }
 
-hipError_t launch_router(const MoeArgs& a, hipStream_t s) {
+template <int kBlocks>
+static hipError_t launch_router_blocks(const MoeArgs& a, hipStream_t s) {
   const size_t lds = router_lds_bytes(a.d);
-  hipError_t e = hipFuncSetAttribute((const void*)k_router, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = hipFuncSetAttribute((const void*)k_router<kBlocks>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const uint64_t blocks = (a.tokens + kRouterTokens - 1) / kRouterTokens;
-  hipLaunchKernelGGL(k_router, dim3((uint32_t)blocks), dim3(kRouterThreads), lds, s, a);
+  hipLaunchKernelGGL(k_router<kBlocks>, dim3((uint32_t)blocks), dim3(kRouterThreads), lds, s, a);
   return hipGetLastError();
+}
+
+// d is a multiple of 256 and at most 1280 (checked at plan time)
+hipError_t launch_router(const MoeArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 256: return launch_router_blocks<2>(a, s);
+    case 512: return launch_router_blocks<4>(a, s);
+    case 768: return launch_router_blocks<6>(a, s);
+    case 1024: return launch_router_blocks<8>(a, s);
+    case 1280: return launch_router_blocks<10>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_moe_prefix(const MoeArgs& a, hipStream_t s) {
@@ -419,7 +475,7 @@ hipError_t launch_ffn(const MoeArgs& a, bool second, uint32_t cus, hipStream_t s
 }
 
 hipError_t launch_combine(const MoeArgs& a, hipStream_t s) {
-  const uint64_t blocks = std::min<uint64_t>((a.tokens + 3) / 4, kCombineBlocks);
+  const uint64_t blocks = std::min<uint64_t>((a.tokens + 4 * kCombineTokens - 1) / (4 * kCombineTokens), kCombineBlocks);
   hipLaunchKernelGGL(k_combine, dim3((uint32_t)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
