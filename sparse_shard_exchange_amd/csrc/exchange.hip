@@ -173,51 +173,113 @@ __device__ __forceinline__ void scan_finish(const ExchangeArgs& a, ScanShared& s
 }
 
 // --------------------------------------------------------------------- rank
-// A wave's destinations, loaded before any is used (up to kMaxChunks chunks
-// of 64 tuples: tile <= 4096 split over 4 waves), so that the loads of its
-// whole sub-tile are in flight together.
-constexpr uint32_t kMaxChunks = 16;
-
+// A wave's destinations (kChunks chunks of 64 tuples: tile / 256), loaded
+// before any is checked, so that the loads of its whole sub-tile are in
+// flight together: the loads are unconditional (indices clamped to the last
+// tuple) because a load under a branch, or one whose value is checked right
+// away, makes the compiler wait for it before issuing the next. -1: past the
+// end, or out of range (latched through `bad`).
+template <uint32_t kChunks>
 struct WaveDests {
-  int d[kMaxChunks];
+  int d[kChunks];
 };
 
-__device__ __forceinline__ WaveDests load_wave_dests(const ExchangeArgs& a, uint64_t g0, uint32_t sub, uint32_t lane,
-                                                     bool& bad) {
-  WaveDests w;
+template <uint32_t kChunks>
+__device__ __forceinline__ WaveDests<kChunks> load_wave_dests(const ExchangeArgs& a, uint64_t g0, uint32_t lane,
+                                                              bool& bad) {
+  WaveDests<kChunks> w;
+  if (a.G == 0) {  // uniform: an empty step reads nothing
 #pragma unroll
-  for (uint32_t i = 0; i < kMaxChunks; ++i) w.d[i] = i * 64 < sub ? load_dest(a, g0 + i * 64 + lane, bad) : -1;
+    for (uint32_t i = 0; i < kChunks; ++i) w.d[i] = -1;
+    return w;
+  }
+  const uint64_t last = a.G - 1;
+#pragma unroll
+  for (uint32_t i = 0; i < kChunks; ++i) w.d[i] = a.dest[min<uint64_t>(g0 + i * 64 + lane, last)];
+#pragma unroll
+  for (uint32_t i = 0; i < kChunks; ++i) {
+    const int d = w.d[i];
+    const bool in_range = d >= 0 && (uint32_t)d < a.N;
+    const bool exists = g0 + i * 64 + lane < a.G;
+    bad |= exists && !in_range;
+    w.d[i] = exists && in_range ? d : -1;
+  }
   return w;
 }
 
 // At least 8 waves per SIMD (the compiler then keeps some scalars in vector
 // lanes): 4096 ranking tiles are then exactly two rounds of resident
 // workgroups instead of 2.3 (rank 60 -> 58 us).
+//
+// The ballot matching costs about eight vector instructions per key bit per
+// chunk, and bounds this kernel by instruction issue. A tile usually holds far
+// fewer distinct destinations than N (a source shard sends to a few shards),
+// so the destinations present in the tile are first given dense ids (their
+// order among the present ones) and the lanes are matched on the bits of
+// those ids only: 2 bits instead of 8 for 4 destinations out of 256. Equal
+// ids mean equal destinations, so the groups, and the ranks, are the same
+// (rank 44 -> 30 us on 256 shards x 65536 tuples sent to 4 shards each).
+// Tried and dropped: with at most 4 ids, one running count per id in scalar
+// registers and one ballot per id and chunk instead of the matching (39 us).
+template <uint32_t kChunks>
 __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
   extern __shared__ uint32_t lds[];
+  __shared__ uint32_t s_wsum[kWaves];
   const uint32_t N = a.N;
   uint32_t* wrun = lds;  // [kWaves][N]: counts of each wave's sub-tile, then its next rank per destination
+  uint16_t* cid = reinterpret_cast<uint16_t*>(lds + kWaves * N);  // [N]: 1 if present, then the dense id
   for (uint32_t i = threadIdx.x; i < kWaves * N; i += kBlock) wrun[i] = 0;
-  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < N; i += kBlock) cid[i] = 0;
   const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t sub = a.tile / kWaves;
+  constexpr uint32_t sub = kChunks * 64;  // the wave's sub-tile (tile = 4 sub-tiles)
   const uint64_t g0 = (uint64_t)blockIdx.x * a.tile + (uint64_t)w * sub;
   uint32_t* mine = wrun + w * N;
   bool bad = false;
+  const WaveDests<kChunks> wd = load_wave_dests<kChunks>(a, g0, lane, bad);
+  __syncthreads();
+  // 0. dense ids of the destinations present in the tile, 256 destinations
+  //    at a time: a ballot of the present ones, offset by the earlier waves'
+  //    and the earlier rounds' counts
+#pragma unroll
+  for (uint32_t i = 0; i < kChunks; ++i)
+    if (wd.d[i] >= 0) cid[wd.d[i]] = 1;
+  __syncthreads();
+  uint32_t K = 0;  // destinations present (uniform)
+  for (uint32_t d0 = 0; d0 < N; d0 += kBlock) {
+    const uint32_t d = d0 + threadIdx.x;
+    const bool present = d < N && cid[d] != 0;
+    const uint64_t m = __ballot(present);
+    if (lane == 0) s_wsum[w] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t pre = K, tot = 0;
+#pragma unroll
+    for (uint32_t ww = 0; ww < kWaves; ++ww) {
+      const uint32_t c = s_wsum[ww];
+      pre += ww < w ? c : 0u;
+      tot += c;
+    }
+    if (present) {
+      const uint32_t id = pre + (uint32_t)__popcll(m & lanemask_lt(lane));
+      cid[d] = (uint16_t)id;
+    }
+    K += tot;
+    __syncthreads();
+  }
+  K = __builtin_amdgcn_readfirstlane(K);
+  const uint32_t nb = K <= 1 ? 0u : 32u - (uint32_t)__builtin_clz(K - 1);  // bits of the largest id
   // 1. per-wave counts of its contiguous sub-tile: each 64-tuple chunk's
-  //    lanes are matched by destination once (ballots); the lowest lane of
+  //    lanes are matched by destination id once (ballots); the lowest lane of
   //    each group adds the group's size (one LDS atomic per group: one per
   //    lane queued up to 64 deep on a tile's few destinations) and every lane
   //    keeps its rank inside the group, 16 bits each, for step 3
-  const WaveDests wd = load_wave_dests(a, g0, sub, lane, bad);
-  uint32_t grp[kMaxChunks];  // rank inside the chunk's group | group size << 16
+  uint32_t grp[kChunks];  // rank inside the chunk's group | group size << 16
 #pragma unroll
-  for (uint32_t i = 0; i < kMaxChunks; ++i) {
+  for (uint32_t i = 0; i < kChunks; ++i) {
     grp[i] = 0;
-    if (i * 64 >= sub) continue;  // uniform
     const int d = wd.d[i];
     const bool valid = d >= 0;
-    const uint64_t peers = match_peers(d, valid, a.nbits);
+    const int c = valid ? (int)cid[d] : -1;
+    const uint64_t peers = match_peers(c, valid, nb);
     if (valid) {
       const uint32_t rank = (uint32_t)__popcll(peers & lanemask_lt(lane)), n = (uint32_t)__popcll(peers);
       if (rank == 0) atomicAdd(&mine[d], n);
@@ -243,8 +305,7 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
   // 3. stable rank inside the tile: the chunks in order, each group starting
   //    where the earlier chunks (and earlier waves) left its destination
 #pragma unroll
-  for (uint32_t i = 0; i < kMaxChunks; ++i) {
-    if (i * 64 >= sub) break;  // uniform
+  for (uint32_t i = 0; i < kChunks; ++i) {
     const int d = wd.d[i];
     if (d >= 0) {
       const uint32_t rank = grp[i] & 0xffffu;
@@ -562,8 +623,19 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
 
 }  // namespace
 
+// tile / 256 chunks of 64 tuples per wave (tiles are powers of two in
+// [256, 4096], chosen at plan time)
 hipError_t launch_rank(const ExchangeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_rank, dim3(a.num_tiles), dim3(kBlock), (size_t)kWaves * a.N * sizeof(uint32_t), s, a);
+  // per-wave counts [kWaves][N] u32, then the dense ids [N] u16
+  const size_t lds = (size_t)kWaves * a.N * sizeof(uint32_t) + ((size_t)a.N * 2 + 3) / 4 * 4;
+  switch (a.tile) {
+    case 256: hipLaunchKernelGGL(k_rank<1>, dim3(a.num_tiles), dim3(kBlock), lds, s, a); break;
+    case 512: hipLaunchKernelGGL(k_rank<2>, dim3(a.num_tiles), dim3(kBlock), lds, s, a); break;
+    case 1024: hipLaunchKernelGGL(k_rank<4>, dim3(a.num_tiles), dim3(kBlock), lds, s, a); break;
+    case 2048: hipLaunchKernelGGL(k_rank<8>, dim3(a.num_tiles), dim3(kBlock), lds, s, a); break;
+    case 4096: hipLaunchKernelGGL(k_rank<16>, dim3(a.num_tiles), dim3(kBlock), lds, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
