@@ -193,6 +193,18 @@ __device__ __forceinline__ WaveDests<kChunks> load_wave_dests(const ExchangeArgs
     for (uint32_t i = 0; i < kChunks; ++i) w.d[i] = -1;
     return w;
   }
+  if (g0 + kChunks * 64 <= a.G) {  // uniform: the whole sub-tile exists (every tile but the last)
+    const int* p = a.dest + g0 + lane;
+#pragma unroll
+    for (uint32_t i = 0; i < kChunks; ++i) w.d[i] = p[i * 64];
+#pragma unroll
+    for (uint32_t i = 0; i < kChunks; ++i) {
+      const bool in_range = (uint32_t)w.d[i] < a.N;  // also rejects negatives
+      bad |= !in_range;
+      w.d[i] = in_range ? w.d[i] : -1;
+    }
+    return w;
+  }
   const uint64_t last = a.G - 1;
 #pragma unroll
   for (uint32_t i = 0; i < kChunks; ++i) w.d[i] = a.dest[min<uint64_t>(g0 + i * 64 + lane, last)];
