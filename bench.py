@@ -113,12 +113,16 @@ def chain_sweep(pw, torch, pw_inputs, steps):
 
 def dispatch_study(pw, torch, pw_inputs, total=4096):
     """Per-node cost of the chained A -> B program against program length D
-    (steps per call) for four ways of dispatching it: the persistent executor
-    (one launch per call, device-side futures gate every node), parallel
-    asynchronous dispatch (one launch per node, all enqueued without waiting),
-    a fused kernel loop (no futures), and sequential dispatch (one step per
-    call, the host waiting for it before the next)."""
-    modes = {"chained": pw.PW_CHAIN_CHAINED, "opbyop": pw.PW_CHAIN_OPBYOP, "fused": pw.PW_CHAIN_FUSED}
+    (steps per call) for five ways of dispatching it: the persistent executor
+    (one launch per call, device-side futures gate every node) with A[i] and
+    B[i] on the same wave ("chained") or on different workgroups, normally on
+    different XCDs ("split": every gate a cross-workgroup release and
+    acquire), parallel asynchronous dispatch (one launch per node, all
+    enqueued without waiting), a fused kernel loop (no futures), and
+    sequential dispatch (one step per call, the host waiting for it before the
+    next)."""
+    modes = {"chained": pw.PW_CHAIN_CHAINED, "split": pw.PW_CHAIN_SPLIT, "opbyop": pw.PW_CHAIN_OPBYOP,
+             "fused": pw.PW_CHAIN_FUSED}
     depths = (1, 4, 16, 64, 256, 1024, 4096)
     out = {"total_steps_per_point": total, "elems_per_shard": 128, "unit": "ns per gated node (2 nodes per step)",
            "by_n": {}}
