@@ -108,9 +108,11 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
       L.G = (uint64_t)S * d.tuples_per_shard * fan;
       L.tile = pick_tile(L.G);
       L.num_tiles = (uint32_t)std::max<uint64_t>(1, (L.G + L.tile - 1) / L.tile);
-      // ~sqrt(num_tiles) tiles per scan block: both scan levels stay short
+      // 16 tiles per scan block (more only beyond 4096 tiles): at most 256
+      // blocks, so the scan's second level holds every block total of a
+      // destination in 16 threads x 16 registers
       L.scan_tiles = 16;
-      while ((uint64_t)L.scan_tiles * L.scan_tiles < L.num_tiles) L.scan_tiles *= 2;
+      while ((uint64_t)L.scan_tiles * 256 < L.num_tiles) L.scan_tiles *= 2;
       L.num_blk = (L.num_tiles + L.scan_tiles - 1) / L.scan_tiles;
       L.width = std::max<uint32_t>(std::max(N, S), 1);
       L.fut = c.take((size_t)kNodes * L.width * 4);
