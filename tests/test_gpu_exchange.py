@@ -119,6 +119,25 @@ def test_exchange_parity(gpu, n, t, p, kind):
     assert ep[pw.PW_NODE_RESULT, 0] == 1 and fi[pw.PW_NODE_RESULT, 0] == 1
 
 
+def test_more_than_4096_tiles(gpu):
+    """18 M tuples over 3 destinations: 4395 ranking tiles, so the scan's
+    blocks hold 32 tiles (two rounds per column) and its second level runs
+    as its own launch with a partial group of destinations."""
+    pw = gpu
+    n, t = 3, 6_000_000
+    print(f"exchange N={n} T={t} P=1 (more than 4096 tiles)", flush=True)
+    x = torch.from_numpy(pw_inputs.exchange_uniform(n, t, 1).x)
+    dest = _dest_case("uniform", n, t)
+    ex, _ = run(pw, x, dest, n, t)
+    ref = ox.exchange_step(x.numpy(), dest, n, n)
+    assert np.array_equal(ex.offsets.cpu().numpy(), ref.offsets)
+    assert np.array_equal(ex.counts.cpu().numpy(), ref.counts.astype(np.int32))
+    assert np.array_equal(ex.src_index.cpu().numpy(), ref.src_index.astype(np.int32))
+    assert np.array_equal(_bits(ex.dst), ref.y.view(np.uint32))
+    ep, fi, _ = ex.plan.read_futures()
+    assert np.all(fi[pw.PW_NODE_EXCHANGE, :n] == 1) and fi[pw.PW_NODE_RESULT, 0] == 1
+
+
 def test_tiny_rows_full_size_chunks(gpu):
     """16.7 M tuples of one fp32: 4096-tuple tiles and the largest scatter
     chunk (1024 tuples per workgroup, 4 per tile)."""
