@@ -82,7 +82,7 @@ def chain_sweep(pw, torch, pw_inputs, steps):
              "fused": pw.PW_CHAIN_FUSED}
     out = {"steps": steps, "elems_per_shard": 128, "steps_per_s": {}, "ns_per_node": {},
            "placement": "chained: A[i] and B[i] on the same lanes (gate ordered by program order); split: A[i] "
-                        "and B[i] on different workgroups, normally different XCDs (cross-CU release/acquire)",
+                        "and B[i] on different workgroups, normally different XCDs (cross-CU handoff: coherent stores, epoch, coherent loads)",
            "split_cross_xcd_fraction": {}}
     for name, mode in modes.items():
         out["steps_per_s"][name] = {}

@@ -10,7 +10,8 @@
 // shards sends one tuple to the same shard of the next node.
 //
 // Split placement (k_chain_split): A[i] and B[i] on different workgroups,
-// normally on different XCDs, so every gate is a cross-CU release/acquire.
+// normally on different XCDs, so every gate is a handoff across CUs (coherent
+// stores, an epoch store, coherent loads).
 //
 // Device mapping of the default chained kernel: one group of lanes per shard (the whole wave, or with
 // 128-element shards and many shards half of it, so that the CUs hold fewer
@@ -78,6 +79,25 @@ __device__ __forceinline__ void node_body(const float* in, float* out, uint32_t 
     out[e + 64] = body(kind, ca, cb, x1);
   }
   if (e < E) out[e] = body(kind, ca, cb, in[e]);
+}
+
+// node_body for data handed across XCDs inside one launch: every load and
+// store is agent-coherent (device.h), so that no fence is needed around it.
+__device__ __forceinline__ void node_body_coherent(const float* in, float* out, uint32_t E, uint32_t lane,
+                                                   uint32_t kind, float ca, float cb) {
+  const __amdgpu_buffer_rsrc_t ri = raw_buffer(in, E * 4u), ro = raw_buffer(out, E * 4u);
+  uint32_t e = lane;
+  for (; e + 64 < E; e += 128) {
+    const float x0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ri, e * 4u, 0, kCoherent));
+    const float x1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ri, (e + 64) * 4u, 0, kCoherent));
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, body(kind, ca, cb, x0)), ro, e * 4u, 0, kCoherent);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, body(kind, ca, cb, x1)), ro, (e + 64) * 4u, 0,
+                                          kCoherent);
+  }
+  if (e < E) {
+    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ri, e * 4u, 0, kCoherent));
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, body(kind, ca, cb, x)), ro, e * 4u, 0, kCoherent);
+  }
 }
 
 // Fire a future whose only consumer is this lane group (its first lane calls
@@ -151,17 +171,17 @@ __global__ __launch_bounds__(256) void k_chain_chained(ChainArgs a) {
 // so A[i] and B[i] run on different waves of different workgroups; A prefers
 // the first half of the XCDs and B the second, so the two nodes of a shard
 // normally sit on different XCDs and every future crosses them: the producer
-// writes its node's output, releases (agent scope) and stores the epoch; the
-// consumer polls the epoch with relaxed loads, acquires with one fence, then
-// reads. The claim counters give every shard exactly one wave per role (the
+// writes its node's output with agent-coherent stores, waits until they have
+// completed and stores the epoch; the consumer polls the epoch, then reads
+// with agent-coherent loads (no release or acquire fence, each of which
+// would write back or invalidate the XCD's whole L2). The claim counters give every shard exactly one wave per role (the
 // grid has one wave per (role, group) slot, plus at most three spare waves
 // that find nothing and leave). With PW_FLAG_TRACE each node stamps its last
 // fire at the moment it fires.
 // kG shards per wave (64 / kG lanes each; with kG > 1 the shards have 128
 // elements, 2 kG per lane): a wave claims a group of kG consecutive shards for
-// one role, waits until every one of its shards' inputs fired, and releases
-// once for all of their outputs. Every release writes back the XCD's L2, and
-// thousands of single-shard waves releasing every step queue behind each other.
+// one role, waits until every one of its shards' inputs fired, and publishes
+// all of their outputs after one wait for its stores.
 template <int kG>
 __global__ __launch_bounds__(256) void k_chain_split(ChainArgs a) {
   constexpr uint32_t kLanes = 64 / kG;
@@ -202,7 +222,7 @@ __global__ __launch_bounds__(256) void k_chain_split(ChainArgs a) {
     const uint32_t k = a.epoch0 + j;
     // A of step k consumes B of step k - 1 (the Result; epoch0 = the Arg), B consumes A of step k.
     // Each group's first lane polls its shard's input future (relaxed); the
-    // wave goes on once all have fired, with one acquire fence.
+    // wave goes on once all have fired.
     const uint32_t need = role == 0 ? k - 1 : k;
     bool ok = true;
     if (sub == 0 && mine) ok = epoch_reached(__hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), need);
@@ -219,28 +239,28 @@ __global__ __launch_bounds__(256) void k_chain_split(ChainArgs a) {
       }
       if (__ballot(!ok)) break;  // expired
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if constexpr (kG > 1) {  // 2 kG consecutive elements per lane, as kG / 2 float4 (16-byte aligned)
       if (mine) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
         constexpr int kQ = kG > 1 ? kG / 2 : 1;
-        const float4* src = reinterpret_cast<const float4*>(in) + sub * kQ;
-        float4* dst = reinterpret_cast<float4*>(out) + sub * kQ;
-        float4 x[kQ];
+        const __amdgpu_buffer_rsrc_t ri = raw_buffer(in, a.E * 4u), ro = raw_buffer(out, a.E * 4u);
+        f4 x[kQ];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) x[q] = src[q];
+        for (int q = 0; q < kQ; ++q)
+          x[q] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(ri, (sub * kQ + q) * 16u, 0, kCoherent));
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-          x[q].x = body(kind, ca, cb, x[q].x);
-          x[q].y = body(kind, ca, cb, x[q].y);
-          x[q].z = body(kind, ca, cb, x[q].z);
-          x[q].w = body(kind, ca, cb, x[q].w);
-          dst[q] = x[q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[q][e] = body(kind, ca, cb, x[q][e]);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x[q]), ro, (sub * kQ + q) * 16u, 0,
+                                                 kCoherent);
         }
       }
     } else {
-      node_body(in, out, a.E, lane, kind, ca, cb);
+      node_body_coherent(in, out, a.E, lane, kind, ca, cb);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the wave's stores of every output, then the epochs
+    wait_vmem_all();  // the wave's coherent stores of every output have completed, then the epochs
     if (sub == 0 && mine) {
       const uint32_t idx = node * a.f.width + i;
       if (a.f.stamps && j == a.steps) a.f.stamps[idx] = wall_clock64();

@@ -100,6 +100,48 @@ __device__ __forceinline__ bool await_prior(const Futures& f, uint32_t node, uin
   }
 }
 
+// Agent-coherent accesses, for data handed between workgroups of one launch
+// without cache-wide fences. Each XCD has its own L2: an agent-scope release
+// fence writes back every dirty line of the XCD's L2 and an agent-scope
+// acquire invalidates it (buffer_wbl2 / buffer_inv), several microseconds
+// each, and the invalidation also throws away every other workgroup's cached
+// data. Instead, each access to such data carries the agent-scope coherence
+// bit (sc1), as the compiler's relaxed agent-scope atomic loads and stores
+// do: such a store writes through to the memory side, such a load does not
+// hit a possibly stale cached copy. A producer waits until its coherent
+// stores have completed (vmcnt 0) before the counter add or flag store that
+// publishes them; a consumer issues its coherent loads only after it has seen
+// that flag (a value it branched on, or a barrier after the wait).
+constexpr int kCoherent = 16;  // sc1 in the cache-policy operand of buffer instructions
+constexpr int kRawBufWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit format, stride 0, size in bytes
+
+// A raw buffer resource over `bytes` bytes at p (bytes < 2^31); accesses past
+// the end return zero / are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRawBufWord3);
+}
+
+// Wait until every vector-memory operation of this wave has completed; a
+// compiler barrier as well.
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// await() for consumers whose reads of the producer's data are coherent
+// loads: the same bounded poll, without the acquire fence.
+__device__ __forceinline__ bool await_coherent(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
+  const uint32_t* p = &f.epoch[node * f.width + shard];
+  bool ok = epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
+  const uint64_t t0 = ok ? 0 : wall_clock64();
+  while (!ok) {
+    __builtin_amdgcn_s_sleep(1);
+    ok = epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
+    if (!ok && wall_clock64() - t0 > f.spin_ticks) {
+      latch(f, ST_TIMEOUT);
+      return false;
+    }
+  }
+  return true;
+}
+
 // Which XCD (accelerator complex die, with its own L2) this wave runs on.
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;

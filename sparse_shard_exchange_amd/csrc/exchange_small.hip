@@ -12,36 +12,38 @@
 //   1. workgroup b ranks the tuples of its slab of S consecutive tuples per
 //      destination, 64 at a time by wave ballots (stable: chunk order, then
 //      lane order), and loads the slab's payload (<= 32 KiB) into registers;
-//   2. wave 0 publishes the slab's per-destination counts (a row of the slab
-//      table) and release-adds the call's publish counter; every workgroup
-//      waits (bounded) until all have published: the one device-wide step
-//      the counting sort needs, since a destination's segment start depends
-//      on every earlier destination's total;
-//   3. each workgroup reads the slab table (at most 8192 words) and derives
+//   2. wave 0 publishes the slab's per-destination counts as a row of the
+//      slab table, each entry tagged with the call;
+//   3. every workgroup reads the whole table (at most 8192 entries), waiting
+//      (bounded) until every entry carries this call's tag: the one
+//      device-wide step the counting sort needs, since a destination's
+//      segment start depends on every earlier destination's total. From it,
 //      the totals, the segment offsets and its own run start inside each
-//      segment, then stores its rows straight from registers (A applied);
-//   4. one release, then an add per destination it wrote to; the add that
-//      completes a destination fires EXCHANGE[d] (release);
-//   5. B: workgroup b takes output rows [b S, (b + 1) S); it acquire-waits
-//      the EXCHANGE futures of the destinations those rows belong to, so B of
-//      a segment starts as soon as that segment is complete, while other
+//      segment; then it stores its rows straight from registers (A applied);
+//   4. once its row stores have completed, an add per destination it wrote
+//      to; the add that completes a destination fires EXCHANGE[d];
+//   5. B: workgroup b takes output rows [b S, (b + 1) S); it waits for the
+//      EXCHANGE futures of the destinations those rows belong to, so B of a
+//      segment starts as soon as that segment is complete, while other
 //      workgroups still scatter. The add that completes a segment's B fires
 //      B[d]; the last B fires the Result.
 //
-// Measured on this part, every such device-wide hop (a release, an atomic, a
-// poll, an acquire) costs a few microseconds, more than the kernel boundary
-// that orders the separate launches does, so the separate launches stay the
-// default; this path is the in-launch form of the gating.
+// Everything handed between workgroups here (table entries, rows) is
+// written and read with agent-coherent accesses (device.h), never through an
+// agent-scope release or acquire fence: on this part such a fence writes
+// back or invalidates a whole XCD's L2 and costs microseconds per workgroup
+// (the fenced form of this kernel ran 28 us per 8-shard step, this one
+// about 19). Each hop still costs about a microsecond or two of memory
+// latency.
 //
-// The grid must be co-resident (step 2 waits for every workgroup); the plan
+// The grid must be co-resident (step 3 waits for every workgroup); the plan
 // takes this path only for grids of at most 256 workgroups of 256 threads,
 // after checking the occupancy. Every wait is bounded by the plan's spin
 // limit; an expired wait latches a timeout and the workgroup leaves. The
-// publish counter is cumulative (target: calls x grid) and every workgroup
-// adds to it once per call whatever happens, so it stays aligned. The arrival
-// counters come in two sets used by alternate calls; a call clears the other
-// set (which the previous call used) for the next one, so no clearing races
-// with this call's adds.
+// table's tags make it safe to reuse across calls without clearing. The
+// arrival counters come in two sets used by alternate calls; a call clears
+// the other set (which the previous call used) for the next one, so no
+// clearing races with this call's adds.
 #include <algorithm>
 
 #include "device.h"
@@ -59,8 +61,6 @@ constexpr uint32_t kMaxChunks = kMaxSlab / 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bool reached(uint32_t v, uint32_t target) { return (int32_t)(v - target) >= 0; }
-
 struct SmallShared {
   uint32_t cnt[kMaxChunks][kMaxN];  // per 64-tuple chunk: counts, then the chunk's start inside the slab's run
   uint32_t mine[kMaxN];             // the slab's tuples per destination
@@ -69,7 +69,6 @@ struct SmallShared {
   uint32_t tup[kMaxSlab];           // rank inside its chunk's group | destination << 16; ~0: dropped
   int slot[kMaxSlab];
   uint32_t red_t[kBlock], red_p[kBlock];
-  uint32_t ok;
 };
 
 __device__ __forceinline__ u32x4 affine4(u32x4 v, float ca, float cb) {
@@ -81,28 +80,38 @@ __device__ __forceinline__ u32x4 affine4(u32x4 v, float ca, float cb) {
   return __builtin_bit_cast(u32x4, f);
 }
 
+// Bytes of the destination rows, as a buffer size (< 2^31: the one-launch
+// path holds at most 256 Ki tuples of at most 512 bytes, so every slot it
+// writes lies below it). Offsets at or past it read zero.
+__device__ __forceinline__ uint32_t dst_bytes(const ExchangeArgs& a) {
+  return (uint32_t)min<uint64_t>((uint64_t)a.dst_rows * a.row_bytes, 0x7fffffffu);
+}
+
 // Row sums of output rows [r0, r1) (fp32, P elements, P % 4 == 0): 16 lanes
 // per row, 16 rows per pass, each lane summing float4 chunks l16, l16 + 16,
 // ... as (x + y) + (z + w), then a butterfly over the 16 lanes. The loads of
 // kPasses passes (128 rows: a whole slab of 256-byte rows) are in flight
-// together. The same arithmetic, in the same order, as the separate B
-// kernel, so both paths give the same bits.
-__device__ __forceinline__ void rowsum_rows(const ExchangeArgs& a, int64_t r0, int64_t r1) {
+// together; they are coherent loads (the rows were written by other
+// workgroups of this launch), and those of rows past r1 or chunks past the
+// row end go out of range and read zero. The same arithmetic, in the same
+// order, as the separate B kernel, so both paths give the same bits.
+__device__ __forceinline__ void rowsum_rows(const ExchangeArgs& a, __amdgpu_buffer_rsrc_t rows, int64_t r0,
+                                            int64_t r1) {
   constexpr uint32_t kPasses = 8;
   const uint32_t P4 = a.row_bytes / 16u;  // float4 chunks per row (<= 32)
-  const float4* y = reinterpret_cast<const float4*>(a.dst);
+  const uint32_t oob = dst_bytes(a);
   float* out = reinterpret_cast<float*>(a.b_out);
   const uint32_t l16 = threadIdx.x & 15, r = threadIdx.x >> 4;
   for (int64_t base = r0; base < r1; base += 16 * kPasses) {
-    float4 v0[kPasses], v1[kPasses];
+    f32x4 v0[kPasses], v1[kPasses];
 #pragma unroll
     for (uint32_t p = 0; p < kPasses; ++p) {
       const int64_t s = base + p * 16 + r;
-      v0[p] = v1[p] = float4{0.f, 0.f, 0.f, 0.f};
-      if (s < r1) {
-        if (l16 < P4) v0[p] = y[s * P4 + l16];
-        if (l16 + 16 < P4) v1[p] = y[s * P4 + l16 + 16];
-      }
+      const uint32_t c = (uint32_t)s * P4 + l16;
+      const uint32_t o0 = s < r1 && l16 < P4 ? c * 16u : oob;
+      const uint32_t o1 = s < r1 && l16 + 16 < P4 ? (c + 16) * 16u : oob;
+      v0[p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, o0, 0, kCoherent));
+      v1[p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rows, o1, 0, kCoherent));
     }
 #pragma unroll
     for (uint32_t p = 0; p < kPasses; ++p) {
@@ -158,9 +167,7 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
   }
 
   // 1. the destinations first (wave w ranks chunks w, w + 4, ...), then the
-  //    payload of waves 1-3. Wave 0 publishes the counts, and its stores of
-  //    them must be complete first; the vector-memory counter retires in
-  //    order, so wave 0 loads its payload only after the publish.
+  //    payload
   constexpr uint32_t kPerWave = kMaxChunks / 4;
   int dv[kPerWave];
   uint32_t in_range = 0;
@@ -171,7 +178,7 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
     dv[j] = a.dest[g0 + min(t, nt - 1)];
   }
   u32x4 v[kUnits];
-  if (w != 0) load_payload(a, g0, units, vu, v);
+  load_payload(a, g0, units, vu, v);
   for (uint32_t i = tid; i < chunks * kMaxN; i += kBlock) sh.cnt[i / kMaxN][i % kMaxN] = 0;
   __syncthreads();
   bool bad = false;
@@ -193,65 +200,66 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
     if (ir) sh.tup[c * 64 + lane] = code;
   }
   __syncthreads();
-  // 2. wave 0: the slab's counts, its row of the slab table, the publish
-  if (w == 0) {
-    if (tid < N) {
-      uint32_t run = 0;
-      for (uint32_t c = 0; c < chunks; ++c) {
-        const uint32_t x = sh.cnt[c][tid];
-        sh.cnt[c][tid] = run;
-        run += x;
-      }
-      sh.mine[tid] = run;
-      a.slab_cnt[(uint64_t)b * N + tid] = run;
+  // 2. wave 0: the slab's counts and its row of the slab table, each entry
+  //    tagged with the call (one coherent 64-bit store: count | call << 32)
+  if (tid < N) {
+    uint32_t run = 0;
+    for (uint32_t c = 0; c < chunks; ++c) {
+      const uint32_t x = sh.cnt[c][tid];
+      sh.cnt[c][tid] = run;
+      run += x;
     }
-    if (tid == 0)  // release: the count stores above (all of this wave's) are complete and visible first
-      __hip_atomic_fetch_add(a.small_ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    load_payload(a, g0, units, vu, v);
-    if (tid == 0) {
-      // relaxed polls, one acquire fence once every slab is in (an acquire
-      // load per poll would invalidate the XCD's L2 at each poll)
-      const uint32_t target = a.call * grid;
-      bool ok = reached(__hip_atomic_load(a.small_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), target);
-      const uint64_t t0 = wall_clock64();
-      while (!ok) {
-        __builtin_amdgcn_s_sleep(1);
-        ok = reached(__hip_atomic_load(a.small_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), target);
-        if (!ok && wall_clock64() - t0 > a.f.spin_ticks) {
-          latch(a.f, ST_TIMEOUT);
-          break;
-        }
-      }
-      if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      sh.ok = ok;
-    }
+    sh.mine[tid] = run;
+    __hip_atomic_store(&a.slab_cnt[(uint64_t)b * N + tid], (uint64_t)a.call << 32 | run, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  if (!sh.ok) return;  // uniform
 
   // 3. totals, segment offsets and this slab's run starts, from the table
-  //    (thread t reads column t % N of rows t / N, t / N + R, ...; the loads
-  //    of 8 rows in flight at once)
+  //    (thread t reads column t % N of rows t / N, t / N + R, ...; 8 rows per
+  //    round of coherent loads). The one device-wide step of the counting
+  //    sort, since a destination's segment start depends on every earlier
+  //    destination's total: an entry counts once it carries this call's tag;
+  //    the loads of a round are repeated until all do (bounded).
   const uint32_t R = kBlock / N;
+  bool ok = true;
   if (tid < R * N) {
     const uint32_t d = tid % N;
     uint32_t tt = 0, pp = 0;
-    for (uint32_t r0 = tid / N; r0 < grid; r0 += 8 * R) {
-      uint32_t x[8];
+    const uint64_t t0 = wall_clock64();
+    for (uint32_t r0 = tid / N; r0 < grid && ok; r0 += 8 * R) {
+      const uint64_t* e[8];
+      uint64_t x[8];
 #pragma unroll
-      for (uint32_t u = 0; u < 8; ++u)  // unconditional loads (see load_payload)
-        x[u] = a.slab_cnt[(uint64_t)min(r0 + u * R, grid - 1) * N + d];
+      for (uint32_t u = 0; u < 8; ++u) {  // unconditional loads (see load_payload)
+        e[u] = &a.slab_cnt[(uint64_t)min(r0 + u * R, grid - 1) * N + d];
+        x[u] = __hip_atomic_load(e[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      while (true) {
+        bool all = true;
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) all &= (uint32_t)(x[u] >> 32) == a.call;
+        if (all) break;
+        if (wall_clock64() - t0 > a.f.spin_ticks) {
+          latch(a.f, ST_TIMEOUT);
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u)
+          if ((uint32_t)(x[u] >> 32) != a.call) x[u] = __hip_atomic_load(e[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
 #pragma unroll
       for (uint32_t u = 0; u < 8; ++u) {
-        const uint32_t r = r0 + u * R;
-        tt += r < grid ? x[u] : 0u;
-        pp += r < b ? x[u] : 0u;
+        const uint32_t r = r0 + u * R, n = (uint32_t)x[u];
+        tt += r < grid ? n : 0u;
+        pp += r < b ? n : 0u;
       }
     }
     sh.red_t[tid] = tt;
     sh.red_p[tid] = pp;
   }
-  __syncthreads();
+  if (!__syncthreads_and(ok)) return;  // a slab never published: the call's waits time out
   if (tid < N) {
     uint32_t tt = 0, pp = 0;
     for (uint32_t r = 0; r < R; ++r) {
@@ -300,6 +308,7 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
     sh.slot[t] = slot;
   }
   __syncthreads();
+  const __amdgpu_buffer_rsrc_t out_rows = raw_buffer(a.dst, dst_bytes(a));
 #pragma unroll
   for (uint32_t u = 0; u < kUnits; ++u) {
     const uint32_t i = u * kBlock + tid;
@@ -308,23 +317,23 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
       const int slot = sh.slot[t];
       if (slot >= 0) {
         const u32x4 x = kAffine ? affine4(v[u], a.a_a, a.a_b) : v[u];
-        *reinterpret_cast<u32x4*>(a.dst + (uint64_t)slot * a.row_bytes + (uint64_t)(i - t * vu) * 16u) = x;
+        __builtin_amdgcn_raw_buffer_store_b128(x, out_rows, (uint32_t)slot * a.row_bytes + (i - t * vu) * 16u, 0,
+                                               kCoherent);
       }
     }
   }
   if (bad) latch(a.f, ST_BAD_DEST);
 
-  // 4. progress: one release for the workgroup's rows, then an add per
-  //    destination written; the add that completes one fires its future
-  __builtin_amdgcn_s_waitcnt(0);
+  // 4. progress: every wave's coherent row stores have completed, then an
+  //    add per destination written; the add that completes one fires its
+  //    future (every slab's rows of d were complete before its add)
+  wait_vmem_all();
   __syncthreads();
-  if (tid < N && sh.mine[tid]) {  // lanes of wave 0: one release fence for the wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (tid < N && sh.mine[tid]) {
     const uint32_t n = sh.mine[tid];
     const uint32_t old = __hip_atomic_fetch_add(&arrived[tid], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + n == sh.tot[tid]) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every other slab's rows of d, through their adds
-      fire(a.f, NODE_EXCH, tid, a.epoch, true);
+      fire(a.f, NODE_EXCH, tid, a.epoch, false);
       if (!a.b_gated) {  // B has no work of its own: it completes with its input
         fire(a.f, NODE_B, tid, a.epoch, false);
         const uint32_t r = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -339,19 +348,21 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
   const int64_t r0 = (int64_t)b * S, r1 = min<int64_t>((int64_t)(b + 1) * S, sh.seg[N]);
   if (r0 >= r1) return;  // uniform
   bool in = false;
-  bool ok = true;
+  bool ready = true;
   if (tid < N) {
     in = sh.tot[tid] && sh.seg[tid] < r1 && sh.seg[tid + 1] > r0;
-    if (in) ok = await(a.f, NODE_EXCH, tid, a.epoch);
+    if (in) ready = await_coherent(a.f, NODE_EXCH, tid, a.epoch);
   }
-  if (!__syncthreads_and(ok)) return;
+  if (!__syncthreads_and(ready)) return;
+  const __amdgpu_buffer_rsrc_t in_rows = raw_buffer(a.dst, dst_bytes(a));
   if (a.b_kind == OP_ROWSUM) {
-    rowsum_rows(a, r0, r1);
+    rowsum_rows(a, in_rows, r0, r1);
   } else if (a.b_kind == OP_AFFINE) {
     const uint32_t P = a.row_bytes / 4u;
-    const float* y = reinterpret_cast<const float*>(a.dst);
     float* out = reinterpret_cast<float*>(a.b_out);
-    for (int64_t i = r0 * (int64_t)P + tid; i < r1 * (int64_t)P; i += kBlock) out[i] = fmaf(a.b_a, y[i], a.b_b);
+    for (uint32_t i = (uint32_t)r0 * P + tid; i < (uint32_t)r1 * P; i += kBlock)
+      out[i] = fmaf(a.b_a, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(in_rows, i * 4u, 0, kCoherent)),
+                    a.b_b);
   }
   __syncthreads();
   if (in) {

@@ -114,7 +114,9 @@ __device__ __forceinline__ Lanes lane_offsets(const Tile& t) {
 
 // Issue half h (0 or 1) of the direct-to-LDS loads of K columns [k0, k0 + 32)
 // into one stage: loads 2h and 2h + 1 of A and of B^T (4 vector-memory
-// operations per lane).
+// operations per lane). kAuxA: cache-policy bits of the A loads (e.g. sc0,
+// served past the CU's L1, when A was written by other CUs of the launch).
+template <int kAuxA>
 __device__ __forceinline__ void issue_half(const Tile& t, const Lanes& o, int k0, unsigned char* stage, int h) {
   const int w = threadIdx.x >> 6;
   const unsigned char* A = reinterpret_cast<const unsigned char*>(t.A) + (uint32_t)k0 * 2u;
@@ -122,7 +124,7 @@ __device__ __forceinline__ void issue_half(const Tile& t, const Lanes& o, int k0
 #pragma unroll
   for (int ii = 0; ii < 2; ++ii) {
     const int i = 2 * h + ii, group = w * 4 + i;
-    __builtin_amdgcn_global_load_lds(A + o.a[i], (lds_ptr)(stage + group * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(A + o.a[i], (lds_ptr)(stage + group * 1024), 16, 0, kAuxA);
     __builtin_amdgcn_global_load_lds(B + o.b[i], (lds_ptr)(stage + kHalf + group * 1024), 16, 0, 0);
   }
 }
@@ -211,14 +213,14 @@ __device__ __forceinline__ unsigned char* ring_slot(unsigned char* lds, int stag
 // ks + 2 / the first half of stage ks + 3. kWait: vector-memory operations
 // allowed in flight once stage ks + 1 has landed (those issued after it: the
 // two halves of stage ks + 2, 8 operations, while there is one).
-template <bool kLoadB, bool kLoadA, int kWait>
+template <bool kLoadB, bool kLoadA, int kWait, int kAuxA>
 __device__ __forceinline__ void k_stage(const Tile& t, const Lanes& o, const Frag& f, unsigned char* lds, int ks,
                                         bf16x8 (&a0)[4], bf16x8 (&b0)[4], bf16x8 (&a1)[4], bf16x8 (&b1)[4],
                                         f32x16 (&acc)[4][4]) {
   read_frags(ring_slot(lds, ks), f, 1, a1, b1);
   // loads after the reads in program order: the compiler keeps LDS-writing
   // loads behind earlier LDS reads (these go to another slot)
-  if (kLoadB) issue_half(t, o, (ks + kStages - 2) * BK, ring_slot(lds, ks + kStages - 2), 1);
+  if (kLoadB) issue_half<kAuxA>(t, o, (ks + kStages - 2) * BK, ring_slot(lds, ks + kStages - 2), 1);
   mfma_step(a0, b0, acc);
   schedule_half<kLoadB>();
   wait_vmem<kWait>();
@@ -227,7 +229,7 @@ __device__ __forceinline__ void k_stage(const Tile& t, const Lanes& o, const Fra
   // (on the last stage this reads a stale slot, harmlessly: the reads stay
   // unconditional so that the counter waits stay exact)
   read_frags(ring_slot(lds, ks + 1), f, 0, a0, b0);
-  if (kLoadA) issue_half(t, o, (ks + kStages - 1) * BK, ring_slot(lds, ks + kStages - 1), 0);
+  if (kLoadA) issue_half<kAuxA>(t, o, (ks + kStages - 1) * BK, ring_slot(lds, ks + kStages - 1), 0);
   mfma_step(a1, b1, acc);
   schedule_half<kLoadA>();
 }
@@ -235,15 +237,16 @@ __device__ __forceinline__ void k_stage(const Tile& t, const Lanes& o, const Fra
 // The loads of the first stages of a tile (stages 0 and 1, the first half of
 // stage 2): issued ahead, e.g. while the previous tile's epilogue runs, once
 // every wave has finished reading the ring. tile_finish must follow with the
-// same tile.
+// same tile (and the same kAuxA).
+template <int kAuxA = 0>
 __device__ __forceinline__ void tile_start(const Tile& t, unsigned char* lds) {
   const Lanes o = lane_offsets(t);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    issue_half(t, o, s * BK, ring_slot(lds, s), 0);
-    issue_half(t, o, s * BK, ring_slot(lds, s), 1);
+    issue_half<kAuxA>(t, o, s * BK, ring_slot(lds, s), 0);
+    issue_half<kAuxA>(t, o, s * BK, ring_slot(lds, s), 1);
   }
-  issue_half(t, o, 2 * BK, ring_slot(lds, 2), 0);
+  issue_half<kAuxA>(t, o, 2 * BK, ring_slot(lds, 2), 0);
 }
 
 // tile_start predicated on `live` without a branch: the same loads through
@@ -252,6 +255,7 @@ __device__ __forceinline__ void tile_start(const Tile& t, unsigned char* lds) {
 // the caller discards after waiting for it). Used where the next tile is
 // started speculatively right before an epilogue: a conditional tile_start
 // there makes the compiler move the accumulators out before the branch.
+template <int kAuxA = 0>
 __device__ __forceinline__ void tile_start_if(const Tile& t, unsigned char* lds, bool live) {
   const Lanes o = lane_offsets(t);
   const int w = threadIdx.x >> 6;
@@ -266,7 +270,8 @@ __device__ __forceinline__ void tile_start_if(const Tile& t, unsigned char* lds,
       for (int ii = 0; ii < 2; ++ii) {
         const int i = 2 * h + ii, group = w * 4 + i;
         unsigned char* stage = ring_slot(lds, s);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(stage + group * 1024), 16, o.a[i] + s * BK * 2, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(stage + group * 1024), 16, o.a[i] + s * BK * 2, 0, 0,
+                                                 kAuxA);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(stage + kHalf + group * 1024), 16, o.b[i] + s * BK * 2, 0, 0, 0);
       }
 }
@@ -274,13 +279,13 @@ __device__ __forceinline__ void tile_start_if(const Tile& t, unsigned char* lds,
 // Stage kHookStage of the K loop with a hook: if hook.active() (uniform),
 // every wave waits for all of its vector-memory operations (so stores issued
 // before the loop are complete), and after the barrier `hook()` runs (e.g.
-// thread 0 publishes an earlier tile with one release).
-template <int kWait, typename Hook>
+// thread 0 publishes an earlier tile).
+template <int kWait, int kAuxA, typename Hook>
 __device__ __forceinline__ void k_stage_hook(const Tile& t, const Lanes& o, const Frag& f, unsigned char* lds, int ks,
                                              bf16x8 (&a0)[4], bf16x8 (&b0)[4], bf16x8 (&a1)[4], bf16x8 (&b1)[4],
                                              f32x16 (&acc)[4][4], Hook& hook) {
   read_frags(ring_slot(lds, ks), f, 1, a1, b1);
-  issue_half(t, o, (ks + kStages - 2) * BK, ring_slot(lds, ks + kStages - 2), 1);
+  issue_half<kAuxA>(t, o, (ks + kStages - 2) * BK, ring_slot(lds, ks + kStages - 2), 1);
   mfma_step(a0, b0, acc);
   schedule_half<true>();
   if (hook.active())
@@ -292,7 +297,7 @@ __device__ __forceinline__ void k_stage_hook(const Tile& t, const Lanes& o, cons
   hook();
   __builtin_amdgcn_sched_barrier(0);
   read_frags(ring_slot(lds, ks + 1), f, 0, a0, b0);
-  issue_half(t, o, (ks + kStages - 1) * BK, ring_slot(lds, ks + kStages - 1), 0);
+  issue_half<kAuxA>(t, o, (ks + kStages - 1) * BK, ring_slot(lds, ks + kStages - 1), 0);
   mfma_step(a1, b1, acc);
   schedule_half<true>();
 }
@@ -312,7 +317,7 @@ constexpr int kHookStage = 2;
 // kHookStage; when hook.active(), every earlier vector-memory operation of
 // every wave is complete by then. On return every wave has finished reading
 // LDS and every load has landed.
-template <typename Hook>
+template <int kAuxA = 0, typename Hook>
 __device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f32x16 (&acc)[4][4], Hook& hook) {
   constexpr int S = kStages, W = 8;
 #pragma unroll
@@ -327,12 +332,12 @@ __device__ __forceinline__ void tile_finish(const Tile& t, unsigned char* lds, f
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   read_frags(lds, f, 0, a0, b0);
   int ks = 0;
-  for (; ks < kHookStage; ++ks) k_stage<true, true, W>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
-  k_stage_hook<W>(t, o, f, lds, ks++, a0, b0, a1, b1, acc, hook);
-  for (; ks < nk - S + 1; ++ks) k_stage<true, true, W>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
-  k_stage<true, false, W>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);  // issues the last half (stage nk-1)
-  k_stage<false, false, 0>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
-  k_stage<false, false, 0>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
+  for (; ks < kHookStage; ++ks) k_stage<true, true, W, kAuxA>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
+  k_stage_hook<W, kAuxA>(t, o, f, lds, ks++, a0, b0, a1, b1, acc, hook);
+  for (; ks < nk - S + 1; ++ks) k_stage<true, true, W, kAuxA>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
+  k_stage<true, false, W, kAuxA>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);  // issues the last half (stage nk-1)
+  k_stage<false, false, 0, kAuxA>(t, o, f, lds, ks++, a0, b0, a1, b1, acc);
+  k_stage<false, false, 0, kAuxA>(t, o, f, lds, ks, a0, b0, a1, b1, acc);
   ring_barrier();
 }
 
@@ -379,6 +384,7 @@ constexpr int kLdsTotal = kLdsBytes;  // the epilogue needs no LDS
 // to lane l and lane l's half of quad 2p + 1 to lane l + 32, so that lane l
 // holds columns 16 p + [0, 8) and lane l + 32 columns 16 p + [8, 16) of the
 // row: one 16-byte store each, 32 contiguous bytes per row and instruction.
+
 template <bool kGelu>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], __bf16* out, int64_t ldo, int rows) {
   typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;

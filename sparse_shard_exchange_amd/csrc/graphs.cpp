@@ -79,10 +79,13 @@ int plan_init_kind(Plan* p) {
     // or with PW_FLAG_STAGE_WINDOWS stage by stage within windows of
     // kWindow microbatches (item (s, m) then comes a whole window of items
     // after (s - 1, m), so its input is long complete, and a window's
-    // activations stay in the last-level cache), are dealt round-robin to
-    // one queue per XCD; an item's tiles (row block, then column block) stay
-    // together in its queue. Both orders keep each stage's microbatches in
-    // ascending order and every item after its predecessor stage. Uploaded once.
+    // activations stay in the last-level cache), go to one queue per XCD by
+    // microbatch: every stage of microbatch m runs on XCD m mod nq, so each
+    // activation block is written and read through one L2 and the handoff
+    // needs no cache-wide fence. An item's tiles (row block, then column
+    // block) stay together in its queue. Both orders keep each stage's
+    // microbatches in ascending order and every item after its predecessor
+    // stage. Uploaded once.
     const pw_plan_desc& d = p->desc;
     const uint32_t S = d.num_shards, M = d.microbatches;
     const uint32_t RB = (uint32_t)((d.tuples_per_shard + 255) / 256), CT = d.payload_elems / 256;
@@ -95,12 +98,14 @@ int plan_init_kind(Plan* p) {
     // share one L2
     int xccs = 0;
     if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, p->device) != hipSuccess || xccs <= 0) xccs = 1;
-    const uint32_t nq = std::min<uint32_t>(std::min<uint32_t>(kQueues, (uint32_t)xccs), ks->grid);
+    // every queue must belong to exactly one XCD (its activations stay in
+    // that XCD's L2)
+    if ((uint32_t)xccs > kQueues) return fail(PW_ERR_UNSUPPORTED, "PIPELINE: %d XCDs, at most %u supported", xccs, kQueues);
+    const uint32_t nq = std::min<uint32_t>((uint32_t)xccs, ks->grid);
     ks->nq = nq;
     std::vector<std::vector<uint32_t>> queues(nq);
-    uint32_t item = 0;
     auto deal = [&](uint32_t s, uint32_t m) {
-      auto& q = queues[item++ % nq];
+      auto& q = queues[m % nq];
       for (uint32_t r = 0; r < RB; ++r)
         for (uint32_t c = 0; c < CT; ++c) q.push_back(s | m << 8 | r << 16 | c << 24);
     };

@@ -132,7 +132,7 @@ int plan_layout(const pw_plan_desc& d, Layout& L) {
         L.slab = exchange_small_slab(L.G, N, row, d.b_op.kind, d.dtype == PW_F32);
         if (L.slab) {
           L.small_grid = (uint32_t)((L.G + L.slab - 1) / L.slab);
-          L.slab_cnt = c.take((size_t)L.small_grid * N * 4);
+          L.slab_cnt = c.take((size_t)L.small_grid * N * 8);
           L.small_tab = c.take((size_t)2 * (2 * N + 1) * 4);
         }
       }
@@ -468,8 +468,7 @@ void exchange_args(const pw_plan_desc& d, const Layout& L, unsigned char* base, 
   a.seg = reinterpret_cast<int64_t*>(base + L.seg);
   a.slab = L.slab;
   a.call = 0;
-  a.slab_cnt = L.slab ? reinterpret_cast<uint32_t*>(base + L.slab_cnt) : nullptr;
-  a.small_ctr = reinterpret_cast<uint32_t*>(base + L.ctl + 64) + 4;
+  a.slab_cnt = L.slab ? reinterpret_cast<uint64_t*>(base + L.slab_cnt) : nullptr;
   a.small_tab = L.slab ? reinterpret_cast<uint32_t*>(base + L.small_tab) : nullptr;
 }
 

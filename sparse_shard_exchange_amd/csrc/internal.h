@@ -69,8 +69,7 @@ struct ExchangeArgs {
   // one-launch path (exchange_small.hip)
   uint32_t slab;              // tuples per workgroup (0: path not available)
   uint32_t call;              // one-launch calls of the plan so far, this one included
-  uint32_t* slab_cnt;         // [grid][N] tuples per (slab, destination)
-  uint32_t* small_ctr;        // cumulative publish counter (target: call x grid)
+  uint64_t* slab_cnt;         // [grid][N] tuples per (slab, destination) | call << 32
   uint32_t* small_tab;        // [2][2N + 1]: arrivals, B arrivals, finished destinations, by call parity
 };
 

@@ -12,11 +12,21 @@
 // h[s][m] = bf16(GELU(h[s-1][m] . W_s)) (rows x d times d x d). The work is cut
 // into 256 x 256 output tiles (s, m, r, c): row block r, column block c. The
 // plan uploads the claim order: items in GPipe lock-step order (tick s + m
-// ascending, then stage) dealt round-robin to one queue per XCD, each item's
-// tiles consecutive. Persistent workgroups claim tiles from their XCD's
-// queue. Tile (s, m, r, c) waits for the row-block future (s - 1, m, r) (all
-// column tiles of that row block of the previous stage written), so a row
-// block flows to the next stage before the rest of its microbatch is done.
+// ascending, then stage), microbatch m's items in the queue of XCD m mod 8,
+// each item's tiles consecutive. Persistent workgroups claim tiles from
+// their own XCD's queue only. Tile (s, m, r, c) waits for the row-block
+// future (s - 1, m, r) (all column tiles of that row block of the previous
+// stage written), so a row block flows to the next stage before the rest of
+// its microbatch is done.
+//
+// Producer and consumer of every activation block share an XCD, and with it
+// the L2, the coherence point of the XCD's CUs: a tile's plain stores are
+// complete (every wave waited for them) before the row-block counter add
+// that publishes them, and the consumer reads the block with loads that skip
+// its CU's L1 (sc0), after it saw the counter. No agent-scope release or
+// acquire is needed, each of which would write back or invalidate the XCD's
+// whole L2. (Each activation block is written once per launch and read only
+// after it is complete, and the L1s start the launch empty.)
 #include "device.h"
 #include "gemm.h"
 
@@ -27,17 +37,7 @@ namespace {
 __device__ __forceinline__ bool reached(uint32_t v, uint32_t target) { return (int32_t)(v - target) >= 0; }
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
-
-// Claim the next tile, blocking: queue q first, then the others in turn (one
-// atomic add per queue tried). Returns an index into the order table (and
-// leaves q at the queue it came from) or kNone once every queue is empty.
-__device__ __forceinline__ uint32_t claim_from(const PipeArgs& a, uint32_t& q) {
-  for (uint32_t n = 0; n < a.nq; ++n, q = (q + 1) % a.nq) {
-    const uint32_t k = __hip_atomic_fetch_add(&a.qctr[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (k < a.qlen[q]) return a.qstart[q] + k;
-  }
-  return kNone;
-}
+constexpr int kPastL1 = 1;  // sc0 in the cache-policy operand: the load is served by the L2, never a CU's L1
 
 __global__ void k_pipe_reset(PipeArgs a) {
   if (threadIdx.x < a.nq) a.qctr[threadIdx.x] = 0;
@@ -77,13 +77,13 @@ __device__ __forceinline__ mm::Tile tile_of(const PipeArgs& a, const PipeTile& p
   return tile;
 }
 
-// Thread 0: count tile p as done; the last tile of a row block completes it
-// (release: the tile's stores, completed by every wave before the barrier
-// that precedes this call, become visible first), the last row block of an
-// item fires the item's future.
+// Thread 0: count tile p as done; the last tile of a row block completes it,
+// the last row block of an item fires the item's future. Every wave waited
+// for its stores of the tile before the barrier that precedes this call, and
+// the consumers share this XCD's L2, so the add needs no release.
 __device__ __forceinline__ void publish(const PipeArgs& a, const PipeTile& p) {
   uint32_t* ctr = a.rb_ctr + ((uint64_t)p.s * a.M + p.m) * a.RB + p.r;
-  const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (reached(old + 1, a.rb_target)) {
     uint32_t* ic = a.item_ctr + (uint64_t)p.s * a.M + p.m;
     const uint32_t io = __hip_atomic_fetch_add(ic, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -97,11 +97,9 @@ __device__ __forceinline__ bool gate_open(const PipeArgs& a, const PipeTile& p) 
          reached(__hip_atomic_load(gate_of(a, p.s, p.m, p.r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), a.rb_target);
 }
 
-// Thread 0: is tile p's input row block complete (acquire)? With `block`,
-// wait for it, bounded by the spin limit (false once it expires). The gate is
-// polled with relaxed loads and acquired with one fence once open: an acquire
-// load per poll would invalidate the XCD's L2 each time, under the operand
-// streams of the other workgroups on it.
+// Thread 0: is tile p's input row block complete? With `block`, wait for it,
+// bounded by the spin limit (false once it expires). No acquire: the tile
+// reads its activation operand from this XCD's L2, past the L1.
 __device__ __forceinline__ bool input_ready(const PipeArgs& a, const PipeTile& p, bool block) {
   if (p.s == 0) return true;
   bool ok = gate_open(a, p);
@@ -115,7 +113,6 @@ __device__ __forceinline__ bool input_ready(const PipeArgs& a, const PipeTile& p
       return false;
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return true;
 }
 
@@ -126,21 +123,22 @@ struct Claims {
   uint32_t cand;   // start_blocking: the candidate after an expired wait
 };
 
-// Thread 0's claim pipeline. A claim is an atomic add on a queue counter
-// shared by the CUs of an XCD, a round trip of several microseconds; its
-// result is needed only a whole tile later. So take() hands out the ticket
-// claimed on the previous call and issues the next claim without waiting for
-// it (`raw` holds the counter value in flight, for queue q), falling back to
-// the other queues (blocking) once queue q is exhausted, and claiming ahead
-// on the queue that had work. Before the workgroup waits for an input,
-// resolve() turns the claim in flight into a held ticket, so that the wait
-// can take it too (see start_blocking); take() hands out a held ticket first.
+// Thread 0's claim pipeline. A claim is an atomic add on the counter of the
+// XCD's queue, a round trip of several microseconds; its result is needed
+// only a whole tile later. So take() hands out the ticket claimed on the
+// previous call and issues the next claim without waiting for it (`raw`
+// holds the counter value in flight); once the queue is exhausted the
+// workgroup is done (it never takes work from another XCD's queue: the
+// activations it would read sit in that XCD's L2). Before the workgroup
+// waits for an input, resolve() turns the claim in flight into a held
+// ticket, so that the wait can take it too (see start_blocking); take()
+// hands out a held ticket first.
 struct Claimer {
   uint32_t raw;   // value returned by the add in flight on queue q
-  uint32_t q;     // the queue being drained
+  uint32_t q;     // this XCD's queue
   uint32_t held;  // a claimed ticket not handed out yet, or kNone
   bool live;      // an add is in flight
-  bool done;      // every queue is empty
+  bool done;      // the queue is empty
   __device__ void issue(const PipeArgs& a) {
     raw = __hip_atomic_fetch_add(&a.qctr[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     live = true;
@@ -149,18 +147,12 @@ struct Claimer {
     if (held != kNone) {
       const uint32_t t = held;
       held = kNone;
-      if (!live && !done) issue(a);  // claim ahead again (if q is exhausted, the next take moves on)
+      if (!live && !done) issue(a);  // claim ahead again
       return t;
     }
     if (done) return kNone;
     if (!live) issue(a);  // nothing in flight (resolved into a ticket earlier): claim now
-    uint32_t t;
-    if (raw < a.qlen[q]) {
-      t = a.qstart[q] + raw;
-    } else {
-      q = (q + 1) % a.nq;
-      t = claim_from(a, q);  // blocking; leaves q at the queue that had work
-    }
+    const uint32_t t = raw < a.qlen[q] ? a.qstart[q] + raw : kNone;
     if (t == kNone) {
       done = true;
       live = false;
@@ -180,7 +172,7 @@ struct Claimer {
 // Thread 0: which of the tiles at tickets t, n and h (n, h may be kNone) has
 // its input complete first: 0, 1 or 2, or -1 once the spin limit expired
 // (latched as a timeout). The gates are polled with relaxed loads, all in
-// flight together, and acquired with one fence once one is open.
+// flight together (no acquire, as in input_ready).
 __device__ int await_any(const PipeArgs& a, uint32_t t, uint32_t n, uint32_t h) {
   const uint32_t* g[3] = {nullptr, nullptr, nullptr};
   const uint32_t tk[3] = {t, n, h};
@@ -201,10 +193,7 @@ __device__ int await_any(const PipeArgs& a, uint32_t t, uint32_t n, uint32_t h) 
 #pragma unroll
     for (int i = 2; i >= 0; --i)
       if (open0[i] || (g[i] && reached(v[i], a.rb_target))) which = i;  // the earliest held ticket wins ties
-    if (which >= 0) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      return which;
-    }
+    if (which >= 0) return which;
     if (wall_clock64() - t0 > a.f.spin_ticks) {
       latch(a.f, ST_TIMEOUT);
       return -1;
@@ -217,15 +206,13 @@ __device__ int await_any(const PipeArgs& a, uint32_t t, uint32_t n, uint32_t h) 
 // until one of the tiles the workgroup holds has its input complete and issue
 // its first stages. The workgroup holds at most three unstarted tickets: t,
 // cl.next, and the claim that was in flight, resolved into a ticket first;
-// the others stay held, t still the candidate. Waiting on all of them is what
-// guarantees progress, since a held ticket may come from another queue and
-// be an input of t. Let E be the earliest unfinished tile in the plan's
-// claim order (each queue is a subsequence of that order, and every tile's
-// inputs come earlier in it): E's input is complete; if a waiting workgroup
-// holds E, it polls E and starts it; if nobody holds E, E's queue is not
-// exhausted, and a workgroup claiming from that queue holds no unstarted
-// ticket of it (those would precede E) so it is not waiting, and claims E
-// when it has finished its tile. A tile whose wait expires (the spin limit) is
+// the others stay held, t still the candidate. Progress, per queue (a tile's
+// inputs are earlier tiles of its own queue): let E be the earliest
+// unfinished tile of a queue. E's input is complete; if a waiting workgroup
+// holds E, it polls E and starts it; if nobody holds E, E is not claimed
+// yet, every claimed ticket of the queue precedes it and is finished, so no
+// workgroup of the XCD is waiting, and one of them claims E when it has
+// finished its tile. A tile whose wait expires (the spin limit) is
 // published as done, so nothing downstream waits forever, and the next ticket
 // is taken. Returns false once the queues are empty.
 __device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl, Claimer& cr, uint32_t t,
@@ -255,7 +242,7 @@ __device__ bool start_blocking(const PipeArgs& a, unsigned char* lds, Claims& cl
     const uint32_t s = uniform(cl.start);
     if (s != kNone) {
       code = code_at(a, s);
-      mm::tile_start(tile_of(a, unpack(code)), lds);
+      mm::tile_start<kPastL1>(tile_of(a, unpack(code)), lds);
       return true;
     }
     t = uniform(cl.cand);
@@ -277,12 +264,11 @@ struct PublishPrev {
   }
 };
 
-// Persistent: one workgroup per CU loops over tiles. The plan puts all
-// tiles of an item in one XCD's queue (items dealt round-robin to the 8
-// queues in GPipe order), so the item's activation rows and weight columns
-// are shared through that XCD's L2. Each queue is in dependency order and a
-// workgroup leaves its own queue only once it is empty, so the earliest
-// unfinished tile is always held or next in line. (A tile, not a whole row
+// Persistent: one workgroup per CU loops over tiles of its XCD's queue (all
+// the items of the microbatches pinned to that XCD, in GPipe order), so an
+// item's activation rows and weight columns are shared through that XCD's
+// L2. Each queue is in dependency order, so the earliest unfinished tile of
+// each queue is always held or next in line. (A tile, not a whole row
 // block, is the unit of work: one GPipe tick holds at most S items, and only
 // at tile granularity do they outnumber the workgroups.)
 //
@@ -317,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
   uint32_t nxt_code = nxt != kNone ? code_at(a, nxt) : 0;
   while (have) {
     mm::f32x16 acc[4][4];
-    mm::tile_finish(tile_of(a, unpack(cur)), lds, acc, prev);  // may publish the previous tile; ends with a barrier
+    mm::tile_finish<kPastL1>(tile_of(a, unpack(cur)), lds, acc, prev);  // may publish the previous tile; ends with a barrier
     const uint32_t t2 = nxt, code2 = nxt_code;
     // every thread read cl.next and cl.ready before the barriers of the K loop
     if (tid == 0) {
@@ -337,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
     // of range and touch no memory, and the ring contents are discarded below
     // once every wave has waited for them. (code2 is a valid tile even when
     // there is no candidate.)
-    mm::tile_start_if(tile_of(a, unpack(code2)), lds, started);
+    mm::tile_start_if<kPastL1>(tile_of(a, unpack(code2)), lds, started);
     const PipeTile p = unpack(cur);
     __bf16* out = a.acts + ((uint64_t)p.s * a.M + p.m) * item_elems + (uint64_t)p.r * mm::BM * a.d +
                   (uint64_t)p.c * mm::BN;

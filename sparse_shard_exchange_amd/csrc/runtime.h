@@ -27,7 +27,7 @@ struct Layout {
   size_t tile_cnt = 0;    // [num_tiles][N] u32
   size_t tile_done = 0;   // [num_tiles] u32
   size_t rank = 0;        // [G] u16
-  size_t slab_cnt = 0;    // [grid][N] u32 (one-launch path)
+  size_t slab_cnt = 0;    // [grid][N] u64 (one-launch path): count | call << 32
   size_t small_tab = 0;   // [2][2N + 1] u32 (one-launch path counters, by call parity)
   size_t experts = 0, gates = 0, slot_of = 0, hidden_act = 0;  // MOE
   size_t rb_start = 0, b_done = 0;                              // MOE

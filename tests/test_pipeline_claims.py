@@ -6,27 +6,26 @@ GPipe-like schedule) and sections 4.4-4.5 (a computation starts once the
 futures of its inputs are ready): tile (s, m, r, c) of the pass may start only
 once every column tile of row block (s - 1, m, r) was published, and the pass
 must always finish. The kernel runs one persistent workgroup per CU; thread 0
-of each claims tiles from per-XCD queues (its own queue with one claim in
-flight, then the other queues on demand), publishes each finished tile from
-inside the next tile's K loop, and waits, bounded, when the next tile's input
-is not complete. This models thread 0 of every workgroup as a coroutine over
-shared counters (each step between two yields is atomic, as one atomic
-instruction is), with random tile, epilogue and poll times, and checks:
+of each claims tiles from the queue of its own XCD only (one claim in
+flight), publishes each finished tile from inside the next tile's K loop,
+and waits, bounded, when the next tile's input is not complete. Every stage
+of a microbatch is in one queue, so producer and consumer of each
+activation block share an XCD and its L2. This models thread 0 of every
+workgroup as a coroutine over shared counters (each step between two yields
+is atomic, as one atomic instruction is), with random tile, epilogue and
+poll times, and checks:
 
   * no wait ever reaches the spin limit (the kernel would latch a timeout
     and publish a tile it never ran);
   * every tile starts exactly once, after its input row block was complete,
     and is published exactly once;
-  * the order table is a bijection over the tiles and keeps every tile after
-    its inputs (the deal of the plan, re-derived here from its description).
+  * the order table is a bijection over the tiles, keeps every tile after
+    its inputs and puts every tile in the queue of its inputs (the deal of
+    the plan, re-derived here from its description).
 
-The kernel's rules: a claim is always in flight a tile ahead (on the own
-queue, then on whichever queue had work); before waiting for an input, the
-workgroup turns that claim into a held ticket and then waits for whichever
-of its (at most three) held tickets becomes ready first. The rules before
-the fix (the same claims ahead, but waiting on the candidate alone) are
-simulated too: they can leave a workgroup waiting for a tile it holds
-itself.
+The kernel's rules: a claim is always in flight a tile ahead; before waiting
+for an input, the workgroup turns that claim into a held ticket and then
+waits for whichever of its (at most three) held tickets becomes ready first.
 """
 import heapq
 import random
@@ -37,7 +36,7 @@ import pytest
 def deal(S, M, RB, CT, nq, windows):
     """The plan's claim order: items in GPipe lock-step order (tick s + m,
     then stage) or, with stage windows, stage by stage within windows of 16
-    microbatches, dealt round robin to nq queues, each item's tiles together."""
+    microbatches, item (s, m) in queue m mod nq, each item's tiles together."""
     queues = [[] for _ in range(nq)]
     items = []
     if windows:
@@ -50,8 +49,8 @@ def deal(S, M, RB, CT, nq, windows):
             for s in range(S):
                 if 0 <= t - s < M:
                     items.append((s, t - s))
-    for i, (s, m) in enumerate(items):
-        queues[i % nq].extend((s, m, r, c) for r in range(RB) for c in range(CT))
+    for s, m in items:
+        queues[m % nq].extend((s, m, r, c) for r in range(RB) for c in range(CT))
     order, head, length = [], [], []
     for q in queues:
         head.append(len(order))
@@ -61,8 +60,7 @@ def deal(S, M, RB, CT, nq, windows):
 
 
 class Sim:
-    def __init__(self, S, M, RB, CT, nwg, windows, seed, legacy=False, spin_limit=400.0, tile=(0.8, 1.2),
-                 start=(0.0, 0.3)):
+    def __init__(self, S, M, RB, CT, nwg, windows, seed, spin_limit=400.0, tile=(0.8, 1.2), start=(0.0, 0.3)):
         self.S, self.M, self.RB, self.CT = S, M, RB, CT
         self.nq = min(8, nwg)
         self.order, self.qstart, self.qlen, self.items = deal(S, M, RB, CT, self.nq, windows)
@@ -73,7 +71,6 @@ class Sim:
         self.expired = 0
         self.rng = random.Random(seed)
         self.nwg = nwg
-        self.legacy = legacy
         self.spin_limit = spin_limit
         self.now = 0.0
         self.tile_time, self.start_time = tile, start
@@ -105,14 +102,6 @@ class Sim:
             st["raw"] = sim.claim(st["q"])
             st["live"] = True
 
-        def claim_from():
-            for _ in range(nq):
-                k = sim.claim(st["q"])
-                if k < sim.qlen[st["q"]]:
-                    return sim.qstart[st["q"]] + k
-                st["q"] = (st["q"] + 1) % nq
-            return None
-
         def take():
             if st["held"] is not None:
                 t, st["held"] = st["held"], None
@@ -123,11 +112,7 @@ class Sim:
                 return None
             if not st["live"]:
                 issue()
-            if st["raw"] < sim.qlen[st["q"]]:
-                t = sim.qstart[st["q"]] + st["raw"]
-            else:
-                st["q"] = (st["q"] + 1) % nq
-                t = claim_from()
+            t = sim.qstart[st["q"]] + st["raw"] if st["raw"] < sim.qlen[st["q"]] else None
             if t is None:
                 st["done"], st["live"] = True, False
             else:
@@ -147,10 +132,9 @@ class Sim:
 
         def start_blocking(t):
             while t is not None:
-                if not sim.legacy:
-                    resolve()
+                resolve()
                 n, h = st["next"], st["held"]
-                cands = [t] if sim.legacy else [t, n, h]
+                cands = [t, n, h]
                 t0 = sim.now
                 which = -1
                 while sim.now - t0 <= sim.spin_limit:
@@ -246,6 +230,16 @@ def test_order_table_keeps_inputs_first(windows):
             assert pos[(s - 1, m)] < pos[(s, m)]
         if m:
             assert pos[(s, m - 1)] < pos[(s, m)]  # each stage takes its microbatches in order
+    # every tile sits in the queue (the XCD) of the row blocks it reads, after them
+    where = {}
+    for q in range(8):
+        for k, tile in enumerate(order[head[q]:head[q] + length[q]]):
+            where[tile] = (q, k)
+    for (s, m, r, c), (q, k) in where.items():
+        for c2 in range(4):
+            if s:
+                assert where[(s - 1, m, r, c2)][0] == q and where[(s - 1, m, r, c2)][1] < k
+    assert len(set(length)) == 1  # 64 microbatches over 8 XCDs: equal work per XCD
 
 
 @pytest.mark.parametrize("S,M,RB,CT,nwg", [(3, 5, 2, 2, 4), (4, 9, 1, 4, 16), (5, 20, 3, 1, 12), (8, 16, 2, 2, 32)])
@@ -260,19 +254,3 @@ def test_claim_protocol_always_finishes(S, M, RB, CT, nwg, windows, seed):
 def test_claim_protocol_full_pass(windows):
     """The 16-stage, 64-microbatch pass of 2048 x 1024 microbatches on 256 workgroups."""
     check_complete(Sim(16, 64, 8, 4, 256, windows, 7, tile=(0.3, 3.0), start=(0.0, 8.0)).run())
-
-
-@pytest.mark.parametrize("S,M,RB,CT,nwg", [(8, 16, 2, 2, 32)])
-def test_old_claim_rules_could_wait_on_a_held_tile(S, M, RB, CT, nwg):
-    """Before the fix a workgroup waited on its candidate alone while it could
-    hold, claimed ahead from another queue, a tile that the candidate needed.
-    With tile times spread over 0.3-3 units and start times over 8, some of
-    20 random schedules reach the spin limit under the old rules; none does
-    under the new ones on the same schedules."""
-    hits = 0
-    for seed in range(20):
-        kw = dict(tile=(0.3, 3.0), start=(0.0, 8.0))
-        old = Sim(S, M, RB, CT, nwg, False, seed, legacy=True, **kw).run()
-        hits += old.expired > 0
-        check_complete(Sim(S, M, RB, CT, nwg, False, seed, **kw).run())
-    assert hits > 0
