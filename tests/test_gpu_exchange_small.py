@@ -96,6 +96,31 @@ def test_one_launch_equals_split_launches_and_oracle(gpu, n, t, p, kind):
         assert np.all(st[pw.PW_NODE_B, :n] <= st[pw.PW_NODE_RESULT, 0])
 
 
+def test_one_launch_new_inputs_every_call(gpu):
+    """Back-to-back calls with different payloads and routings into the same
+    output buffers: every call's rows, indices and row sums must be its own
+    (the slab table is reused across calls, told apart by the call tag, and B
+    reads rows written by other workgroups of the same launch; a stale read
+    from an earlier call would show here, not with repeated inputs)."""
+    pw = gpu
+    n, t, p = 8, 4096, 64
+    aff, rs = pw.op(pw.PW_OP_AFFINE, 2.0, 1.0), pw.op(pw.PW_OP_ROWSUM)
+    one, split = _pair(pw, n, t, p, aff, rs)
+    for k, kind in enumerate(("uniform", "zipf4", "reversed", "half_empty", "uniform")):
+        print(f"one-launch call {k}: {kind}", flush=True)
+        x = torch.from_numpy(pw_inputs.exchange_uniform(n, t, p, variant=100 + k).x).cuda()
+        dest = _dest(kind, n, t, seed=k)
+        dd = torch.from_numpy(dest).cuda()
+        pw.future_wait(one.step(x, dd), 30_000_000_000)
+        pw.future_wait(split.step(x, dd), 30_000_000_000)
+        for name in ("dst", "src_index", "counts", "offsets", "b_out"):
+            assert _same(getattr(one, name), getattr(split, name)), (k, name)
+        ref = ox.exchange_step(x.cpu().numpy(), dest, n, n, a_op=ox.op_affine(2.0, 1.0))
+        rows = int(ref.offsets[-1])
+        assert np.array_equal(one.src_index.cpu().numpy()[:rows], ref.src_index.astype(np.int32))
+        assert np.array_equal(one.dst.cpu().numpy().view(np.uint32)[:rows], ref.y.view(np.uint32))
+
+
 def test_one_launch_b_overlaps_the_exchange(gpu):
     """32 destinations fed by disjoint source shards (identity routing): each
     segment completes when its own 8 slabs have arrived, and B of a segment

@@ -117,6 +117,34 @@ def test_pipeline_repeat_is_deterministic(gpu):
     assert np.all(fi[pw.PW_NODE_STAGE, :6] == 2) and fi[pw.PW_NODE_RESULT, 0] == 2
 
 
+def test_pipeline_new_input_each_pass(gpu):
+    """Passes on different inputs into the same activation buffer: the last
+    pass must equal a fresh plan's single pass on its input, bit for bit
+    (each activation block is handed from producer to consumer inside one
+    launch; a stale read of an earlier pass's block would show here, not
+    with repeated inputs)."""
+    pw = gpu
+    s, m, rows, d = 4, 16, 512, 512
+    inp = pw_inputs.pipeline(s, m, rows, d)
+    w = inp.w.cuda()
+    pipe = pw.Pipeline(w, m, rows)
+    acts = torch.empty((s, m, rows, d), dtype=torch.bfloat16, device="cuda")
+    xs = [inp.x.cuda(), (inp.x.float() * -0.5).to(torch.bfloat16).cuda(), inp.x.flip(0).cuda()]
+    for k, x in enumerate(xs):
+        print(f"pipeline pass {k}", flush=True)
+        pw.future_wait(pipe.run(x, acts), 60_000_000_000)
+    fresh = pw.Pipeline(w, m, rows)
+    ref = torch.empty_like(acts)
+    pw.future_wait(fresh.run(xs[-1], ref), 60_000_000_000)
+    assert torch.equal(acts.view(torch.int16), ref.view(torch.int16))
+    wn = inp.w.float().numpy()
+    x_last = xs[-1].float().cpu().numpy()
+    for mb in (0, m - 1):
+        got = acts[:, mb].float().cpu().numpy()
+        for stg in range(s):
+            check_conditional(x_last[mb] if stg == 0 else got[stg - 1], wn[stg], got[stg], (stg, mb))
+
+
 def test_pipeline_full_size(gpu):
     """16 stages x 64 microbatches x 2048 x 1024, the configuration the bench
     times: every row of microbatches 0, 31 and 63 through all 16 stages against
