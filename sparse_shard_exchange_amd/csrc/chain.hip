@@ -64,7 +64,7 @@ __device__ __forceinline__ bool await_local(const Futures& f, uint32_t node, uin
 __device__ __forceinline__ void finish_shard(const ChainArgs& a, uint32_t sub) {
   if (sub == 0) {
     const uint32_t old = __hip_atomic_fetch_add(a.done_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == a.done_target) fire(a.f, NODE_RESULT, 0, a.epoch0 + a.steps, false);
+    if (old + 1 == a.done_target) fire(a.f, NODE_RESULT, 0, a.epoch0 + a.steps);
   }
 }
 
@@ -288,11 +288,11 @@ __global__ __launch_bounds__(256) void k_chain_node(ChainArgs a) {
   if (a.node == NODE_A) {
     if (!await_local(a.f, NODE_B, i, k - 1, lane)) return;
     node_body(st, ab, a.E, lane, a.a_kind, a.a_a, a.a_b);
-    if (lane == 0) fire(a.f, NODE_A, i, k, false);
+    if (lane == 0) fire(a.f, NODE_A, i, k);
   } else {
     if (!await_local(a.f, NODE_A, i, k, lane)) return;
     node_body(ab, st, a.E, lane, a.b_kind, a.b_a, a.b_b);
-    if (lane == 0) fire(a.f, NODE_B, i, k, false);
+    if (lane == 0) fire(a.f, NODE_B, i, k);
     if (a.done_ctr) finish_shard(a, lane);
   }
 }
@@ -315,8 +315,8 @@ __global__ __launch_bounds__(256) void k_chain_fused(ChainArgs a) {
     st[e] = x;
   }
   if (lane == 0) {
-    fire(a.f, NODE_A, i, a.epoch0 + a.steps, false);
-    fire(a.f, NODE_B, i, a.epoch0 + a.steps, false);
+    fire(a.f, NODE_A, i, a.epoch0 + a.steps);
+    fire(a.f, NODE_B, i, a.epoch0 + a.steps);
   }
   finish_shard(a, lane);
 }
@@ -330,23 +330,19 @@ __global__ __launch_bounds__(256) void k_chain_fused(ChainArgs a) {
 // counts above 1536 pack them; four per wave were slower (~480-500).
 static uint32_t chain_pack(uint32_t N, uint32_t E) { return E == 128 && N > 1536 ? 2 : 1; }
 
-// Shards per wave of the split placement: one below 256 shards, more above
-// (128-element shards only), so that a step's releases stay few.
-static uint32_t split_pack(uint32_t N, uint32_t E) {
-  if (E != 128) return 1;
-  return N <= 128 ? 1 : N <= 512 ? 2 : N <= 1024 ? 4 : 8;
-}
+// Shards per wave of the split placement: one up to 128 shards, two above
+// (128-element shards only). A wave goes on once the inputs of all its
+// shards have fired, so it waits for the slowest of their producers: per
+// gated node at 256 / 512 / 1024 / 2048 shards, one shard per wave 1.55 /
+// 1.67 / 1.98 / 2.17 us, two 1.50 / 1.52 / 1.61 / 1.75, four 2.13 / 2.15 /
+// 2.17 / 2.20, eight 4.17 / 4.25 / 4.26 / 4.22.
+static uint32_t split_pack(uint32_t N, uint32_t E) { return E == 128 && N > 128 ? 2 : 1; }
 
 // Workgroups of the split-placement kernel: one wave per (role, group of shards).
 static uint32_t split_grid(uint32_t N, uint32_t g) { return (2 * ((N + g - 1) / g) + 3) / 4; }
 
 static const void* split_kernel(uint32_t g) {
-  switch (g) {
-    case 8: return (const void*)k_chain_split<8>;
-    case 4: return (const void*)k_chain_split<4>;
-    case 2: return (const void*)k_chain_split<2>;
-    default: return (const void*)k_chain_split<1>;
-  }
+  return g == 2 ? (const void*)k_chain_split<2> : (const void*)k_chain_split<1>;
 }
 
 bool chain_split_fits(int device, uint32_t N, uint32_t E) {
@@ -365,11 +361,7 @@ hipError_t launch_chain(const ChainArgs& a, uint32_t mode, hipStream_t s) {
     if (e != hipSuccess) return e;
     const uint32_t g = split_pack(a.N, a.E);
     const dim3 sgrid(split_grid(a.N, g));
-    if (g == 8)
-      hipLaunchKernelGGL(k_chain_split<8>, sgrid, block, 0, s, a);
-    else if (g == 4)
-      hipLaunchKernelGGL(k_chain_split<4>, sgrid, block, 0, s, a);
-    else if (g == 2)
+    if (g == 2)
       hipLaunchKernelGGL(k_chain_split<2>, sgrid, block, 0, s, a);
     else
       hipLaunchKernelGGL(k_chain_split<1>, sgrid, block, 0, s, a);

@@ -36,47 +36,22 @@ __device__ __forceinline__ void latch(const Futures& f, uint32_t code) {
                                        __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Fire future (node, shard) for `epoch`. The epoch is stored at system scope,
-// so that a host thread polling the future table sees it while the launch
-// still runs. `release` first orders every earlier write of this thread (and,
-// after a workgroup barrier that followed a wait for the workgroup's stores,
-// of its workgroup) before the store, for consumers in the same launch;
-// without it, visibility to device consumers comes from the end of the kernel
-// (consumers in a later launch).
-__device__ __forceinline__ void fire(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch,
-                                     bool release) {
+// Fire future (node, shard) for `epoch`: the fire-count add, then the epoch
+// stored at system scope, so that a host thread polling the future table
+// sees it while the launch still runs. Orders nothing before it: consumers in
+// the same launch read the producer's data with agent-coherent loads (the
+// producer wrote it with agent-coherent stores and waited for them) or share
+// its XCD (the pipeline); consumers in a later launch are ordered by the kernel
+// boundary.
+__device__ __forceinline__ void fire(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
   const uint32_t i = node * f.width + shard;
   if (f.stamps) f.stamps[i] = wall_clock64();
   __hip_atomic_fetch_add(&f.fires[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (release) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __hip_atomic_store(&f.epoch[i], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 __device__ __forceinline__ bool epoch_reached(uint32_t v, uint32_t epoch) {
   return (int32_t)(v - epoch) >= 0;
-}
-
-// Wait (acquire) until future (node, shard) fired for `epoch` or later. The
-// word is polled with relaxed agent-scope loads and the acquire is one fence
-// once it is seen: an acquire load in the loop would invalidate the XCD's L2
-// at every poll, under the feet of every other workgroup on it. The wait is
-// bounded by f.spin_ticks of the 100 MHz wall clock; on expiry it latches
-// ST_TIMEOUT and returns false so the caller skips its work and the wave
-// still exits.
-__device__ __forceinline__ bool await(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
-  const uint32_t* p = &f.epoch[node * f.width + shard];
-  bool ok = epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
-  const uint64_t t0 = ok ? 0 : wall_clock64();
-  while (!ok) {
-    __builtin_amdgcn_s_sleep(1);
-    ok = epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
-    if (!ok && wall_clock64() - t0 > f.spin_ticks) {
-      latch(f, ST_TIMEOUT);
-      return false;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return true;
 }
 
 // Wait on a future fired by an EARLIER launch on the same stream: the kernel
@@ -85,7 +60,7 @@ __device__ __forceinline__ bool await(const Futures& f, uint32_t node, uint32_t 
 // hot future words, one or two per token in the MoE combine, would all go to
 // memory); only if that finds the epoch missing (the producer failed) does
 // the bounded spin with relaxed agent-scope loads follow. Same bound and
-// latch as await().
+// latch as await_coherent().
 __device__ __forceinline__ bool await_prior(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
   const uint32_t* p = &f.epoch[node * f.width + shard];
   if (epoch_reached(*p, epoch)) return true;
@@ -125,8 +100,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, uint
 // compiler barrier as well.
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// await() for consumers whose reads of the producer's data are coherent
-// loads: the same bounded poll, without the acquire fence.
+// Wait until future (node, shard) fired for `epoch` or later, for consumers
+// in the same launch whose reads of the producer's data are agent-coherent
+// loads (so no acquire fence: one would invalidate the XCD's whole L2). The
+// word is polled with relaxed agent-scope loads, bounded by f.spin_ticks of
+// the 100 MHz wall clock; on expiry it latches ST_TIMEOUT and returns false
+// so the caller skips its work and the wave still exits.
 __device__ __forceinline__ bool await_coherent(const Futures& f, uint32_t node, uint32_t shard, uint32_t epoch) {
   const uint32_t* p = &f.epoch[node * f.width + shard];
   bool ok = epoch_reached(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);

@@ -90,18 +90,26 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
 // ------------------------------------------------------------ scan helpers
 // Exclusive running sum, in place, of the column d of rows [r0, r1) of a
 // row-major [rows][N] table; returns the column total. The loads of 16 rows
-// are issued before any is needed.
+// are issued before any is needed (unconditionally: rows past r1 re-read row
+// r1 - 1 and count zero). kCoherent: the rows were written by other
+// workgroups of the same launch, read with agent-coherent loads.
+template <bool kCoherent = false>
 __device__ __forceinline__ uint32_t column_scan(uint32_t* t, uint32_t N, uint32_t d, uint32_t r0, uint32_t r1) {
   constexpr uint32_t kB = 16;
   uint32_t run = 0;
   for (uint32_t r = r0; r < r1; r += kB) {
     uint32_t v[kB];
 #pragma unroll
-    for (uint32_t u = 0; u < kB; ++u) v[u] = r + u < r1 ? t[(uint64_t)(r + u) * N + d] : 0u;
+    for (uint32_t u = 0; u < kB; ++u) {
+      uint32_t* e = &t[(uint64_t)min(r + u, r1 - 1) * N + d];
+      v[u] = kCoherent ? __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *e;
+    }
 #pragma unroll
     for (uint32_t u = 0; u < kB; ++u) {
-      if (r + u < r1) t[(uint64_t)(r + u) * N + d] = run;
-      run += v[u];
+      if (r + u < r1) {
+        t[(uint64_t)(r + u) * N + d] = run;
+        run += v[u];
+      }
     }
   }
   return run;
@@ -115,15 +123,17 @@ struct ScanShared {
 };
 
 // True in the last workgroup of the grid to get here (counter ctl[1], reset
-// by scan_finish); its writes before the call are then visible to that one.
+// by scan_finish). What that workgroup reads of the others' writes is
+// written with agent-coherent stores, complete (every wave waits for its
+// stores here) before the workgroup's count, and read with agent-coherent
+// loads: no release or acquire fence, each of which would write back or
+// invalidate the XCD's whole L2.
 __device__ __forceinline__ bool last_to_arrive(const ExchangeArgs& a, ScanShared& sh) {
-  __threadfence();
+  wait_vmem_all();
   __syncthreads();
   if (threadIdx.x == 0) sh.is_last = atomicAdd(&a.ctl[1], 1u) == gridDim.x - 1;
   __syncthreads();
-  if (!sh.is_last) return false;
-  __threadfence();
-  return true;
+  return sh.is_last;
 }
 
 // The scan's last step, in one workgroup, once expected[d] (the tuples d
@@ -149,8 +159,8 @@ __device__ __forceinline__ void scan_finish(const ExchangeArgs& a, ScanShared& s
     a.arrived[d] = 0;
     a.b_arrived[d] = 0;
     if (e == 0) {  // nothing will arrive: the input of B[d] is complete now
-      fire(a.f, NODE_EXCH, d, a.epoch, false);
-      fire(a.f, NODE_B, d, a.epoch, false);
+      fire(a.f, NODE_EXCH, d, a.epoch);
+      fire(a.f, NODE_B, d, a.epoch);
       ++zeros;
     }
   }
@@ -169,7 +179,7 @@ __device__ __forceinline__ void scan_finish(const ExchangeArgs& a, ScanShared& s
     for (uint32_t i = 0; i < kWaves; ++i) zt += sh.zero_count[i];
     __hip_atomic_store(&a.ctl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
     __hip_atomic_store(&a.ctl[0], zt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // B futures fired
-    if (zt == N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+    if (zt == N) fire(a.f, NODE_RESULT, 0, a.epoch);
   }
 }
 
@@ -310,7 +320,8 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
       wrun[ww * N + d] = run;
       run += c;
     }
-    a.tile_base[(uint64_t)blockIdx.x * N + d] = run;
+    // coherent: with a fused scan the last workgroup reads it (below)
+    __hip_atomic_store(&a.tile_base[(uint64_t)blockIdx.x * N + d], run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.tile_cnt[(uint64_t)blockIdx.x * N + d] = run;
   }
   if (threadIdx.x == 0) a.tile_done[blockIdx.x] = 0;
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
   if (!last_to_arrive(a, sh)) return;
   uint32_t* exp_lds = wrun;
   for (uint32_t d = threadIdx.x; d < N; d += kBlock) {
-    const uint32_t total = column_scan(a.tile_base, N, d, 0, a.num_tiles);
+    const uint32_t total = column_scan<true>(a.tile_base, N, d, 0, a.num_tiles);
     const uint32_t e = a.capacity ? min(total, a.capacity) : total;  // the tuples d keeps
     a.expected[d] = e;
     a.blk_base[d] = 0;  // the one scan block starts every run at 0 (the scatter adds this row)
@@ -385,11 +396,12 @@ __global__ __launch_bounds__(kBlock) void k_scan(ExchangeArgs a) {
   {
     const uint32_t t0 = blockIdx.x * a.scan_tiles, t1 = min(a.num_tiles, t0 + a.scan_tiles);
     for (uint32_t d = threadIdx.x; d < a.N; d += kBlock)
-      a.blk_base[(uint64_t)blockIdx.x * a.N + d] = column_scan(a.tile_base, a.N, d, t0, t1);
+      __hip_atomic_store(&a.blk_base[(uint64_t)blockIdx.x * a.N + d], column_scan(a.tile_base, a.N, d, t0, t1),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (!last_to_arrive(a, sh)) return;
   for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) {
-    const uint32_t total = column_scan(a.blk_base, a.N, d, 0, a.num_blk);
+    const uint32_t total = column_scan<true>(a.blk_base, a.N, d, 0, a.num_blk);
     a.expected[d] = a.capacity ? min(total, a.capacity) : total;  // the tuples d keeps
   }
   __syncthreads();
@@ -442,7 +454,9 @@ __global__ __launch_bounds__(kBlock) void k_scan_top(ExchangeArgs a) {
     if (live && r < per && b0 + r < B) a.blk_base[(uint64_t)(b0 + r) * N + d] = run;
     run += v[r];
   }
-  if (live && p == 0) a.expected[d] = a.capacity ? min(tot, a.capacity) : tot;  // the tuples d keeps
+  if (live && p == 0)  // the tuples d keeps; the last workgroup reads them (coherent)
+    __hip_atomic_store(&a.expected[d], a.capacity ? min(tot, a.capacity) : tot, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   if (!last_to_arrive(a, sh)) return;
   scan_finish(a, sh, [&](uint32_t dd) {
     return __hip_atomic_load(&a.expected[dd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -597,11 +611,11 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
     if (n == 0) continue;
     const uint32_t old = __hip_atomic_fetch_add(&a.arrived[d], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + n == a.expected[d]) {
-      fire(a.f, NODE_EXCH, d, a.epoch, false);
+      fire(a.f, NODE_EXCH, d, a.epoch);
       if (!a.b_gated) {  // B has no work of its own: it completes with its input
-        fire(a.f, NODE_B, d, a.epoch, false);
+        fire(a.f, NODE_B, d, a.epoch);
         const uint32_t r = __hip_atomic_fetch_add(&a.ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (r + 1 == N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+        if (r + 1 == N) fire(a.f, NODE_RESULT, 0, a.epoch);
       }
     }
   }
@@ -692,9 +706,9 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
     const uint32_t n = (uint32_t)(hi - lo), want = (uint32_t)(over_hi[threadIdx.x] - over_lo[threadIdx.x]);
     const uint32_t old = __hip_atomic_fetch_add(&a.b_arrived[d], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + n == want) {
-      fire(a.f, NODE_B, d, a.epoch, false);
+      fire(a.f, NODE_B, d, a.epoch);
       const uint32_t r = __hip_atomic_fetch_add(&a.ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (r + 1 == a.N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+      if (r + 1 == a.N) fire(a.f, NODE_RESULT, 0, a.epoch);
     }
   }
 }

@@ -286,10 +286,10 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
     }
     if (tid < N) a.expected[tid] = sh.tot[tid];
     if (tid < N && sh.tot[tid] == 0) {  // nothing will arrive: its input (and B, which has no rows) is complete
-      fire(a.f, NODE_EXCH, tid, a.epoch, false);
-      fire(a.f, NODE_B, tid, a.epoch, false);
+      fire(a.f, NODE_EXCH, tid, a.epoch);
+      fire(a.f, NODE_B, tid, a.epoch);
       const uint32_t r = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (r + 1 == N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+      if (r + 1 == N) fire(a.f, NODE_RESULT, 0, a.epoch);
     }
   }
   for (uint32_t t = tid; t < nt; t += kBlock) {
@@ -333,11 +333,11 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
     const uint32_t n = sh.mine[tid];
     const uint32_t old = __hip_atomic_fetch_add(&arrived[tid], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + n == sh.tot[tid]) {
-      fire(a.f, NODE_EXCH, tid, a.epoch, false);
+      fire(a.f, NODE_EXCH, tid, a.epoch);
       if (!a.b_gated) {  // B has no work of its own: it completes with its input
-        fire(a.f, NODE_B, tid, a.epoch, false);
+        fire(a.f, NODE_B, tid, a.epoch);
         const uint32_t r = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (r + 1 == N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+        if (r + 1 == N) fire(a.f, NODE_RESULT, 0, a.epoch);
       }
     }
   }
@@ -370,9 +370,9 @@ __global__ __launch_bounds__(kBlock) void k_exchange_small(ExchangeArgs a) {
     const uint32_t n = (uint32_t)(hi - lo);
     const uint32_t old = __hip_atomic_fetch_add(&b_arrived[tid], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + n == sh.tot[tid]) {
-      fire(a.f, NODE_B, tid, a.epoch, false);
+      fire(a.f, NODE_B, tid, a.epoch);
       const uint32_t r = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (r + 1 == N) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+      if (r + 1 == N) fire(a.f, NODE_RESULT, 0, a.epoch);
     }
   }
 }

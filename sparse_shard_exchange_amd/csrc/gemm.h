@@ -423,8 +423,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], __bf16* ou
 }
 
 // Every wave's global stores have completed (vmcnt = 0) before the caller's
-// barrier, so one thread's agent-scope release afterwards covers the
-// workgroup's output.
+// barrier, so that one thread's publish afterwards covers the workgroup's
+// output.
 __device__ __forceinline__ void wait_stores() { wait_vmem<0>(); }
 
 }  // namespace mm

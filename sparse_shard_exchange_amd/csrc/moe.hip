@@ -269,7 +269,7 @@ struct CountTile {
   __device__ void operator()() {
     if (pending && threadIdx.x == 0) {
       const uint32_t old = __hip_atomic_fetch_add(&a->b_done[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old + 1 == tiles_e) fire(a->f, NODE_B, e, a->epoch, false);
+      if (old + 1 == tiles_e) fire(a->f, NODE_B, e, a->epoch);
     }
     pending = false;
   }
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256) void k_combine(MoeArgs a) {
   __syncthreads();
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&a.ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == gridDim.x) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+    if (old + 1 == gridDim.x) fire(a.f, NODE_RESULT, 0, a.epoch);
   }
 }
 

@@ -87,7 +87,7 @@ __device__ __forceinline__ void publish(const PipeArgs& a, const PipeTile& p) {
   if (reached(old + 1, a.rb_target)) {
     uint32_t* ic = a.item_ctr + (uint64_t)p.s * a.M + p.m;
     const uint32_t io = __hip_atomic_fetch_add(ic, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (reached(io + 1, a.item_target)) fire(a.f, NODE_STAGE, p.s * a.M + p.m, a.epoch, false);
+    if (reached(io + 1, a.item_target)) fire(a.f, NODE_STAGE, p.s * a.M + p.m, a.epoch);
   }
 }
 
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void k_pipeline(PipeArgs a) {
   }
   if (tid == 0) {
     const uint32_t dn = __hip_atomic_fetch_add(a.done_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (reached(dn + 1, a.done_target)) fire(a.f, NODE_RESULT, 0, a.epoch, false);
+    if (reached(dn + 1, a.done_target)) fire(a.f, NODE_RESULT, 0, a.epoch);
   }
 }
 
