@@ -375,6 +375,19 @@ def pipeline_bench(pw, torch, pw_inputs, passes=3):
     out.update(timed(0))
     out["stage_windows"] = timed(pw.PW_FLAG_STAGE_WINDOWS)
     out.update({"flop_per_pass": flops, "gpipe_bubble_lockstep": (s - 1) / (m + s - 1)})
+    # the same GEMM + GELU as one stage over the 64 microbatches (no GPipe
+    # dependencies): the shape of the vendor reference's pipeline_stage_gemm_gelu
+    one = pw.Pipeline(w[:1].contiguous(), m, rows, flags=pw.PW_FLAG_TIMING)
+    acts1 = torch.empty((1, m, rows, d), dtype=torch.bfloat16, device="cuda")
+    pw.future_wait(one.run(x, acts1), 60_000_000_000)
+    one.plan.reset_times()
+    for _ in range(5):
+        f = one.run(x, acts1)
+    pw.future_wait(f, 60_000_000_000)
+    kt = one.plan.kernel_times()
+    kms = kt["pipeline"][1] / kt["pipeline"][0]
+    out["single_stage"] = {"shape": f"{m} x [{rows}x{d}] @ [{d}x{d}] with GELU, one launch", "kernel_ms": kms,
+                           "tflops": flops / s / (kms * 1e-3) / 1e12}
     return out
 
 
