@@ -250,7 +250,9 @@ int pw_plan_destroy(pw_plan_t plan);
  * k expert rows back and sums them weighted by the gates into `result`.
  *
  * Stream ordered; *done receives the Result future. Argument errors return
- * PW_ERR_INVALID before anything is enqueued.
+ * PW_ERR_INVALID before anything is enqueued. The calls of one plan share its
+ * workspace (tables, counters, futures): issue them on one stream or order
+ * them across streams; calls of one plan that overlap on the device race.
  */
 int pw_exchange(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done);
 
@@ -315,7 +317,10 @@ int pw_exchange_scratch(const pw_plan_desc* d, const pw_exchange_io* io, void* s
  * `aux` must be 16-byte aligned (else PW_ERR_INVALID).
  * PIPELINE: steps must be 1. `state` holds the M microbatches [M][rows][d]
  * bf16; `aux` (device, required) receives every stage output [S][M][rows][d]
- * bf16. Item (s, m) runs after (s-1, m) fired its future and after (s, m-1).
+ * bf16. Item (s, m) (stage s of microbatch m) reads the output of (s-1, m)
+ * only once that row block's future fired; items of one stage start in
+ * ascending m on each XCD (microbatch m runs on XCD m mod 8), and items of
+ * different XCDs run concurrently.
  *
  * *done receives the future of the last Result.
  */
