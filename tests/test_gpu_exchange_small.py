@@ -76,7 +76,7 @@ def test_one_launch_equals_split_launches_and_oracle(gpu, n, t, p, kind):
     assert set(probe.plan.kernel_times()) == {"exchange_small"}  # the step is one launch
     for a_op, b_op in ((aff, rs), (None, None), (aff, pw.op(pw.PW_OP_AFFINE, 0.5, 0.0))):
         one, split = _pair(pw, n, t, p, a_op, b_op, flags=pw.PW_FLAG_TRACE)
-        for _ in range(3):  # repeated calls: the cumulative publish counter stays aligned
+        for _ in range(3):  # repeated calls: the call-tagged slab table and the counter sets by call parity
             f1 = one.step(x, dd)
             f2 = split.step(x, dd)
         pw.future_wait(f1, 30_000_000_000)
