@@ -253,6 +253,10 @@ int pw_plan_destroy(pw_plan_t plan);
  * PW_ERR_INVALID before anything is enqueued. The calls of one plan share its
  * workspace (tables, counters, futures): issue them on one stream or order
  * them across streams; calls of one plan that overlap on the device race.
+ * A call's epoch (and, one-launch, its slab-table tag) is fixed when the call
+ * is made, so a captured call must not be replayed as a HIP graph: a replay
+ * would reuse them (and the one-launch path could accept a previous call's
+ * table entries).
  */
 int pw_exchange(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done);
 
