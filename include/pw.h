@@ -254,9 +254,9 @@ int pw_plan_destroy(pw_plan_t plan);
  * workspace (tables, counters, futures): issue them on one stream or order
  * them across streams; calls of one plan that overlap on the device race.
  * A call's epoch (and, one-launch, its slab-table tag) is fixed when the call
- * is made, so a captured call must not be replayed as a HIP graph: a replay
- * would reuse them (and the one-launch path could accept a previous call's
- * table entries).
+ * is made, and a graph replay would reuse them: on a stream under HIP graph
+ * capture every call of a plan returns PW_ERR_UNSUPPORTED before enqueueing
+ * anything (pw_exchange_scratch is the capturable form of the step).
  */
 int pw_exchange(pw_plan_t plan, const pw_exchange_io* io, void* stream, pw_future_t* done);
 

@@ -278,7 +278,13 @@ int Plan::begin_call(hipStream_t s) {
   int cur = -1;
   (void)hipGetDevice(&cur);
   if (cur != device) return fail(PW_ERR_STATE, "plan built on device %d, current device is %d", device, cur);
-  (void)s;
+  // A call's epoch (and the one-launch table tag) is fixed here, on the host:
+  // a graph replay would reuse it, so capture is refused before anything is
+  // enqueued (pw_exchange_scratch is the capturable form of the step).
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+    return fail(PW_ERR_UNSUPPORTED, "a plan's calls cannot be captured into a HIP graph (each call's epoch is fixed "
+                "when it is made); pw_exchange_scratch can be");
   return PW_OK;
 }
 

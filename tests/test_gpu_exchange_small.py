@@ -121,6 +121,28 @@ def test_one_launch_new_inputs_every_call(gpu):
         assert np.array_equal(one.dst.cpu().numpy().view(np.uint32)[:rows], ref.y.view(np.uint32))
 
 
+def test_plan_calls_refuse_graph_capture(gpu):
+    """A plan's call fixes its epoch (and the one-launch table tag) on the
+    host, so a graph replay would reuse them: a call on a capturing stream
+    returns PW_ERR_UNSUPPORTED and enqueues nothing; the plan then works as
+    before."""
+    pw = gpu
+    n, t, p = 8, 512, 16
+    x = torch.from_numpy(pw_inputs.exchange_uniform(n, t, p).x).cuda()
+    dd = torch.from_numpy(_dest("uniform", n, t)).cuda()
+    for flags in (0, pw.PW_FLAG_ONE_LAUNCH):
+        ex = pw.Exchange(n, t, p, b_op=pw.op(pw.PW_OP_ROWSUM), flags=flags)
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with pytest.raises(pw.PwError) as err:
+            with torch.cuda.graph(g, stream=s):
+                ex.step(x, dd, stream=s)
+        assert err.value.code == pw.PW_ERR_UNSUPPORTED and "graph" in str(err.value)
+        pw.future_wait(ex.step(x, dd), 30_000_000_000)
+        ref = ox.exchange_step(x.cpu().numpy(), _dest("uniform", n, t), n, n)
+        assert np.array_equal(ex.dst.cpu().numpy().view(np.uint32), ref.y.view(np.uint32))
+
+
 def test_one_launch_b_overlaps_the_exchange(gpu):
     """32 destinations fed by disjoint source shards (identity routing): each
     segment completes when its own 8 slabs have arrived, and B of a segment
