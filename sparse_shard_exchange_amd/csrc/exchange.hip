@@ -633,18 +633,39 @@ constexpr uint32_t kBPasses = kBRows / 16;  // row sum: 16 rows of 16 lanes per 
 // LDS list. After the rows, one thread per listed destination adds its slot
 // count to the B arrivals. A segment's length is the tuple count its
 // destination keeps, so the last adder knows it completed B[d].
+//
+// Row sums of rows of at most 256 bytes (one float4 per lane) load the rows
+// before that round of checks, so that the two round trips overlap: the
+// scatter ran in an earlier launch on this stream, so the rows are complete
+// whatever the checks find, and the values are used only once every future
+// checked has fired (rows past the buffer re-read its last row and are never
+// stored).
 __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
   __shared__ uint32_t n_over;
   __shared__ uint32_t over_d[kBRows];
   __shared__ int64_t over_lo[kBRows], over_hi[kBRows];
   if (threadIdx.x == 0) n_over = 0;
-  __syncthreads();
   const int64_t s0 = (int64_t)blockIdx.x * kBRows;
+  const uint32_t P = a.row_bytes / 4u, P4 = P / 4u;
+  const uint32_t l16 = threadIdx.x & 15, r = threadIdx.x >> 4;
+  const bool early = a.b_kind == OP_ROWSUM && P % 4u == 0 && P4 <= 16 && a.dst_rows > 0;  // uniform
+  float4 ev[kBPasses];
+  if (early) {
+    const float4* y4 = reinterpret_cast<const float4*>(a.dst);
+#pragma unroll
+    for (uint32_t p = 0; p < kBPasses; ++p) {  // unconditional loads: all in flight together
+      const uint64_t row = min<uint64_t>((uint64_t)s0 + p * 16 + r, a.dst_rows - 1);
+      ev[p] = y4[row * P4 + min(l16, P4 - 1)];
+    }
+  }
+  __syncthreads();
   const int64_t total = a.seg[a.N];
   bool ok = true;
   for (uint32_t d = threadIdx.x; d < a.N; d += kBlock) {
     const int64_t lo = a.seg[d], hi = a.seg[d + 1];
-    const uint32_t v = a.f.epoch[NODE_EXCH * a.f.width + d];
+    // volatile: issued with the segment loads, not sunk into the branch
+    // below (which would add a round trip)
+    const uint32_t v = *reinterpret_cast<const volatile uint32_t*>(&a.f.epoch[NODE_EXCH * a.f.width + d]);
     if (lo < hi && lo < s0 + kBRows && hi > s0) {
       if (!epoch_reached(v, a.epoch)) ok = ok && await_prior(a.f, NODE_EXCH, d, a.epoch);
       const uint32_t k = atomicAdd(&n_over, 1u);
@@ -656,13 +677,23 @@ __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
   if (!__syncthreads_and(ok) || s0 >= total) return;  // uniform
   const int64_t s1 = min<int64_t>(total, s0 + kBRows);
 
-  const uint32_t P = a.row_bytes / 4u;
   const float* y = reinterpret_cast<const float*>(a.dst);
   float* out = reinterpret_cast<float*>(a.b_out);
-  if (a.b_kind == OP_ROWSUM) {
+  if (early) {  // the same sums, in the same order, as below
+#pragma unroll
+    for (uint32_t p = 0; p < kBPasses; ++p) {
+      float x = 0.f;
+      if (l16 < P4) x += (ev[p].x + ev[p].y) + (ev[p].z + ev[p].w);
+      x += __shfl_xor(x, 8, 16);
+      x += __shfl_xor(x, 4, 16);
+      x += __shfl_xor(x, 2, 16);
+      x += __shfl_xor(x, 1, 16);
+      const int64_t s = s0 + p * 16 + r;
+      if (s < s1 && l16 == 0) out[s] = x;
+    }
+  } else if (a.b_kind == OP_ROWSUM) {
     // 16 lanes per row, 16 rows per pass; the passes are unrolled so that
     // every lane's loads of all of them are in flight together
-    const uint32_t l16 = threadIdx.x & 15, r = threadIdx.x >> 4;
     const bool vec = (P % 4u) == 0;
     float acc[kBPasses];
 #pragma unroll
