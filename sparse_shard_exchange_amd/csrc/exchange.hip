@@ -39,7 +39,7 @@
 //           arrival counters; the add that completes a destination fires that
 //           destination's future.
 //
-// B (exchange.hip: k_b) runs per block of output slots and starts only after
+// B (exchange.hip: k_b) runs per block of output slots and computes only once
 // the futures of every destination those slots belong to have fired.
 
 #include "device.h"
