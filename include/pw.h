@@ -92,8 +92,9 @@ typedef enum {
   PW_CHAIN_FUSED   = 2, /* one launch, one node per shard looping over the steps, no futures */
   PW_CHAIN_SPLIT   = 3  /* as CHAINED, but A[i] and B[i] run on different waves, of different
                            workgroups, with A preferably on the first half of the XCDs and B on
-                           the other: every gate is a cross-workgroup acquire of the producer's
-                           release (section 4.5, parallel asynchronous dispatch). Needs all 2 N
+                           the other: every gate is a cross-workgroup handoff, the producer's
+                           agent-coherent stores and epoch, the consumer's poll and coherent
+                           loads (section 4.5, parallel asynchronous dispatch). Needs all the
                            waves resident at once (else pw_plan returns PW_ERR_UNSUPPORTED)  */
 } pw_chain_mode;
 
