@@ -14,8 +14,10 @@
 //           its destinations (one LDS atomic per group), writes the row
 //           tile_base[tile][*] (and a copy, tile_cnt), and ranks each tuple
 //           among the tuples of the tile with the same destination, in tuple
-//           order (wave by wave), into rank[g] (16 bits); with at most 16
-//           tiles its last workgroup also runs the scan below;
+//           order (wave by wave), into rank[g] (16 bits); with few tiles
+//           (one scan block, or at most 16 blocks with at most 256 (block,
+//           destination) columns in all) its last workgroup also runs the
+//           scan below, one column per thread;
 //   scan    one workgroup per block of 16 tiles runs, per destination, down
 //           its rows (where each tile's run of d starts inside the block)
 //           and writes the block totals; those are scanned over the blocks
@@ -183,6 +185,43 @@ __device__ __forceinline__ void scan_finish(const ExchangeArgs& a, ScanShared& s
   }
 }
 
+// Both levels in one workgroup, for small tables (at most kOneMaxBlk blocks
+// and at most one (block, destination) column per thread): thread b N + d
+// runs down column d of block b (one round of loads) and leaves the block
+// total in `part`; then every block's run start (the earlier blocks' totals
+// of its destination) and the destination totals come from LDS, and the
+// finish runs. kCoherent: the tile rows were written by other workgroups of
+// the same launch (the fused scan of k_rank).
+constexpr uint32_t kOneMaxBlk = 16;
+
+template <bool kCoherent>
+__device__ __forceinline__ void scan_one(const ExchangeArgs& a, ScanShared& sh, uint32_t* part, uint32_t* tot) {
+  const uint32_t N = a.N, B = a.num_blk;
+  const uint32_t b = threadIdx.x / N, d = threadIdx.x % N;
+  const bool live = b < B;  // N * B <= kBlock
+  if (live) {
+    const uint32_t t0 = b * a.scan_tiles, t1 = min(a.num_tiles, t0 + a.scan_tiles);
+    part[threadIdx.x] = column_scan<kCoherent>(a.tile_base, N, d, t0, t1);
+  }
+  __syncthreads();
+  if (live) {
+    uint32_t pre = 0, all = 0;
+    for (uint32_t q = 0; q < B; ++q) {
+      const uint32_t x = part[q * N + d];
+      pre += q < b ? x : 0u;
+      all += x;
+    }
+    a.blk_base[(uint64_t)b * N + d] = pre;
+    if (b == 0) {
+      const uint32_t e = a.capacity ? min(all, a.capacity) : all;  // the tuples d keeps
+      a.expected[d] = e;
+      tot[d] = e;
+    }
+  }
+  __syncthreads();
+  scan_finish(a, sh, [&](uint32_t dd) { return tot[dd]; });
+}
+
 // --------------------------------------------------------------------- rank
 // A wave's destinations (kChunks chunks of 64 tuples: tile / 256), loaded
 // before any is checked, so that the loads of its whole sub-tile are in
@@ -346,6 +385,11 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
   // totals pass through LDS (wrun is free once every wave has ranked).
   __shared__ ScanShared sh;
   if (!last_to_arrive(a, sh)) return;
+  if (a.num_blk > 1) {  // several scan blocks, one column of one block per thread
+    __shared__ uint32_t part[kBlock], tot[kBlock];
+    scan_one<true>(a, sh, part, tot);
+    return;
+  }
   uint32_t* exp_lds = wrun;
   for (uint32_t d = threadIdx.x; d < N; d += kBlock) {
     const uint32_t total = column_scan<true>(a.tile_base, N, d, 0, a.num_tiles);
@@ -408,6 +452,14 @@ __global__ __launch_bounds__(kBlock) void k_scan(ExchangeArgs a) {
   scan_finish(a, sh, [&](uint32_t d) {
     return __hip_atomic_load(&a.expected[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   });
+}
+
+// The scan in a launch of its own for small tables: one workgroup, no
+// workgroup waiting for another, a single round of loads before its stores.
+__global__ __launch_bounds__(kBlock) void k_scan_one(ExchangeArgs a) {
+  __shared__ ScanShared sh;
+  __shared__ uint32_t part[kBlock], tot[kBlock];
+  scan_one<false>(a, sh, part, tot);
 }
 
 // Level 2: kTopDest destinations per workgroup and kTopLanes threads per
@@ -622,10 +674,8 @@ __global__ __launch_bounds__(kBlock) void k_scatter(ExchangeArgs a) {
 }
 
 // ------------------------------------------------------------------------ B
-constexpr uint32_t kBRows = 64;  // output slots per B workgroup
-constexpr uint32_t kBPasses = kBRows / 16;  // row sum: 16 rows of 16 lanes per pass
-
-// B over output slots [s0, s0 + kBRows). The destinations whose non-empty
+// B over output slots [s0, s0 + kBRows) (kBRows: 64 or 128; row sums in
+// passes of 16 rows of 16 lanes). The destinations whose non-empty
 // segments overlap those slots are found, and their exchange futures checked,
 // with one round of loads: each thread reads the segment bounds and the
 // future of the destinations it owns (d = threadIdx.x + k * kBlock), and the
@@ -640,7 +690,9 @@ constexpr uint32_t kBPasses = kBRows / 16;  // row sum: 16 rows of 16 lanes per 
 // whatever the checks find, and the values are used only once every future
 // checked has fired (rows past the buffer re-read its last row and are never
 // stored).
+template <uint32_t kBRows>
 __global__ __launch_bounds__(kBlock) void k_b(ExchangeArgs a) {
+  constexpr uint32_t kBPasses = kBRows / 16;
   __shared__ uint32_t n_over;
   __shared__ uint32_t over_d[kBRows];
   __shared__ int64_t over_lo[kBRows], over_hi[kBRows];
@@ -778,6 +830,10 @@ hipError_t launch_src_counts(const ExchangeArgs& a, hipStream_t s) {
 
 hipError_t launch_scan(const ExchangeArgs& a, hipStream_t s) {
   if (a.num_blk > 256) return hipErrorInvalidValue;  // the layout keeps it <= 256
+  if (a.num_blk <= kOneMaxBlk && (uint64_t)a.num_blk * a.N <= kBlock) {
+    hipLaunchKernelGGL(k_scan_one, dim3(1), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.num_blk <= 16) {
     hipLaunchKernelGGL(k_scan, dim3(a.num_blk), dim3(kBlock), 0, s, a);
     return hipGetLastError();
@@ -825,10 +881,16 @@ hipError_t launch_scatter(const ExchangeArgs& a, hipStream_t s) {
   return launch_scatter_u<u32x4, false>(a, (uint32_t)grid, s);
 }
 
+// 128 output slots per B workgroup once that still gives every CU one (each
+// then has twice the rows in flight, and a destination half the arrival adds:
+// the 8-shard step's B 12.8 -> 10.4 us between events), else 64.
 hipError_t launch_b(const ExchangeArgs& a, hipStream_t s) {
-  const uint64_t blocks = (a.G + kBRows - 1) / kBRows;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_b, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+  if (a.G == 0) return hipSuccess;
+  if (a.G >= 256ull * 128) {
+    hipLaunchKernelGGL(k_b<128>, dim3((uint32_t)((a.G + 127) / 128)), dim3(kBlock), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_b<64>, dim3((uint32_t)((a.G + 63) / 64)), dim3(kBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@ struct ExchangeArgs {
   uint32_t tile;              // tuples per workgroup tile (multiple of 256)
   uint32_t num_tiles;
   uint32_t scan_tiles, num_blk;  // tiles per scan block; scan blocks
-  uint32_t fuse_scan;            // 1: the rank kernel also runs the scan (num_blk == 1)
+  uint32_t fuse_scan;            // 1: the rank kernel also runs the scan (small tables)
   uint32_t nbits;             // bits needed to tell destinations apart
   uint32_t is_f32;
   uint32_t a_kind; float a_a, a_b;
