@@ -313,7 +313,7 @@ def small_step_bench(pw, torch, pw_inputs, iters=50, cold_iters=20):
                 "tuples_per_s_warm": g / (warm_us * 1e-6), "gbs_warm_algorithmic": 780 * g / (warm_us * 1e-6) / 1e9}
 
     out = {"workload": "8 shards x 4096 tuples x 64 fp32 ~U(-1,1), dest uniform, A = 2x+1, B = per-tuple sum",
-           "bytes_per_tuple_step": 780, "path": "separate launches (rank, scan, scatter, B)"}
+           "bytes_per_tuple_step": 780, "path": "separate launches (rank with the scan in its last workgroup, scatter, B)"}
     out.update(timed(0))
     out["one_launch"] = timed(pw.PW_FLAG_ONE_LAUNCH)
     tr = pw.Exchange(n, t, p, a_op=pw.op(pw.PW_OP_AFFINE, 2.0, 1.0), b_op=pw.op(pw.PW_OP_ROWSUM),

@@ -109,7 +109,7 @@ typedef enum {
                                    run the whole step as one co-resident launch in which B of each
                                    segment waits on that segment's EXCHANGE future inside the
                                    launch (sections 4.4-4.5); otherwise, and by default, as
-                                   separate launches (rank, scan, scatter, B). Same results      */
+                                   separate launches (rank and scan, scatter, B). Same results   */
 
 /* ---- plan descriptor ------------------------------------------------------ */
 typedef struct {
