@@ -67,7 +67,8 @@ def check_expert_rows(xrows, w1e, w2e, y_gpu):
     (512, 256, 8, 512, 4), (300, 512, 64, 256, 3), (1000, 256, 2, 256, 8), (64, 256, 5, 768, 1),
     (1, 256, 4, 256, 1),   # one token: two expert rows, every other expert empty
     (400, 768, 8, 256, 2),  # the router's 6-block instance (one per d / 128)
-    (700, 1280, 16, 256, 2)])  # the largest d: the router's W_r^T fills a CU's whole LDS
+    (700, 1280, 16, 256, 2),  # the largest d: the router's W_r^T fills a CU's whole LDS
+    (4096, 256, 8, 256, 4)])  # 32 ranking tiles in 2 scan blocks: the one-workgroup scan launch
 def test_moe_small(gpu, tokens, d, experts, hidden, shards):
     pw = gpu
     print(f"moe T={tokens} d={d} E={experts} H={hidden} S={shards}", flush=True)
