@@ -380,9 +380,10 @@ __global__ __launch_bounds__(kBlock, 8) void k_rank(ExchangeArgs a) {
   }
   if (bad) latch(a.f, ST_BAD_DEST);
   if (!a.fuse_scan) return;
-  // Few tiles (one scan block): the last workgroup to finish ranking runs
-  // the whole scan here instead of in a launch of its own. The destination
-  // totals pass through LDS (wrun is free once every wave has ranked).
+  // Few tiles (one scan block, or a small table of blocks: the host decides):
+  // the last workgroup to finish ranking runs the whole scan here instead of
+  // in a launch of its own. With one block the destination totals pass
+  // through LDS (wrun is free once every wave has ranked).
   __shared__ ScanShared sh;
   if (!last_to_arrive(a, sh)) return;
   if (a.num_blk > 1) {  // several scan blocks, one column of one block per thread
