@@ -95,8 +95,8 @@ CASES = [
     (8192, 2, 64, "half_empty"),
     (4, 10, 8192, "uniform"),     # 32 KiB rows: one tuple per scatter workgroup, two copy batches each
     (1024, 4, 16, "zipf4"),       # <= 16 ranking tiles: the last ranking workgroup runs the scan
-    (16, 4096, 16, "uniform"),    # 16 scan blocks x 16 destinations: the most the fused one-column-per-thread scan takes
-    (32, 1024, 16, "zipf4"),      # 8 blocks x 32 destinations, fused; (64, 300) above: 5 x 64, a scan launch
+    (16, 8192, 16, "uniform"),    # 16 scan blocks x 16 destinations: the most the fused one-column-per-thread scan takes
+    (32, 2048, 16, "zipf4"),      # 8 blocks x 32 destinations, fused; (64, 1001) above: 8 x 64, a scan launch
     (2048, 2, 4, "uniform"),
 ]
 
